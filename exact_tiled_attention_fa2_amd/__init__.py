@@ -1,0 +1,129 @@
+"""Exact tiled attention (FlashAttention-2 style) for AMD MI355X, Python binding.
+
+The compute lives in ``libfa2.so`` (HIP kernels for gfx950 behind a C ABI, declared in
+``include/fa2.h``). This module only marshals arguments to it: the functions named like the
+C entry points take raw device addresses (ints) or torch tensors and return the C status.
+``forward``/``backward`` are thin conveniences that allocate outputs with torch (device
+memory and streams only) and raise on a non-zero status.
+
+There is no fallback: if the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa2.so")
+
+FA2_OK = 0
+STATUS_NAMES = {
+    0: "FA2_OK", 1: "FA2_ERR_NULL_POINTER", 2: "FA2_ERR_BAD_SHAPE", 3: "FA2_ERR_UNSUPPORTED_HEAD_DIM",
+    4: "FA2_ERR_BAD_GQA", 5: "FA2_ERR_BAD_SCALE", 6: "FA2_ERR_MISALIGNED", 7: "FA2_ERR_ALIASING",
+    8: "FA2_ERR_WORKSPACE", 9: "FA2_ERR_HIP",
+}
+EXPORTED = ("fa2_forward", "fa2_backward", "fa2_backward_workspace_size", "fa2_status_string")
+
+_lib = None
+
+
+class Fa2Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__("%s returned %s (%d)" % (where, STATUS_NAMES.get(status, "?"), status))
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa2.so; raises if it has not been built (no fallback path exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libfa2.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fa2_forward.restype = i
+    lib.fa2_forward.argtypes = [p, p, p, p, p, i, i, i, i, i, i, f, p]
+    lib.fa2_backward.restype = i
+    lib.fa2_backward.argtypes = [p, p, p, p, p, p, p, p, p, i, i, i, i, i, i, f, p, ctypes.c_size_t, p]
+    lib.fa2_backward_workspace_size.restype = ctypes.c_size_t
+    lib.fa2_backward_workspace_size.argtypes = [i, i, i]
+    lib.fa2_status_string.restype = ctypes.c_char_p
+    lib.fa2_status_string.argtypes = [i]
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()  # torch tensor
+
+
+def _stream(s):
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream  # torch.cuda.Stream
+
+
+# ---------------------------------------------------------------- C entry points, same names
+
+def fa2_forward(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream=None) -> int:
+    return load().fa2_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
+                              int(bool(causal)), float(scale), _stream(stream))
+
+
+def fa2_backward_workspace_size(B, Hq, N) -> int:
+    return int(load().fa2_backward_workspace_size(B, Hq, N))
+
+
+def fa2_backward(q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale,
+                 workspace, workspace_bytes, stream=None) -> int:
+    return load().fa2_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
+                               _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
+                               _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def fa2_status_string(status: int) -> str:
+    return load().fa2_status_string(int(status)).decode()
+
+
+# ------------------------------------------------------------ torch conveniences (memory only)
+
+def _dims(q, k):
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    return B, Hq, Hkv, N, d
+
+
+def forward(q, k, v, causal: bool, scale: float, stream=None):
+    """O (fp32) and LSE (fp32) for bf16 device tensors q [B,Hq,N,d], k/v [B,Hkv,N,d]."""
+    import torch
+    B, Hq, Hkv, N, d = _dims(q, k)
+    o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    st = fa2_forward(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream)
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_forward")
+    return o, lse
+
+
+def backward(q, k, v, o, lse, dO, causal: bool, scale: float, stream=None, workspace=None):
+    """dQ, dK, dV (fp32) of sum(O * dO) for the outputs of :func:`forward`."""
+    import torch
+    B, Hq, Hkv, N, d = _dims(q, k)
+    dq = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device)
+    dv = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device)
+    need = fa2_backward_workspace_size(B, Hq, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = fa2_backward(q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale,
+                      workspace, workspace.numel() * workspace.element_size(), stream)
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_backward")
+    return dq, dk, dv

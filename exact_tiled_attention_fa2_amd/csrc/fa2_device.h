@@ -1,0 +1,91 @@
+// fa2_device.h -- gfx950 building blocks shared by the attention kernels.
+//
+// Facts these helpers rely on (checked on gfx950 with a lane-layout probe):
+//  * v_mfma_f32_32x32x16_bf16, wave64. A (32x16): lane l holds row l%32, k = 8*(l/32)+e.
+//    B (16x32): lane l holds column l%32, k = 8*(l/32)+e. C/D (32x32): lane l holds column
+//    l%32 and, in register r, row 8*(r/4) + 4*(l/32) + (r%4). An accumulator can therefore be
+//    fed back as the B operand of the next product (its rows become the contraction index).
+//  * ds_read_b64_tr_b16: inside each group of 16 lanes, output lane t element e is element
+//    t%4 of the 8 bytes addressed by lane 4*e + t/4 -- a 4x16 -> 16x4 transpose of bf16.
+//  * v_permlane32_swap exchanges the upper half of the first operand with the lower half of
+//    the second; swapping a value with itself hands each lane its partner's (lane ^ 32) value.
+//  * buffer_load_dwordx4 ... lds writes lane l's 16 bytes at (wave-uniform LDS base) + 16*l;
+//    out-of-range buffer offsets read as zero.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa2 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+#define FA2_LDS __attribute__((address_space(3)))
+typedef FA2_LDS char lds_char;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Buffer resource over [base, base + bytes); loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rs, uint32_t voffset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voffset, 0, 0));
+}
+
+// Direct global -> LDS copy of 16 bytes per lane; lane l lands at lds_wave_base + 16*l.
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t rs, lds_char* lds_wave_base,
+                                                  uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA2_LDS void*)lds_wave_base, 16, voffset, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const lds_char* p) {
+  return *(const FA2_LDS u32x4*)p;
+}
+
+__device__ __forceinline__ u32x2 lds_read8_tr(const lds_char* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS i16x4*)p);
+  return __builtin_bit_cast(u32x2, r);
+}
+
+__device__ __forceinline__ float partner_half(float x) {
+  // value held by lane (l ^ 32)
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return (__lane_id() < 32) ? __uint_as_float(r[1]) : __uint_as_float(r[0]);
+}
+
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(unsigned, v);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+}  // namespace fa2

@@ -1,0 +1,326 @@
+// fa2_fwd.hip -- exact attention forward for gfx950: O and the per-row logsumexp.
+//
+// Method (FlashAttention-2 pages: "Flash Attention spiegata: una guida completa", datacamp,
+// sections "Tiling" and "Flash Attention 2"; wiki article "FlashAttention-2", section on
+// technical architecture): Q is split into row blocks, K/V are streamed through on-chip
+// memory tile by tile, and the softmax is applied incrementally -- a running row max m and
+// row sum l, with the output accumulator rescaled whenever m grows -- so the N x N matrix is
+// never stored. Only O and LSE = m + ln l reach HBM.
+//
+// gfx950 mapping (one workgroup per (batch, query head, 256-row query block)):
+//  * 4 waves; each wave owns 64 query rows (two 32-row MFMA blocks) for the whole pass, so
+//    the online-softmax state and all row reductions stay in that wave's registers.
+//  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: each lane then
+//    holds one query row and 16 keys, the row max/sum are in-register reductions plus one
+//    v_permlane32_swap, and S^T's accumulator is directly the B operand of O^T += V^T P^T.
+//  * K and V tiles (64 keys) arrive by buffer_load ... lds (no staging registers), double
+//    buffered. K is read as 16-byte A-operand rows; V^T is read with ds_read_b64_tr_b16.
+//    Both tiles are XOR-swizzled so these reads hit distinct LDS banks.
+//  * Causal: K/V tiles above a wave's last row are skipped; only tiles that straddle the
+//    diagonal (or the ragged end of the sequence) are masked. Query blocks are scheduled
+//    heaviest first, and blocks of one head stay on one XCD so their K/V reads share an L2.
+//  * Scale folded into the exponent: p = 2^(s*c - m) with c = |scale|*log2(e); a negative
+//    scale flips the sign of the Q operand instead. The accumulator rescale is skipped when
+//    no row max in the wave changed.
+#include "fa2_device.h"
+#include "fa2_launch.h"
+
+namespace fa2 {
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  float* o;
+  float* lse;
+  int B, Hq, Hkv, N;
+  int causal;
+  float c;        // |scale| * log2(e)
+  unsigned qneg;  // 0x80008000 flips both bf16 signs of a packed pair when scale < 0
+  int nqb;        // query blocks per head
+  int xcd_remap;  // B*Hq divisible by 8: keep each head's blocks on one XCD
+};
+
+template <int D>
+struct FwdCfg {
+  static constexpr int BN = 64;               // keys per tile
+  static constexpr int WAVES = 4;
+  static constexpr int QPW = 64;              // query rows per wave
+  static constexpr int BM = WAVES * QPW;      // query rows per workgroup
+  static constexpr int KS = D / 16;           // k-steps of the Q.K contraction
+  static constexpr int DB = D / 32;           // 32-wide blocks of the head dim
+  static constexpr int CH = D / 8;            // 16-byte chunks per bf16 row
+  static constexpr int RP = 16 / CH;          // rows per 256 bytes of LDS
+  static constexpr int ROWB = D * 2;          // bytes per bf16 row
+  static constexpr int TILE = BN * ROWB;      // bytes of one K or V tile
+  static constexpr int LPW = TILE / 1024 / WAVES;  // 1 KB direct-to-LDS loads per wave per tile
+};
+
+// K tile: 16-byte chunk c of row r is stored at chunk position c ^ swz_k(r). The 16 rows a
+// quarter-wave reads at one chunk then land in 16 different bank groups.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  constexpr int CH = D / 8, RP = 16 / CH;
+  return (r / RP) & (CH - 1);
+}
+// V tile: chunk c of row r at c ^ swz_v(r). A transposing read touches 4 rows x 4 chunks
+// per half-wave; this XOR spreads them over all 16 bank groups.
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  constexpr int CH = D / 8, RP = 16 / CH;
+  return 4 * ((r / RP) & (CH / 4 - 1));
+}
+
+// Copy keys [j0, j0+64) of one head into a swizzled LDS tile. Rows past N read as zero.
+template <int D, bool IS_V>
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, lds_char* tile, int j0,
+                                          int wave, int lane) {
+  using C = FwdCfg<D>;
+#pragma unroll
+  for (int t = 0; t < C::LPW; ++t) {
+    const int blk = wave * C::LPW + t;
+    const int pos = blk * 1024 + lane * 16;  // where this lane's 16 bytes land
+    const int r = pos / C::ROWB;
+    const int cp = (pos % C::ROWB) / 16;
+    const int c = cp ^ (IS_V ? swz_v<D>(r) : swz_k<D>(r));
+    buffer_load16_lds(rs, tile + blk * 1024, (uint32_t)(j0 + r) * C::ROWB + c * 16);
+  }
+}
+
+__device__ __forceinline__ void map_block(int bid, const FwdParams& p, int& bh, int& qblk) {
+  int r;
+  if (p.xcd_remap) {
+    // Workgroups are dealt round-robin to the 8 XCDs: bid & 7 is the XCD. Give each XCD a
+    // contiguous range of heads and walk its query blocks in order there.
+    const int x = bid & 7, s = bid >> 3;
+    const int heads_per_xcd = (p.B * p.Hq) >> 3;
+    bh = x * heads_per_xcd + s / p.nqb;
+    r = s % p.nqb;
+  } else {
+    bh = bid / p.nqb;
+    r = bid % p.nqb;
+  }
+  qblk = p.causal ? p.nqb - 1 - r : r;  // causal: longest rows first
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa2_fwd_kernel(FwdParams p) {
+  using C = FwdCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE];
+  lds_char* lds = (lds_char*)smem;
+  // stage s: K at lds + 2*s*TILE, V at lds + (2*s+1)*TILE
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int hf = lane >> 5;  // which half of the wave
+  const int l32 = lane & 31;
+
+  int bh, qblk;
+  map_block(blockIdx.x, p, bh, qblk);
+  const int b = bh / p.Hq, hq = bh % p.Hq;
+  const int hkv = hq / (p.Hq / p.Hkv);
+  const int N = p.N;
+  const int q0 = qblk * C::BM;
+  const int qlo = q0 + wave * C::QPW;  // this wave's first query row
+
+  const uint32_t head_bytes = (uint32_t)N * C::ROWB;
+  const size_t qoff = (size_t)bh * N * D;
+  const size_t kvoff = ((size_t)b * p.Hkv + hkv) * (size_t)N * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + qoff, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + kvoff, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + kvoff, head_bytes);
+
+  const int qend = min(q0 + C::BM, N);
+  const int ntiles = p.causal ? (qend + C::BN - 1) / C::BN : (N + C::BN - 1) / C::BN;
+
+  // Start the first K/V tile while Q is fetched into registers.
+  load_tile<D, false>(rk, lds, 0, wave, lane);
+  load_tile<D, true>(rv, lds + C::TILE, 0, wave, lane);
+
+  // Q as the B operand of S^T = K Q^T: lane holds query l32, head-dim k = 16*ks + 8*hf + e.
+  u32x4 qf[2][C::KS];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const uint32_t row = (uint32_t)(qlo + qb * 32 + l32);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      u32x4 x = buffer_load16(rq, row * C::ROWB + (16 * ks + 8 * hf) * 2);
+      qf[qb][ks] = x ^ p.qneg;
+    }
+  }
+
+  // Per-lane LDS read offsets (the swizzles depend on the lane, not on the tile).
+  int koff[C::KS];  // K A-operand row l32 (+32 per key block), chunk 2*ks + hf
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    const int r = l32;  // swz_k(r + 32) == swz_k(r) for both head dims
+    koff[ks] = r * C::ROWB + (((2 * ks + hf) ^ swz_k<D>(r)) << 4);
+  }
+  int voff[C::DB];  // V^T A-operand: transposing read base for each 32-wide head-dim block
+  {
+    const int r = 4 * hf + ((lane & 15) >> 2);  // + 32*kb + 16*h (+8): swz_v unchanged
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const int d = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      voff[db] = r * C::ROWB + (((d >> 3) ^ swz_v<D>(r)) << 4) + (d & 7) * 2;
+    }
+  }
+
+  f32x16 acc[2][C::DB];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) acc[qb][db] = f32x16{};
+  float m[2] = {-INFINITY, -INFINITY};
+  float l[2] = {0.f, 0.f};
+  const float c = p.c;
+
+  wait_vmem_all();
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t & 1;
+    const lds_char* kt = lds + (2 * st) * C::TILE;
+    const lds_char* vt = lds + (2 * st + 1) * C::TILE;
+    if (t + 1 < ntiles) {
+      lds_char* kn = lds + (2 * (st ^ 1)) * C::TILE;
+      load_tile<D, false>(rk, kn, (t + 1) * C::BN, wave, lane);
+      load_tile<D, true>(rv, kn + C::TILE, (t + 1) * C::BN, wave, lane);
+    }
+    const int j0 = t * C::BN;
+    const bool skip = p.causal && j0 > qlo + C::QPW - 1;
+    if (!skip) {
+      // ---- S^T = K_j Q^T : [qb][kb] blocks of 32 keys x 32 queries ----
+      f32x16 s[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[qb][kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const u32x4 kf = lds_read16(kt + koff[ks] + kb * 32 * C::ROWB);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) s[qb][kb] = mfma32x32x16(kf, qf[qb][ks], s[qb][kb]);
+        }
+      }
+      // ---- mask: only tiles crossing the diagonal or the end of the sequence ----
+      const bool need_mask = (j0 + C::BN > N) || (p.causal && j0 + C::BN - 1 > qlo);
+      if (need_mask) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const int qi = qlo + qb * 32 + l32;
+          const int lim = p.causal ? min(qi, N - 1) : N - 1;  // last visible key
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+              if (key > lim) s[qb][kb][r] = -INFINITY;
+            }
+        }
+      }
+      // ---- online softmax; P^T packed to bf16 pairs ----
+      unsigned pk[2][2][8];  // [qb][kb][pair]
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float mt = s[qb][0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[qb][kb][r]);
+        mt = max_halves(mt);
+        const float mnew = fmaxf(m[qb], mt * c);
+        const float alpha = fast_exp2(m[qb] - mnew);
+        m[qb] = mnew;
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const float p0 = fast_exp2(__builtin_fmaf(s[qb][kb][r], c, -mnew));
+            const float p1 = fast_exp2(__builtin_fmaf(s[qb][kb][r + 1], c, -mnew));
+            rs += p0 + p1;
+            pk[qb][kb][r >> 1] = pack_bf16(p0, p1);
+          }
+        l[qb] = l[qb] * alpha + rs;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) acc[qb][db] *= alpha;
+        }
+      }
+      // ---- O^T += V_j^T P^T ----
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const lds_char* base = vt + voff[db] + (32 * kb + 16 * h) * C::ROWB;
+            const u32x2 lo = lds_read8_tr(base);
+            const u32x2 hi = lds_read8_tr(base + 8 * C::ROWB);
+            const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+              const u32x4 pf = {pk[qb][kb][4 * h], pk[qb][kb][4 * h + 1], pk[qb][kb][4 * h + 2],
+                                pk[qb][kb][4 * h + 3]};
+              acc[qb][db] = mfma32x32x16(vf, pf, acc[qb][db]);
+            }
+          }
+        }
+      }
+    }
+    wait_vmem_all();
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lt = sum_halves(l[qb]);
+    const float inv = 1.0f / lt;
+    const int row = qlo + qb * 32 + l32;
+    if (row < N) {
+      float* orow = p.o + qoff + (size_t)row * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const f32x4 val = {acc[qb][db][4 * rq] * inv, acc[qb][db][4 * rq + 1] * inv,
+                             acc[qb][db][4 * rq + 2] * inv, acc[qb][db][4 * rq + 3] * inv};
+          *(f32x4*)(orow + 32 * db + 8 * rq + 4 * hf) = val;
+        }
+      if (hf == 0) p.lse[(size_t)bh * N + row] = (m[qb] + __log2f(lt)) * kLn2;
+    }
+  }
+}
+
+hipError_t launch_forward(const void* q, const void* k, const void* v, float* o, float* lse,
+                          const AttnShape& s, hipStream_t stream) {
+  FwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = o;
+  p.lse = lse;
+  p.B = s.B;
+  p.Hq = s.Hq;
+  p.Hkv = s.Hkv;
+  p.N = s.N;
+  p.causal = s.causal;
+  p.c = fabsf(s.scale) * kLog2e;
+  p.qneg = s.scale < 0.f ? 0x80008000u : 0u;
+  const int BM = FwdCfg<128>::BM;
+  p.nqb = (s.N + BM - 1) / BM;
+  p.xcd_remap = ((s.B * s.Hq) % 8) == 0;
+  const dim3 grid((unsigned)(s.B * s.Hq * p.nqb)), block(256);
+  if (s.d == 128)
+    hipLaunchKernelGGL(fa2_fwd_kernel<128>, grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL(fa2_fwd_kernel<64>, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace fa2

@@ -1,0 +1,108 @@
+/*
+ * fa2.h -- exact tiled attention (FlashAttention-2 style) for AMD MI355X (gfx950).
+ *
+ * The library computes exact scaled dot-product attention
+ *     O = softmax(scale * Q K^T) V
+ * without ever storing the N x N score matrix. The forward streams K/V tiles through on-chip
+ * memory and applies the softmax incrementally, saving only O and the per-row logsumexp;
+ * the backward recomputes the probabilities from that logsumexp instead of reading a stored
+ * matrix. Source: the FlashAttention-2 pages ("Flash Attention spiegata: una guida completa",
+ * datacamp, sections "Attention standard vs Flash attention", "Tiling", "Ricomputazione";
+ * wiki article "FlashAttention-2", section on technical architecture). The result is exact:
+ * it equals standard attention up to floating-point rounding.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers owned by the caller. The library allocates, frees and
+ *     retains nothing, and keeps no state between calls; calls are re-entrant.
+ *   - Layouts are contiguous row-major: q, dO, o, dq        [B, Hq,  N, d]
+ *                                        k, v, dk, dv       [B, Hkv, N, d]
+ *                                        lse                [B, Hq,  N]
+ *   - Dtypes: q, k, v, dO are bfloat16 (raw 16-bit patterns); o, lse, dq, dk, dv are float32.
+ *     lse is the natural-log logsumexp of the scaled scores of each query row.
+ *   - Grouped-query attention: query head hq reads key/value head hq / (Hq / Hkv).
+ *   - causal != 0: query row i attends to key rows j <= i (square, top-left aligned).
+ *   - d must be 64 or 128. Other head dims are rejected with FA2_ERR_UNSUPPORTED_HEAD_DIM
+ *     (the pages treat an unsupported head dimension as a reported error, not a silent
+ *     fallback: "Flash Attention 2: attivarla (llama.cpp, Ollama, vLLM)", qualellm.it,
+ *     section "Risoluzione dei problemi", item "Errore unsupported head dimension").
+ *   - scale must be finite and non-zero (negative values are accepted).
+ *   - Every pointer must be 16-byte aligned; outputs must not overlap inputs or each other.
+ *   - B == 0 or N == 0 is an empty problem: nothing is enqueued and FA2_OK is returned
+ *     (pointers may then be NULL). Negative sizes, Hq or Hkv < 1, Hq % Hkv != 0 and sizes
+ *     whose element offsets would not fit the kernels' index arithmetic are errors.
+ *   - All validation happens before anything is enqueued: on error nothing is launched and
+ *     no output is written. FA2_OK means the work is ENQUEUED on `stream` (NULL = the null
+ *     stream); results are valid once the stream has been synchronised.
+ *   - FA2_ERR_HIP reports a failed launch (hipGetLastError after the launch); an error left
+ *     pending on the device by earlier, unrelated work may surface here as well.
+ *   - Bitwise deterministic: identical inputs, sizes and build give identical outputs (no
+ *     floating-point atomics; each output element is reduced in a fixed order).
+ */
+#ifndef FA2_H
+#define FA2_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA2_OK = 0,
+  FA2_ERR_NULL_POINTER = 1,         /* a required pointer is NULL (non-empty problem)      */
+  FA2_ERR_BAD_SHAPE = 2,            /* negative size, or offsets overflow index arithmetic */
+  FA2_ERR_UNSUPPORTED_HEAD_DIM = 3, /* d not in {64, 128}                                  */
+  FA2_ERR_BAD_GQA = 4,              /* Hq < 1, Hkv < 1 or Hq % Hkv != 0                    */
+  FA2_ERR_BAD_SCALE = 5,            /* scale is NaN, infinite or zero                      */
+  FA2_ERR_MISALIGNED = 6,           /* a pointer is not 16-byte aligned                    */
+  FA2_ERR_ALIASING = 7,             /* an output overlaps an input or another output       */
+  FA2_ERR_WORKSPACE = 8,            /* workspace NULL or smaller than required             */
+  FA2_ERR_HIP = 9                   /* a kernel launch failed                              */
+} fa2_status;
+
+/*
+ * Forward pass: O and LSE from Q, K, V.
+ *   q      bf16 [B,Hq,N,d]   (read only)
+ *   k, v   bf16 [B,Hkv,N,d]  (read only)
+ *   o      f32  [B,Hq,N,d]   (written)   O_i = sum_j P_ij v_j, P = softmax over visible keys
+ *   lse    f32  [B,Hq,N]     (written)   LSE_i = ln sum_j exp(scale <q_i, k_j>)
+ * Tiles Q into row blocks, streams K/V tiles through LDS with an online softmax (running
+ * row max and sum, accumulator rescaled when the max grows), skips K/V tiles that the causal
+ * mask hides entirely and masks only tiles that straddle the diagonal.
+ */
+int fa2_forward(const void* q, const void* k, const void* v, float* o, float* lse,
+                int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                hipStream_t stream);
+
+/* Bytes of device workspace fa2_backward needs: one float per query row (D = rowsum(dO*O)),
+   rounded up to 256 bytes. 0 for an empty problem or negative sizes. */
+size_t fa2_backward_workspace_size(int B, int Hq, int N);
+
+/*
+ * Backward pass: dQ, dK, dV of L = sum(O * dO), recomputing P from the saved LSE.
+ *   q, k, v      as in fa2_forward (read only)
+ *   o, lse       the outputs of fa2_forward for the same q, k, v, sizes, causal, scale
+ *   dO           bf16 [B,Hq,N,d]  (read only)
+ *   dq           f32  [B,Hq,N,d]  (written)  scale * sum_j dS_ij k_j
+ *   dk, dv       f32  [B,Hkv,N,d] (written)  sums over the Hq/Hkv query heads of a group
+ *   workspace    device scratch of at least fa2_backward_workspace_size(B,Hq,N) bytes,
+ *                owned by the caller; its contents on entry do not matter and are
+ *                overwritten. Must not overlap any other argument.
+ * Three launches in stream order: a preprocess (D_i = sum_c dO_ic O_ic), a dK/dV kernel
+ * (one workgroup per key block, looping over query blocks and the group's query heads) and
+ * a dQ kernel (one workgroup per query block, looping over key blocks). No atomics.
+ */
+int fa2_backward(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                 const void* dO, float* dq, float* dk, float* dv,
+                 int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static, human-readable name of a status code ("FA2_OK", ...); "FA2_UNKNOWN" otherwise. */
+const char* fa2_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2_H */

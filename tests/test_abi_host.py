@@ -1,0 +1,96 @@
+"""The C-ABI library on the host: it loads, exports what include/fa2.h declares, and rejects
+invalid arguments before touching the GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_fa2_amd as fa2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa2.LIB_PATH):
+        import importlib
+        importlib.import_module("exact_tiled_attention_fa2_amd.build").build()
+    return fa2.load()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "fa2.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(fa2_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(fa2.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in fa2.STATUS_NAMES.items():
+        assert fa2.fa2_status_string(code) == name
+    assert fa2.fa2_status_string(99) == "FA2_UNKNOWN"
+
+
+def test_workspace_size(lib):
+    assert fa2.fa2_backward_workspace_size(4, 16, 4096) == 4 * 16 * 4096 * 4
+    assert fa2.fa2_backward_workspace_size(1, 1, 3) == 256
+    assert fa2.fa2_backward_workspace_size(0, 16, 4096) == 0
+    assert fa2.fa2_backward_workspace_size(-1, 16, 4096) == 0
+
+
+# Fake, distinct, 16-byte-aligned device addresses: never dereferenced because every call
+# below is rejected by host-side validation before any launch.
+BASE = 1 << 40
+def P(i):
+    return BASE + i * (1 << 32)
+
+
+def fwd(**kw):
+    a = dict(q=P(0), k=P(1), v=P(2), o=P(3), lse=P(4), B=1, Hq=2, Hkv=1, N=128, d=64, causal=1, scale=0.125)
+    a.update(kw)
+    return fa2.fa2_forward(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["N"],
+                           a["d"], a["causal"], a["scale"])
+
+
+def bwd(**kw):
+    a = dict(q=P(0), k=P(1), v=P(2), o=P(3), lse=P(4), dO=P(5), dq=P(6), dk=P(7), dv=P(8),
+             B=1, Hq=2, Hkv=1, N=128, d=64, causal=1, scale=0.125, ws=P(9), wsb=1 << 20)
+    a.update(kw)
+    return fa2.fa2_backward(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dO"], a["dq"], a["dk"], a["dv"],
+                            a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"], a["scale"],
+                            a["ws"], a["wsb"])
+
+
+@pytest.mark.parametrize("call", [fwd, bwd])
+def test_validation_codes(lib, call):
+    assert call(d=96) == 3 and call(d=256) == 3 and call(d=32) == 3
+    assert call(Hq=3, Hkv=2) == 4 and call(Hkv=0) == 4 and call(Hq=0) == 4
+    assert call(B=-1) == 2 and call(N=-5) == 2
+    assert call(N=1 << 22, d=128) == 2           # N*d*4 bytes >= 2^31
+    assert call(scale=float("nan")) == 5 and call(scale=float("inf")) == 5 and call(scale=0.0) == 5
+    assert call(q=P(0) + 8) == 6
+    assert call(q=None) == 1
+    assert call(B=0) == 0 and call(N=0) == 0      # empty problems: nothing to do
+    assert call(B=0, q=None) == 0
+
+
+def test_forward_aliasing(lib):
+    assert fwd(o=P(0)) == 7                       # o overlaps q
+    assert fwd(lse=P(3) + 4096) == 7              # lse inside o
+    assert fwd(o=P(1) + 1024) == 7                # o inside k
+    assert fwd(lse=P(2) - 16) == 7                # lse range reaches into v
+
+
+def test_backward_aliasing_and_workspace(lib):
+    assert bwd(dq=P(5)) == 7                      # dq overlaps dO
+    assert bwd(dk=P(7) + 16, dv=P(7) + 16) == 7   # dk and dv overlap
+    assert bwd(ws=P(4)) == 7                      # workspace overlaps lse
+    assert bwd(ws=None) == 8
+    assert bwd(wsb=fa2.fa2_backward_workspace_size(1, 2, 128) - 1) == 8
+    assert bwd(ws=P(9) + 4) == 6
