@@ -1,8 +1,501 @@
-// placeholder, replaced by the backward kernels
+// fa2_bwd.hip -- exact attention backward for gfx950: dQ, dK, dV from Q, K, V, O, LSE, dO.
+//
+// Method (FlashAttention-2 pages: "Flash Attention spiegata: una guida completa", datacamp,
+// section "Ricomputazione"): the probabilities are recomputed tile by tile from the saved
+// per-row logsumexp, P_ij = exp(scale <q_i,k_j> - LSE_i), instead of being read back from
+// a stored N x N matrix. The gradients are the chain rule of the standard definition:
+//   dV_j = sum_i P_ij dO_i,  dP_ij = <dO_i, v_j>,  dS_ij = P_ij (dP_ij - D_i),
+//   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  D_i = <dO_i, O_i>.
+// Three kernels run in stream order, none with atomics (the result is deterministic, as
+// the wiki article "FlashAttention-2" stresses in its performance section):
+//   1. preprocess   D_i = sum_c dO_ic O_ic                   (one value per query row)
+//   2. dK/dV        one workgroup per (batch, KV head, 128-key block); each wave keeps its
+//                   32 keys' K, V (MFMA B operands) and fp32 dK^T, dV^T in registers and
+//                   walks every query tile of every query head sharing the KV head.
+//   3. dQ           one workgroup per (batch, query head, 128-query block); each wave keeps
+//                   its 32 queries' Q, dO and fp32 dQ^T in registers and walks the key tiles.
+// Q/dO (dK/dV kernel) and K/V (dQ kernel) tiles stream into LDS by buffer_load ... lds,
+// double buffered, in a layout that serves both 16-byte row reads and the transposing
+// ds_read_b64_tr_b16 reads without bank conflicts.
+#include "fa2_device.h"
 #include "fa2_launch.h"
+
 namespace fa2 {
-hipError_t launch_backward(const void*, const void*, const void*, const float*, const float*,
-                           const void*, float*, float*, float*, const AttnShape&, float*, hipStream_t) {
-  return hipErrorNotSupported;
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* o;
+  const float* lse;
+  const uint16_t* dO;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* delta;  // D, [B,Hq,N]
+  int B, Hq, Hkv, N;
+  int causal;
+  float c;        // |scale| * log2(e)
+  float scale;    // signed scale, applied to dQ and dK
+  unsigned kneg;  // sign flip applied to the register-resident score operand when scale < 0
+  int nblk;       // key blocks (dK/dV) or query blocks (dQ) per head
+};
+
+template <int D>
+struct BwdCfg {
+  static constexpr int WAVES = 4;
+  static constexpr int RPW = 32;            // rows (keys or queries) each wave owns
+  static constexpr int BR = WAVES * RPW;    // rows per workgroup
+  static constexpr int BT = 64;             // rows per streamed tile
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int CH = D / 8;
+  static constexpr int RP = 16 / CH;
+  static constexpr int ROWB = D * 2;
+  static constexpr int TILE = BT * ROWB;
+  static constexpr int LPW = TILE / 1024 / WAVES;
+};
+
+// One swizzle for tiles read both as 16-byte rows (16 consecutive rows, one chunk) and by
+// transposing reads (4 consecutive rows x 4 consecutive chunks per half-wave): chunk c of
+// row r sits at c ^ swz(r); both access patterns then cover all 16 LDS bank groups.
+template <int D>
+__device__ __forceinline__ int swz_dual(int r) {
+  constexpr int CH = D / 8, RP = 16 / CH, Q4 = CH / 4;
+  const int i = r / RP;
+  return ((i % Q4) << 2) | ((i / Q4) & 3);
 }
+
+template <int D>
+__device__ __forceinline__ void load_tile_dual(__amdgpu_buffer_rsrc_t rs, lds_char* tile, int row0,
+                                               int wave, int lane) {
+  using C = BwdCfg<D>;
+#pragma unroll
+  for (int t = 0; t < C::LPW; ++t) {
+    const int blk = wave * C::LPW + t;
+    const int pos = blk * 1024 + lane * 16;
+    const int r = pos / C::ROWB;
+    const int cp = (pos % C::ROWB) / 16;
+    buffer_load16_lds(rs, tile + blk * 1024, (uint32_t)(row0 + r) * C::ROWB + ((cp ^ swz_dual<D>(r)) << 4));
+  }
 }
+
+// 16-byte row read (A operand, rows 32*blk + l%32, head-dim chunk 2*ks + half).
+template <int D>
+__device__ __forceinline__ int row_read_off(int lane, int ks) {
+  using C = BwdCfg<D>;
+  const int r = lane & 31;  // + 32*blk leaves the swizzle unchanged
+  return r * C::ROWB + (((2 * ks + (lane >> 5)) ^ swz_dual<D>(r)) << 4);
+}
+
+// Transposing read base (A operand = tile^T, head-dim block db) for tile rows
+// 8*upper + 4*(l/32) + (l%16)/4; adding 32*blk + 16*h leaves the swizzle unchanged, adding 8
+// does not, so the two reads of a fragment (rows +0 and +8) have separate bases.
+template <int D>
+__device__ __forceinline__ int tr_read_off(int lane, int db, int upper) {
+  using C = BwdCfg<D>;
+  const int r = 8 * upper + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int d = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  return r * C::ROWB + (((d >> 3) ^ swz_dual<D>(r)) << 4) + (d & 7) * 2;
+}
+
+__device__ __forceinline__ u32x4 tr_pair(const lds_char* lo_base, const lds_char* hi_base) {
+  const u32x2 lo = lds_read8_tr(lo_base);
+  const u32x2 hi = lds_read8_tr(hi_base);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// ------------------------------------------------------------------ 1. preprocess: D_i
+
+template <int D>
+__global__ __launch_bounds__(256) void fa2_bwd_pre_kernel(const float* __restrict__ o,
+                                                          const uint16_t* __restrict__ dO,
+                                                          float* __restrict__ delta, long rows) {
+  constexpr int LPR = D / 8;  // lanes per row, 8 elements each
+  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  const long row = gid / LPR;
+  const int part = (int)(gid % LPR);
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 g = *(const u32x4*)(dO + row * D + part * 8);
+    const f32x4 a = *(const f32x4*)(o + row * D + part * 8);
+    const f32x4 b = *(const f32x4*)(o + row * D + part * 8 + 4);
+    acc = __uint_as_float(g[0] << 16) * a[0] + __uint_as_float(g[0] & 0xffff0000u) * a[1] +
+          __uint_as_float(g[1] << 16) * a[2] + __uint_as_float(g[1] & 0xffff0000u) * a[3] +
+          __uint_as_float(g[2] << 16) * b[0] + __uint_as_float(g[2] & 0xffff0000u) * b[1] +
+          __uint_as_float(g[3] << 16) * b[2] + __uint_as_float(g[3] & 0xffff0000u) * b[3];
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+  if (row < rows && part == 0) delta[row] = acc;
+}
+
+// ------------------------------------------------------------------ 2. dK / dV
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa2_bwd_dkdv_kernel(BwdParams p) {
+  using C = BwdCfg<D>;
+  constexpr int STAGE = 2 * C::TILE + 2048;  // Q tile, dO tile, LSE[64] @0, D[64] @1024 B
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  lds_char* lds = (lds_char*)smem;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int N = p.N;
+  const int bid = blockIdx.x;
+  const int kblk = bid % p.nblk;  // causal: low key blocks see the most queries, go first
+  const int bg = bid / p.nblk;
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const int G = p.Hq / p.Hkv;
+  const int k0 = kblk * C::BR;
+  const int kw = k0 + wave * C::RPW;
+
+  const uint32_t head_bytes = (uint32_t)N * C::ROWB;
+  const size_t kvoff = ((size_t)b * p.Hkv + g) * (size_t)N * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + kvoff, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + kvoff, head_bytes);
+
+  // Query tiles: all query heads of the group, tiles from the one holding key k0 onward.
+  const int nqt_all = (N + C::BT - 1) / C::BT;
+  const int qt0 = p.causal ? k0 / C::BT : 0;
+  const int nqt = nqt_all - qt0;
+  const int iters = G * nqt;
+
+  auto issue = [&](int it, int stage) {
+    const int hq = g * G + it / nqt;
+    const int qrow0 = (qt0 + it % nqt) * C::BT;
+    const size_t qoff = ((size_t)b * p.Hq + hq) * (size_t)N * D;
+    lds_char* st = lds + stage * STAGE;
+    load_tile_dual<D>(make_rsrc(p.q + qoff, head_bytes), st, qrow0, wave, lane);
+    load_tile_dual<D>(make_rsrc(p.dO + qoff, head_bytes), st + C::TILE, qrow0, wave, lane);
+    if (wave == 0) {
+      // LSE of the tile's 64 rows -> stat[0, 256 B); D -> stat[1024, 1280 B). Lanes past 15
+      // address one past the end of the buffer and fill the rest with zeros.
+      const size_t roff = ((size_t)b * p.Hq + hq) * (size_t)N;
+      const uint32_t off = lane < 16 ? (uint32_t)(qrow0 + 4 * lane) * 4 : (uint32_t)N * 4;
+      buffer_load16_lds(make_rsrc(p.lse + roff, (uint32_t)N * 4), st + 2 * C::TILE, off);
+      buffer_load16_lds(make_rsrc(p.delta + roff, (uint32_t)N * 4), st + 2 * C::TILE + 1024, off);
+    }
+  };
+
+  if (iters > 0) issue(0, 0);
+
+  // K and V of this wave's 32 keys as B operands (lane = key, k = head dim).
+  u32x4 kf[C::KS], vf[C::KS];
+  {
+    const uint32_t row = (uint32_t)(kw + l32);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const uint32_t off = row * C::ROWB + (16 * ks + 8 * hf) * 2;
+      kf[ks] = buffer_load16(rk, off) ^ p.kneg;
+      vf[ks] = buffer_load16(rv, off);
+    }
+  }
+  int roff[C::KS], toff[C::DB], toff8[C::DB];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) roff[ks] = row_read_off<D>(lane, ks);
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    toff[db] = tr_read_off<D>(lane, db, 0);
+    toff8[db] = tr_read_off<D>(lane, db, 1);
+  }
+
+  f32x16 adk[C::DB], adv[C::DB];  // dK^T, dV^T: rows = head dim, columns = keys (lanes)
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    adk[db] = f32x16{};
+    adv[db] = f32x16{};
+  }
+  const float c = p.c;
+
+  wait_vmem_all();
+  __syncthreads();
+
+  for (int it = 0; it < iters; ++it) {
+    const int stage = it & 1;
+    if (it + 1 < iters) issue(it + 1, stage ^ 1);
+    const lds_char* qt = lds + stage * STAGE;
+    const lds_char* dot = qt + C::TILE;
+    const FA2_LDS float* rowstat = (const FA2_LDS float*)(qt + 2 * C::TILE);  // LSE @0, D @256 floats
+    const int qrow0 = (qt0 + it % nqt) * C::BT;
+
+    const bool skip = p.causal && qrow0 + C::BT - 1 < kw;
+    if (!skip) {
+      // ---- S = Q K^T and dP = dO V^T, [mb]: 32 queries x 32 keys ----
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        s[mb] = f32x16{};
+        dp[mb] = f32x16{};
+      }
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const u32x4 qa = lds_read16(qt + roff[ks] + mb * 32 * C::ROWB);
+          s[mb] = mfma32x32x16(qa, kf[ks], s[mb]);
+          const u32x4 da = lds_read16(dot + roff[ks] + mb * 32 * C::ROWB);
+          dp[mb] = mfma32x32x16(da, vf[ks], dp[mb]);
+        }
+      }
+      // ---- P = 2^(S c - LSE log2 e), dS = P (dP - D); registers hold query rows ----
+      const bool need_mask = (p.causal && qrow0 < kw + C::RPW - 1) || (qrow0 + C::BT > N);
+      const int key = kw + l32;
+      unsigned pp[2][8], pd[2][8];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int r0 = 32 * mb + 8 * rq + 4 * hf;  // tile rows r0..r0+3
+          const f32x4 lse4 = *(const FA2_LDS f32x4*)(rowstat + r0);
+          const f32x4 del4 = *(const FA2_LDS f32x4*)(rowstat + 256 + r0);
+          float pv[4], dsv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float pe = fast_exp2(__builtin_fmaf(s[mb][4 * rq + e], c, -lse4[e] * kLog2e));
+            if (need_mask) {
+              const int qi = qrow0 + r0 + e;
+              if (qi >= N || (p.causal && key > qi)) pe = 0.f;
+            }
+            pv[e] = pe;
+            dsv[e] = pe * (dp[mb][4 * rq + e] - del4[e]);
+          }
+          pp[mb][2 * rq] = pack_bf16(pv[0], pv[1]);
+          pp[mb][2 * rq + 1] = pack_bf16(pv[2], pv[3]);
+          pd[mb][2 * rq] = pack_bf16(dsv[0], dsv[1]);
+          pd[mb][2 * rq + 1] = pack_bf16(dsv[2], dsv[3]);
+        }
+      }
+      // ---- dV^T += dO^T P, dK^T += Q^T dS (contraction over the tile's 64 queries) ----
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int rowsel = (32 * mb + 16 * h) * C::ROWB;
+            const u32x4 dta = tr_pair(dot + toff[db] + rowsel, dot + toff8[db] + rowsel);
+            const u32x4 pb = {pp[mb][4 * h], pp[mb][4 * h + 1], pp[mb][4 * h + 2], pp[mb][4 * h + 3]};
+            adv[db] = mfma32x32x16(dta, pb, adv[db]);
+            const u32x4 qta = tr_pair(qt + toff[db] + rowsel, qt + toff8[db] + rowsel);
+            const u32x4 sb = {pd[mb][4 * h], pd[mb][4 * h + 1], pd[mb][4 * h + 2], pd[mb][4 * h + 3]};
+            adk[db] = mfma32x32x16(qta, sb, adk[db]);
+          }
+        }
+      }
+    }
+    wait_vmem_all();
+    __syncthreads();
+  }
+
+  // ---- store dK = scale dK^T^T, dV: lane = key, registers = head dim ----
+  const int key = kw + l32;
+  if (key < N) {
+    float* dkrow = p.dk + kvoff + (size_t)key * D;
+    float* dvrow = p.dv + kvoff + (size_t)key * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int col = 32 * db + 8 * rq + 4 * hf;
+        *(f32x4*)(dkrow + col) = f32x4{adk[db][4 * rq], adk[db][4 * rq + 1], adk[db][4 * rq + 2],
+                                       adk[db][4 * rq + 3]} * p.scale;
+        *(f32x4*)(dvrow + col) = f32x4{adv[db][4 * rq], adv[db][4 * rq + 1], adv[db][4 * rq + 2],
+                                       adv[db][4 * rq + 3]};
+      }
+  }
+}
+
+// ------------------------------------------------------------------ 3. dQ
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa2_bwd_dq_kernel(BwdParams p) {
+  using C = BwdCfg<D>;
+  constexpr int STAGE = 2 * C::TILE;  // K tile, V tile
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  lds_char* lds = (lds_char*)smem;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int N = p.N;
+  const int bid = blockIdx.x;
+  const int r = bid % p.nblk;
+  const int bh = bid / p.nblk;
+  const int qblk = p.causal ? p.nblk - 1 - r : r;  // longest rows first
+  const int b = bh / p.Hq, hq = bh % p.Hq;
+  const int hkv = hq / (p.Hq / p.Hkv);
+  const int q0 = qblk * C::BR;
+  const int qw = q0 + wave * C::RPW;
+
+  const uint32_t head_bytes = (uint32_t)N * C::ROWB;
+  const size_t qoff = (size_t)bh * N * D;
+  const size_t kvoff = ((size_t)b * p.Hkv + hkv) * (size_t)N * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + kvoff, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + kvoff, head_bytes);
+
+  const int qend = min(q0 + C::BR, N);
+  const int ntiles = p.causal ? (qend + C::BT - 1) / C::BT : (N + C::BT - 1) / C::BT;
+
+  load_tile_dual<D>(rk, lds, 0, wave, lane);
+  load_tile_dual<D>(rv, lds + C::TILE, 0, wave, lane);
+
+  // Q and dO of this wave's 32 queries as B operands (lane = query, k = head dim).
+  u32x4 qf[C::KS], df[C::KS];
+  const int qi = qw + l32;
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + qoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dO + qoff, head_bytes);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const uint32_t off = (uint32_t)qi * C::ROWB + (16 * ks + 8 * hf) * 2;
+      qf[ks] = buffer_load16(rq, off) ^ p.kneg;
+      df[ks] = buffer_load16(rd, off);
+    }
+  }
+  const float lse2 = (qi < N ? p.lse[(size_t)bh * N + qi] : 0.f) * kLog2e;
+  const float dlt = qi < N ? p.delta[(size_t)bh * N + qi] : 0.f;
+
+  int roff[C::KS], toff[C::DB], toff8[C::DB];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) roff[ks] = row_read_off<D>(lane, ks);
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    toff[db] = tr_read_off<D>(lane, db, 0);
+    toff8[db] = tr_read_off<D>(lane, db, 1);
+  }
+
+  f32x16 adq[C::DB];  // dQ^T: rows = head dim, columns = queries (lanes)
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) adq[db] = f32x16{};
+  const float c = p.c;
+
+  wait_vmem_all();
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int stage = t & 1;
+    if (t + 1 < ntiles) {
+      lds_char* nx = lds + (stage ^ 1) * STAGE;
+      load_tile_dual<D>(rk, nx, (t + 1) * C::BT, wave, lane);
+      load_tile_dual<D>(rv, nx + C::TILE, (t + 1) * C::BT, wave, lane);
+    }
+    const lds_char* kt = lds + stage * STAGE;
+    const lds_char* vt = kt + C::TILE;
+    const int j0 = t * C::BT;
+    const bool skip = p.causal && j0 > qw + C::RPW - 1;
+    if (!skip) {
+      // ---- S^T = K Q^T and dP^T = V dO^T, [kb]: 32 keys x 32 queries ----
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+        dp[kb] = f32x16{};
+      }
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const u32x4 ka = lds_read16(kt + roff[ks] + kb * 32 * C::ROWB);
+          s[kb] = mfma32x32x16(ka, qf[ks], s[kb]);
+          const u32x4 va = lds_read16(vt + roff[ks] + kb * 32 * C::ROWB);
+          dp[kb] = mfma32x32x16(va, df[ks], dp[kb]);
+        }
+      }
+      const bool need_mask = (p.causal && j0 + C::BT - 1 > qw) || (j0 + C::BT > N);
+      const int lim = p.causal ? min(qi, N - 1) : N - 1;
+      unsigned pd[2][8];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 16; rr += 2) {
+          float ds2[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            float pe = fast_exp2(__builtin_fmaf(s[kb][rr + e], c, -lse2));
+            if (need_mask) {
+              const int key = j0 + 32 * kb + 8 * ((rr + e) >> 2) + 4 * hf + ((rr + e) & 3);
+              if (key > lim) pe = 0.f;
+            }
+            ds2[e] = pe * (dp[kb][rr + e] - dlt);
+          }
+          pd[kb][rr >> 1] = pack_bf16(ds2[0], ds2[1]);
+        }
+      // ---- dQ^T += K^T dS^T (contraction over the tile's 64 keys) ----
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int rowsel = (32 * kb + 16 * h) * C::ROWB;
+            const u32x4 kta = tr_pair(kt + toff[db] + rowsel, kt + toff8[db] + rowsel);
+            const u32x4 sb = {pd[kb][4 * h], pd[kb][4 * h + 1], pd[kb][4 * h + 2], pd[kb][4 * h + 3]};
+            adq[db] = mfma32x32x16(kta, sb, adq[db]);
+          }
+    }
+    wait_vmem_all();
+    __syncthreads();
+  }
+
+  if (qi < N) {
+    float* dqrow = p.dq + qoff + (size_t)qi * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq)
+        *(f32x4*)(dqrow + 32 * db + 8 * rq + 4 * hf) =
+            f32x4{adq[db][4 * rq], adq[db][4 * rq + 1], adq[db][4 * rq + 2], adq[db][4 * rq + 3]} * p.scale;
+  }
+}
+
+// ------------------------------------------------------------------ launcher
+
+template <int D>
+static hipError_t launch_backward_d(BwdParams p, hipStream_t stream) {
+  using C = BwdCfg<D>;
+  const long rows = (long)p.B * p.Hq * p.N;
+  const long threads = rows * (D / 8);
+  hipLaunchKernelGGL(fa2_bwd_pre_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                     p.o, p.dO, p.delta, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  BwdParams pk = p;
+  pk.nblk = (p.N + C::BR - 1) / C::BR;
+  hipLaunchKernelGGL(fa2_bwd_dkdv_kernel<D>, dim3((unsigned)(p.B * p.Hkv * pk.nblk)), dim3(256), 0, stream, pk);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  BwdParams pq = p;
+  pq.nblk = (p.N + C::BR - 1) / C::BR;
+  hipLaunchKernelGGL(fa2_bwd_dq_kernel<D>, dim3((unsigned)(p.B * p.Hq * pq.nblk)), dim3(256), 0, stream, pq);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const void* q, const void* k, const void* v, const float* o,
+                           const float* lse, const void* dO, float* dq, float* dk, float* dv,
+                           const AttnShape& s, float* delta, hipStream_t stream) {
+  BwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = o;
+  p.lse = lse;
+  p.dO = static_cast<const uint16_t*>(dO);
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.delta = delta;
+  p.B = s.B;
+  p.Hq = s.Hq;
+  p.Hkv = s.Hkv;
+  p.N = s.N;
+  p.causal = s.causal;
+  p.c = fabsf(s.scale) * kLog2e;
+  p.scale = s.scale;
+  p.kneg = s.scale < 0.f ? 0x80008000u : 0u;
+  p.nblk = 0;
+  return s.d == 128 ? launch_backward_d<128>(p, stream) : launch_backward_d<64>(p, stream);
+}
+
+}  // namespace fa2

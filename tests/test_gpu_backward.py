@@ -1,0 +1,110 @@
+"""GPU backward parity: fa2_backward (fed by fa2_forward's O and LSE) against the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+
+import exact_tiled_attention_fa2_amd as fa2
+import oracle
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd_bwd(q, k, v, dO, causal, scale, stream=None):
+    import torch
+    qd, kd, vd, dod = H.to_dev(q), H.to_dev(k), H.to_dev(v), H.to_dev(dO)
+    o, lse = fa2.forward(qd, kd, vd, causal, scale, stream=stream)
+    dq, dk, dv = fa2.backward(qd, kd, vd, o, lse, dod, causal, scale, stream=stream)
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
+def check_backward(seed, B, Hq, Hkv, N, d, causal, scale=None, sample=None):
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    q, k, v, dO = H.make_inputs(seed, B, Hq, Hkv, N, d, with_do=True)
+    o, lse, dq, dk, dv = run_fwd_bwd(q, k, v, dO, causal, scale)
+    if sample is None:
+        qrows = np.tile(np.arange(N, dtype=np.int32), (B * Hq, 1))
+        krows = np.tile(np.arange(N, dtype=np.int32), (B * Hkv, 1))
+    else:
+        qrows = H.sample_rows(seed, B * Hq, N, sample)
+        krows = H.sample_rows(seed ^ 0xABCDEF, B * Hkv, N, sample)
+    rdq, rdk, rdv, _ = oracle.backward(H.f64(q), H.f64(k), H.f64(v), H.f64(dO), causal, scale,
+                                       qrows=qrows, krows=krows)
+    gdq, gdk, gdv = H.gather_rows(dq, qrows), H.gather_rows(dk, krows), H.gather_rows(dv, krows)
+    for name, g in (("dQ", gdq), ("dK", gdk), ("dV", gdv)):
+        assert np.all(np.isfinite(g)), name
+    eq, ek, ev = H.rel_l2(gdq, rdq), H.rel_l2(gdk, rdk), H.rel_l2(gdv, rdv)
+    print("bwd B=%d Hq=%d Hkv=%d N=%d d=%d causal=%d scale=%.4g: dQ %.3e dK %.3e dV %.3e"
+          % (B, Hq, Hkv, N, d, causal, scale, eq, ek, ev))
+    assert eq <= H.TOL_GRAD and ek <= H.TOL_GRAD and ev <= H.TOL_GRAD
+    return dq, dk, dv, dO
+
+
+def test_training_step_causal_sampled():
+    check_backward(0x5EED0005, 4, 16, 16, 4096, 128, True, sample=256)
+
+
+def test_small_full():
+    check_backward(0x5EED0001, 1, 2, 2, 256, 64, False)
+    check_backward(0x5EED0001, 1, 2, 2, 256, 128, True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 7, 63, 64, 65, 127, 128, 129, 200, 257, 500])
+def test_ragged_lengths(N, d, causal):
+    check_backward(2000 + N, 1, 2, 1, N, d, causal)
+
+
+@pytest.mark.parametrize("Hkv", [1, 2, 4, 8])
+def test_gqa_ratios(Hkv):
+    check_backward(3000 + Hkv, 2, 8, Hkv, 300, 128, True)
+    check_backward(3100 + Hkv, 1, 8, Hkv, 190, 64, False)
+
+
+@pytest.mark.parametrize("scale", [-0.15, 0.02, 0.7])
+def test_scales(scale):
+    check_backward(4000, 1, 4, 2, 250, 128, True, scale=scale)
+    check_backward(4001, 1, 2, 2, 130, 64, False, scale=scale)
+
+
+def test_gradient_invariants_on_gpu():
+    """sum_j dV_j = sum_i dO_i over the group, sum_j dK_j = 0 (per KV head)."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 700, 128
+    dq, dk, dv, dO = check_backward(4100, B, Hq, Hkv, N, d, True)
+    dv = dv.cpu().numpy().astype(np.float64); dk = dk.cpu().numpy().astype(np.float64)
+    do = H.f64(dO)
+    G = Hq // Hkv
+    for g in range(Hkv):
+        want = do[0, g * G:(g + 1) * G].sum(axis=(0, 1))
+        assert H.max_abs(dv[0, g].sum(axis=0), want) <= 2e-2 * max(1.0, np.abs(want).max())
+        assert np.abs(dk[0, g].sum(axis=0)).max() <= 2e-2 * np.abs(dk[0, g]).sum(axis=0).max()
+
+
+def test_backward_deterministic_and_stream():
+    import torch
+    q, k, v, dO = H.make_inputs(4200, 2, 8, 4, 900, 128, with_do=True)
+    a = run_fwd_bwd(q, k, v, dO, True, 0.1)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = run_fwd_bwd(q, k, v, dO, True, 0.1, stream=s)
+    s.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_backward_rejects_small_workspace():
+    import torch
+    q, k, v, dO = H.make_inputs(4300, 1, 2, 2, 64, 64, with_do=True)
+    qd, kd, vd, dod = H.to_dev(q), H.to_dev(k), H.to_dev(v), H.to_dev(dO)
+    o, lse = fa2.forward(qd, kd, vd, False, 0.125)
+    ws = torch.empty(16, dtype=torch.uint8, device=qd.device)
+    dq = torch.full((1, 2, 64, 64), 3.0, device=qd.device)
+    dk = torch.full((1, 2, 64, 64), 3.0, device=qd.device)
+    dv = torch.full((1, 2, 64, 64), 3.0, device=qd.device)
+    st = fa2.fa2_backward(qd, kd, vd, o, lse, dod, dq, dk, dv, 1, 2, 2, 64, 64, 0, 0.125, ws, 16)
+    assert st == 8
+    torch.cuda.synchronize()
+    assert bool((dq == 3).all() and (dk == 3).all() and (dv == 3).all())
