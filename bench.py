@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = the whole path on one batch: fa2_forward (O, LSE) then the three backward kernels
+(preprocess, dK/dV, dQ), on the causal prefill workload B=2, H=32, N=8192, d=128, bf16 inputs
+drawn from the seeded generator and resident in HBM before timing starts.
+
+Prints ONE JSON line on stdout. FLOPs follow the counting rule 4*B*H*N^2*d for a forward,
+halved when causal, and 2.5x that for the backward; the value is fwd+bwd TFLOP/s. Per-kernel
+durations come from HIP events recorded on the launch stream between the kernels of every
+timed step; the roofline object describes the longest-running kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s (fwd, fwd+bwd) bf16 causal d=128 N=8192; % MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = dict(B=2, Hq=32, Hkv=32, N=8192, d=128, causal=True)
+SEED = 0x5EED0006
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def counted_fwd_flops(B, Hq, N, d, causal):
+    f = 4.0 * B * Hq * N * N * d
+    return f / 2 if causal else f
+
+
+def cpu_baseline(q, k, v, dO, w, budget_s):
+    """The fp64 oracle on a bounded sample: whole (b, h) heads of the workload, forward and
+    backward in full, one head at a time until ``budget_s`` seconds have been spent."""
+    import numpy as np
+
+    import oracle
+    import seedgen
+    N, d, causal = w["N"], w["d"], w["causal"]
+    scale = 1.0 / math.sqrt(d)
+    cores = oracle.default_threads()
+    f64 = seedgen.bf16_bits_to_f64
+    done_heads, flops, elapsed = 0, 0.0, 0.0
+    for h in range(w["B"] * w["Hq"]):
+        b, hq = divmod(h, w["Hq"])
+        g = hq // (w["Hq"] // w["Hkv"])
+        qs, ks, vs, ds = (f64(x[b:b + 1, hh:hh + 1]) for x, hh in ((q, hq), (k, g), (v, g), (dO, hq)))
+        t0 = time.perf_counter()
+        oracle.forward(qs, ks, vs, causal, scale, threads=cores)
+        oracle.backward(qs, ks, vs, ds, causal, scale, threads=cores)
+        elapsed += time.perf_counter() - t0
+        done_heads += 1
+        flops += 3.5 * counted_fwd_flops(1, 1, N, d, causal)
+        if elapsed >= budget_s:
+            break
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "%d of %d (batch, head) slices of the workload, full fp64 forward + backward per slice "
+                  "(%.1f s; input generation not timed)" % (done_heads, w["B"] * w["Hq"], elapsed),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus %d (WORLD_SIZE=%d) is not supported"
+              % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_tiled_attention_fa2_amd as fa2
+    import seedgen
+
+    if not os.path.exists(fa2.LIB_PATH):
+        from exact_tiled_attention_fa2_amd import build as hipbuild
+        hipbuild.build()
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    w = WORKLOAD
+    B, Hq, Hkv, N, d, causal = w["B"], w["Hq"], w["Hkv"], w["N"], w["d"], w["causal"]
+    scale = 1.0 / math.sqrt(d)
+
+    q, k, v, dO = seedgen.attention_inputs(SEED, B, Hq, Hkv, N, d, with_do=True)
+
+    def up(x):
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    qd, kd, vd, dod = up(q), up(k), up(v), up(dO)
+    o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    dq = torch.empty_like(o)
+    dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    delta = torch.empty(fa2.fa2_backward_workspace_size(B, Hq, N) // 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    names = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
+
+    def step(events=None):
+        calls = [
+            lambda: fa2.fa2_forward(qd, kd, vd, o, lse, B, Hq, Hkv, N, d, causal, scale, stream),
+            lambda: fa2.fa2_backward_preprocess(o, dod, delta, B, Hq, N, d, stream),
+            lambda: fa2.fa2_backward_dkdv(qd, kd, vd, lse, delta, dod, dk, dv, B, Hq, Hkv, N, d, causal, scale, stream),
+            lambda: fa2.fa2_backward_dq(qd, kd, vd, lse, delta, dod, dq, B, Hq, Hkv, N, d, causal, scale, stream),
+        ]
+        for i, call in enumerate(calls):
+            if events is not None:
+                events[i].record(stream)
+            st = call()
+            if st != 0:
+                raise fa2.Fa2Error(st, names[i])
+        if events is not None:
+            events[len(calls)].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    per_kernel = {n: [] for n in names}
+    steps_ms = []
+    for s in range(args.steps):
+        for i, n in enumerate(names):
+            per_kernel[n].append(ev[s][i].elapsed_time(ev[s][i + 1]))
+        steps_ms.append(ev[s][0].elapsed_time(ev[s][4]))
+    avg = {n: float(np.mean(per_kernel[n])) for n in names}
+    ms_step = float(np.mean(steps_ms))
+
+    F = counted_fwd_flops(B, Hq, N, d, causal)
+    total = 3.5 * F
+    fwd_tflops = F / (avg["fwd"] * 1e-3) / 1e12
+    bwd_ms = avg["bwd_preprocess"] + avg["bwd_dkdv"] + avg["bwd_dq"]
+    value = total / (ms_step * 1e-3) / 1e12
+    # Algorithmic work per launch: MFMA FLOPs over the visible (query, key) pairs counted as
+    # B*H*N^2/2 when causal: forward 4d per pair, dK/dV 8d, dQ 6d; preprocess moves bytes.
+    pairs = B * Hq * N * N / (2 if causal else 1)
+    algo = {"fwd": ("mfma", pairs * 4 * d / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
+            "bwd_dkdv": ("mfma", pairs * 8 * d / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
+            "bwd_dq": ("mfma", pairs * 6 * d / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
+            "bwd_preprocess": ("hbm", B * Hq * N * (d * 6 + 4) / 1e9, "GB/s", PEAK_HBM_GBS)}
+    kernels = {}
+    for n in names:
+        bound, work, unit, peak = algo[n]
+        ach = work / (avg[n] * 1e-3)
+        kernels[n] = {"avg_ms": round(avg[n], 4), "achieved": round(ach, 1), "unit": unit,
+                      "frac": round(ach / peak, 4)}
+    dom = max(names, key=lambda n: avg[n])
+    bound, work, unit, peak = algo[dom]
+    achieved = work / (avg[dom] * 1e-3)
+    roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(q, k, v, dO, w, args.cpu_seconds)
+
+    props = torch.cuda.get_device_properties(0)
+    log("device %s, %d CUs; step %.3f ms (wall %.3f ms); fwd %.3f ms = %.1f TFLOP/s (%.1f%% peak); "
+        "bwd %.3f ms; fwd+bwd %.1f TFLOP/s (%.1f%%)" % (props.name, props.multi_processor_count, ms_step, wall_ms,
+                                                     avg["fwd"], fwd_tflops, 100 * fwd_tflops / PEAK_BF16_TFLOPS,
+                                                     bwd_ms, value, 100 * value / PEAK_BF16_TFLOPS))
+    for n in names:
+        log("  %-15s %8.3f ms  %9.1f %s  (%.1f%% of peak)" % (n, avg[n], kernels[n]["achieved"], kernels[n]["unit"],
+                                                             100 * kernels[n]["frac"]))
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded i.i.d. N(0,1) rounded to bf16)",
+        "config": {"workload": "causal prefill attention forward+backward, B=2 H=32 N=8192 d=128",
+                   "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "causal": causal,
+                   "global_batch": B, "seq_len": N, "parallelism": "single GPU"},
+        "fwd": {"ms": round(avg["fwd"], 4), "tflops": round(fwd_tflops, 1),
+                "frac_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4)},
+        "fwd_bwd": {"ms": round(ms_step, 4), "tflops": round(value, 1),
+                    "frac_peak": round(value / PEAK_BF16_TFLOPS, 4)},
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "peak_tflops": PEAK_BF16_TFLOPS,
+        "device": props.name,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

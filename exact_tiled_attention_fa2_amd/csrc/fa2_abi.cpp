@@ -43,6 +43,34 @@ int check_shape(int B, int Hq, int Hkv, int N, int d, float scale, bool* empty) 
   return FA2_OK;
 }
 
+struct Buf {
+  const void* p;
+  uint64_t bytes;
+};
+
+// NULL, alignment and overlap rules for one call: outputs must not overlap inputs or each
+// other; inputs may overlap each other (they are only read).
+int check_buffers(const Buf* in, int nin, const Buf* out, int nout) {
+  for (int i = 0; i < nin; ++i)
+    if (!in[i].p) return FA2_ERR_NULL_POINTER;
+  for (int i = 0; i < nout; ++i)
+    if (!out[i].p) return FA2_ERR_NULL_POINTER;
+  for (int i = 0; i < nin; ++i)
+    if (!aligned16(in[i].p)) return FA2_ERR_MISALIGNED;
+  for (int i = 0; i < nout; ++i)
+    if (!aligned16(out[i].p)) return FA2_ERR_MISALIGNED;
+  for (int i = 0; i < nout; ++i) {
+    const Range r = range_of(out[i].p, out[i].bytes);
+    for (int j = 0; j < nin; ++j)
+      if (overlaps(r, range_of(in[j].p, in[j].bytes))) return FA2_ERR_ALIASING;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlaps(r, range_of(out[j].p, out[j].bytes))) return FA2_ERR_ALIASING;
+  }
+  return FA2_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA2_OK : FA2_ERR_HIP; }
+
 }  // namespace
 
 extern "C" {
@@ -68,19 +96,13 @@ int fa2_forward(const void* q, const void* k, const void* v, float* o, float* ls
   bool empty = false;
   int st = check_shape(B, Hq, Hkv, N, d, scale, &empty);
   if (st != FA2_OK || empty) return st;
-  if (!q || !k || !v || !o || !lse) return FA2_ERR_NULL_POINTER;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-    return FA2_ERR_MISALIGNED;
-  const uint64_t rows_q = (uint64_t)B * Hq * N, rows_kv = (uint64_t)B * Hkv * N;
-  const Range in[3] = {range_of(q, rows_q * d * 2), range_of(k, rows_kv * d * 2),
-                       range_of(v, rows_kv * d * 2)};
-  const Range out[2] = {range_of(o, rows_q * d * 4), range_of(lse, rows_q * 4)};
-  for (const Range& r : out)
-    for (const Range& x : in)
-      if (overlaps(r, x)) return FA2_ERR_ALIASING;
-  if (overlaps(out[0], out[1])) return FA2_ERR_ALIASING;
+  const uint64_t rq = (uint64_t)B * Hq * N, rkv = (uint64_t)B * Hkv * N;
+  const Buf in[3] = {{q, rq * d * 2}, {k, rkv * d * 2}, {v, rkv * d * 2}};
+  const Buf out[2] = {{o, rq * d * 4}, {lse, rq * 4}};
+  st = check_buffers(in, 3, out, 2);
+  if (st != FA2_OK) return st;
   fa2::AttnShape s{B, Hq, Hkv, N, d, causal != 0, scale};
-  return fa2::launch_forward(q, k, v, o, lse, s, stream) == hipSuccess ? FA2_OK : FA2_ERR_HIP;
+  return hip_status(fa2::launch_forward(q, k, v, o, lse, s, stream));
 }
 
 size_t fa2_backward_workspace_size(int B, int Hq, int N) {
@@ -96,29 +118,70 @@ int fa2_backward(const void* q, const void* k, const void* v, const float* o, co
   bool empty = false;
   int st = check_shape(B, Hq, Hkv, N, d, scale, &empty);
   if (st != FA2_OK || empty) return st;
-  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA2_ERR_NULL_POINTER;
+  const uint64_t rq = (uint64_t)B * Hq * N, rkv = (uint64_t)B * Hkv * N;
+  const Buf in[6] = {{q, rq * d * 2}, {k, rkv * d * 2}, {v, rkv * d * 2},
+                     {o, rq * d * 4}, {lse, rq * 4},     {dO, rq * d * 2}};
+  const Buf out[3] = {{dq, rq * d * 4}, {dk, rkv * d * 4}, {dv, rkv * d * 4}};
+  st = check_buffers(in, 6, out, 3);
+  if (st != FA2_OK) return st;
   if (!workspace || workspace_bytes < fa2_backward_workspace_size(B, Hq, N))
     return FA2_ERR_WORKSPACE;
-  const void* ptrs[10] = {q, k, v, o, lse, dO, dq, dk, dv, workspace};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return FA2_ERR_MISALIGNED;
-  const uint64_t rows_q = (uint64_t)B * Hq * N, rows_kv = (uint64_t)B * Hkv * N;
-  const Range in[6] = {range_of(q, rows_q * d * 2),  range_of(k, rows_kv * d * 2),
-                       range_of(v, rows_kv * d * 2), range_of(o, rows_q * d * 4),
-                       range_of(lse, rows_q * 4),    range_of(dO, rows_q * d * 2)};
-  const Range out[4] = {range_of(dq, rows_q * d * 4), range_of(dk, rows_kv * d * 4),
-                        range_of(dv, rows_kv * d * 4),
-                        range_of(workspace, fa2_backward_workspace_size(B, Hq, N))};
-  for (int i = 0; i < 4; ++i) {
-    for (const Range& x : in)
-      if (overlaps(out[i], x)) return FA2_ERR_ALIASING;
-    for (int j = i + 1; j < 4; ++j)
-      if (overlaps(out[i], out[j])) return FA2_ERR_ALIASING;
-  }
+  const Buf all_in[9] = {in[0], in[1], in[2], in[3], in[4], in[5], out[0], out[1], out[2]};
+  const Buf ws[1] = {{workspace, fa2_backward_workspace_size(B, Hq, N)}};
+  st = check_buffers(all_in, 9, ws, 1);
+  if (st != FA2_OK) return st;
   fa2::AttnShape s{B, Hq, Hkv, N, d, causal != 0, scale};
-  hipError_t e = fa2::launch_backward(q, k, v, o, lse, dO, dq, dk, dv, s,
-                                      static_cast<float*>(workspace), stream);
-  return e == hipSuccess ? FA2_OK : FA2_ERR_HIP;
+  float* delta = static_cast<float*>(workspace);
+  hipError_t e = fa2::launch_bwd_preprocess(o, dO, delta, s, stream);
+  if (e == hipSuccess) e = fa2::launch_bwd_dkdv(q, k, v, lse, delta, dO, dk, dv, s, stream);
+  if (e == hipSuccess) e = fa2::launch_bwd_dq(q, k, v, lse, delta, dO, dq, s, stream);
+  return hip_status(e);
+}
+
+int fa2_backward_preprocess(const float* o, const void* dO, float* delta, int B, int Hq, int N,
+                            int d, hipStream_t stream) {
+  bool empty = false;
+  int st = check_shape(B, Hq, 1, N, d, 1.0f, &empty);
+  if (st != FA2_OK || empty) return st;
+  const uint64_t rq = (uint64_t)B * Hq * N;
+  const Buf in[2] = {{o, rq * d * 4}, {dO, rq * d * 2}};
+  const Buf out[1] = {{delta, rq * 4}};
+  st = check_buffers(in, 2, out, 1);
+  if (st != FA2_OK) return st;
+  fa2::AttnShape s{B, Hq, 1, N, d, 0, 1.0f};
+  return hip_status(fa2::launch_bwd_preprocess(o, dO, delta, s, stream));
+}
+
+int fa2_backward_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                      const float* delta, const void* dO, float* dk, float* dv, int B, int Hq,
+                      int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
+  bool empty = false;
+  int st = check_shape(B, Hq, Hkv, N, d, scale, &empty);
+  if (st != FA2_OK || empty) return st;
+  const uint64_t rq = (uint64_t)B * Hq * N, rkv = (uint64_t)B * Hkv * N;
+  const Buf in[6] = {{q, rq * d * 2}, {k, rkv * d * 2}, {v, rkv * d * 2},
+                     {lse, rq * 4},   {delta, rq * 4},  {dO, rq * d * 2}};
+  const Buf out[2] = {{dk, rkv * d * 4}, {dv, rkv * d * 4}};
+  st = check_buffers(in, 6, out, 2);
+  if (st != FA2_OK) return st;
+  fa2::AttnShape s{B, Hq, Hkv, N, d, causal != 0, scale};
+  return hip_status(fa2::launch_bwd_dkdv(q, k, v, lse, delta, dO, dk, dv, s, stream));
+}
+
+int fa2_backward_dq(const void* q, const void* k, const void* v, const float* lse,
+                    const float* delta, const void* dO, float* dq, int B, int Hq, int Hkv,
+                    int N, int d, int causal, float scale, hipStream_t stream) {
+  bool empty = false;
+  int st = check_shape(B, Hq, Hkv, N, d, scale, &empty);
+  if (st != FA2_OK || empty) return st;
+  const uint64_t rq = (uint64_t)B * Hq * N, rkv = (uint64_t)B * Hkv * N;
+  const Buf in[6] = {{q, rq * d * 2}, {k, rkv * d * 2}, {v, rkv * d * 2},
+                     {lse, rq * 4},   {delta, rq * 4},  {dO, rq * d * 2}};
+  const Buf out[1] = {{dq, rq * d * 4}};
+  st = check_buffers(in, 6, out, 1);
+  if (st != FA2_OK) return st;
+  fa2::AttnShape s{B, Hq, Hkv, N, d, causal != 0, scale};
+  return hip_status(fa2::launch_bwd_dq(q, k, v, lse, delta, dO, dq, s, stream));
 }
 
 }  // extern "C"

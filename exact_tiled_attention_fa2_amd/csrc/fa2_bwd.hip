@@ -450,42 +450,17 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   }
 }
 
-// ------------------------------------------------------------------ launcher
+// ------------------------------------------------------------------ launchers
 
-template <int D>
-static hipError_t launch_backward_d(BwdParams p, hipStream_t stream) {
-  using C = BwdCfg<D>;
-  const long rows = (long)p.B * p.Hq * p.N;
-  const long threads = rows * (D / 8);
-  hipLaunchKernelGGL(fa2_bwd_pre_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
-                     p.o, p.dO, p.delta, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  BwdParams pk = p;
-  pk.nblk = (p.N + C::BR - 1) / C::BR;
-  hipLaunchKernelGGL(fa2_bwd_dkdv_kernel<D>, dim3((unsigned)(p.B * p.Hkv * pk.nblk)), dim3(256), 0, stream, pk);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  BwdParams pq = p;
-  pq.nblk = (p.N + C::BR - 1) / C::BR;
-  hipLaunchKernelGGL(fa2_bwd_dq_kernel<D>, dim3((unsigned)(p.B * p.Hq * pq.nblk)), dim3(256), 0, stream, pq);
-  return hipGetLastError();
-}
-
-hipError_t launch_backward(const void* q, const void* k, const void* v, const float* o,
-                           const float* lse, const void* dO, float* dq, float* dk, float* dv,
-                           const AttnShape& s, float* delta, hipStream_t stream) {
-  BwdParams p;
+static BwdParams make_params(const void* q, const void* k, const void* v, const float* lse,
+                             const float* delta, const void* dO, const AttnShape& s) {
+  BwdParams p = {};
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
-  p.o = o;
   p.lse = lse;
   p.dO = static_cast<const uint16_t*>(dO);
-  p.dq = dq;
-  p.dk = dk;
-  p.dv = dv;
-  p.delta = delta;
+  p.delta = const_cast<float*>(delta);
   p.B = s.B;
   p.Hq = s.Hq;
   p.Hkv = s.Hkv;
@@ -494,8 +469,48 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const fl
   p.c = fabsf(s.scale) * kLog2e;
   p.scale = s.scale;
   p.kneg = s.scale < 0.f ? 0x80008000u : 0u;
-  p.nblk = 0;
-  return s.d == 128 ? launch_backward_d<128>(p, stream) : launch_backward_d<64>(p, stream);
+  return p;
+}
+
+hipError_t launch_bwd_preprocess(const float* o, const void* dO, float* delta, const AttnShape& s,
+                                 hipStream_t stream) {
+  const long rows = (long)s.B * s.Hq * s.N;
+  const long threads = rows * (s.d / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  if (s.d == 128)
+    hipLaunchKernelGGL(fa2_bwd_pre_kernel<128>, grid, block, 0, stream, o, (const uint16_t*)dO, delta, rows);
+  else
+    hipLaunchKernelGGL(fa2_bwd_pre_kernel<64>, grid, block, 0, stream, o, (const uint16_t*)dO, delta, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                           const float* delta, const void* dO, float* dk, float* dv,
+                           const AttnShape& s, hipStream_t stream) {
+  BwdParams p = make_params(q, k, v, lse, delta, dO, s);
+  p.dk = dk;
+  p.dv = dv;
+  p.nblk = (s.N + BwdCfg<128>::BR - 1) / BwdCfg<128>::BR;
+  const dim3 grid((unsigned)(s.B * s.Hkv * p.nblk)), block(256);
+  if (s.d == 128)
+    hipLaunchKernelGGL(fa2_bwd_dkdv_kernel<128>, grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL(fa2_bwd_dkdv_kernel<64>, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                         const float* delta, const void* dO, float* dq, const AttnShape& s,
+                         hipStream_t stream) {
+  BwdParams p = make_params(q, k, v, lse, delta, dO, s);
+  p.dq = dq;
+  p.nblk = (s.N + BwdCfg<128>::BR - 1) / BwdCfg<128>::BR;
+  const dim3 grid((unsigned)(s.B * s.Hq * p.nblk)), block(256);
+  if (s.d == 128)
+    hipLaunchKernelGGL(fa2_bwd_dq_kernel<128>, grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL(fa2_bwd_dq_kernel<64>, grid, block, 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace fa2

@@ -16,8 +16,15 @@ struct AttnShape {
 hipError_t launch_forward(const void* q, const void* k, const void* v, float* o, float* lse,
                           const AttnShape& s, hipStream_t stream);
 
-hipError_t launch_backward(const void* q, const void* k, const void* v, const float* o,
-                           const float* lse, const void* dO, float* dq, float* dk, float* dv,
-                           const AttnShape& s, float* delta, hipStream_t stream);
+hipError_t launch_bwd_preprocess(const float* o, const void* dO, float* delta, const AttnShape& s,
+                                 hipStream_t stream);
+
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                           const float* delta, const void* dO, float* dk, float* dv,
+                           const AttnShape& s, hipStream_t stream);
+
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                         const float* delta, const void* dO, float* dq, const AttnShape& s,
+                         hipStream_t stream);
 
 }  // namespace fa2

@@ -98,6 +98,28 @@ int fa2_backward(const void* q, const void* k, const void* v, const float* o, co
                  int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * The three steps of fa2_backward as separate calls, in the order fa2_backward runs them.
+ * Each validates its own arguments like fa2_backward (same codes) and enqueues one kernel.
+ * Running the three in order on one stream gives bitwise the results of fa2_backward.
+ *
+ * fa2_backward_preprocess: delta[i] = sum_c dO[i][c] * o[i][c] for every query row.
+ *   o f32 [B,Hq,N,d], dO bf16 [B,Hq,N,d] (read only); delta f32 [B,Hq,N] (written).
+ */
+int fa2_backward_preprocess(const float* o, const void* dO, float* delta, int B, int Hq, int N,
+                            int d, hipStream_t stream);
+
+/* fa2_backward_dkdv: dK, dV (f32 [B,Hkv,N,d], written) from q, k, v, lse, delta (the output of
+   fa2_backward_preprocess) and dO; recomputes P from lse, no atomics. */
+int fa2_backward_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                      const float* delta, const void* dO, float* dk, float* dv, int B, int Hq,
+                      int Hkv, int N, int d, int causal, float scale, hipStream_t stream);
+
+/* fa2_backward_dq: dQ (f32 [B,Hq,N,d], written) from the same inputs as fa2_backward_dkdv. */
+int fa2_backward_dq(const void* q, const void* k, const void* v, const float* lse,
+                    const float* delta, const void* dO, float* dq, int B, int Hq, int Hkv,
+                    int N, int d, int causal, float scale, hipStream_t stream);
+
 /* Static, human-readable name of a status code ("FA2_OK", ...); "FA2_UNKNOWN" otherwise. */
 const char* fa2_status_string(int status);
 

@@ -94,3 +94,18 @@ def test_backward_aliasing_and_workspace(lib):
     assert bwd(ws=None) == 8
     assert bwd(wsb=fa2.fa2_backward_workspace_size(1, 2, 128) - 1) == 8
     assert bwd(ws=P(9) + 4) == 6
+
+
+def test_phase_entry_points_validate(lib):
+    ok = dict(B=1, Hq=2, Hkv=1, N=64, d=64)
+    assert fa2.fa2_backward_preprocess(P(3), P(5), P(9), 1, 2, 64, 96) == 3
+    assert fa2.fa2_backward_preprocess(P(3), P(5), P(3) + 64, 1, 2, 64, 64) == 7
+    assert fa2.fa2_backward_preprocess(None, P(5), P(9), 1, 2, 64, 64) == 1
+    assert fa2.fa2_backward_preprocess(P(3), P(5), P(9), 0, 2, 64, 64) == 0
+    args = [P(0), P(1), P(2), P(4), P(9), P(5)]
+    assert fa2.fa2_backward_dkdv(*args, P(7), P(8), 1, 2, 1, 64, 128, 1, float("nan")) == 5
+    assert fa2.fa2_backward_dkdv(*args, P(7), P(7), 1, 2, 1, 64, 64, 1, 0.1) == 7
+    assert fa2.fa2_backward_dkdv(*args, P(7), P(8), 1, 3, 2, 64, 64, 1, 0.1) == 4
+    assert fa2.fa2_backward_dq(*args, P(0), 1, 2, 1, 64, 64, 1, 0.1) == 7
+    assert fa2.fa2_backward_dq(*args, P(6) + 4, 1, 2, 1, 64, 64, 1, 0.1) == 6
+    assert fa2.fa2_backward_dq(*args, P(6), 1, 2, 1, 64, 32, 1, 0.1) == 3
