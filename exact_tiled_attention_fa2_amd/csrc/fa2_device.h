@@ -86,6 +86,27 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// An empty asm statement with an AGPR operand. Its presence tells the compiler that the kernel
+// uses AGPRs, which makes it select the AGPR-accumulator form of MFMA: the O accumulators then
+// stay in AGPRs across the loop instead of being copied out and back every iteration.
+__device__ __forceinline__ void agpr_accumulators_hint() { asm volatile("" ::"a"(0.0f)); }
+
+// Hides a value's origin from the optimiser (no instruction is emitted), so address
+// arithmetic on it is not re-associated and hoisted into many loop-invariant registers.
+template <typename T>
+__device__ __forceinline__ T opaque(T x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Marks an accumulator as redefined here, in AGPRs (no instruction is emitted): copies of it
+// into VGPRs cannot be scheduled above this point.
+__device__ __forceinline__ void pin_agpr(f32x16& x) { asm volatile("" : "+a"(x)); }
+
+// The VGPR counterpart: score accumulators are consumed by VALU code, so keeping them in
+// VGPRs avoids a copy out of AGPRs per register.
+__device__ __forceinline__ void pin_vgpr(f32x16& x) { asm volatile("" : "+v"(x)); }
+
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace fa2

@@ -22,6 +22,8 @@
 //  * Scale folded into the exponent: p = 2^(s*c - m) with c = |scale|*log2(e); a negative
 //    scale flips the sign of the Q operand instead. The accumulator rescale is skipped when
 //    no row max in the wave changed.
+#include <type_traits>
+
 #include "fa2_device.h"
 #include "fa2_launch.h"
 
@@ -44,8 +46,9 @@ struct FwdParams {
 template <int D>
 struct FwdCfg {
   static constexpr int BN = 64;               // keys per tile
-  static constexpr int WAVES = 4;
-  static constexpr int QPW = 64;              // query rows per wave
+  static constexpr int WAVES = 8;             // two waves per SIMD
+  static constexpr int QPW = 32;              // query rows per wave
+  static constexpr int NQB = QPW / 32;        // 32-row MFMA blocks per wave
   static constexpr int BM = WAVES * QPW;      // query rows per workgroup
   static constexpr int KS = D / 16;           // k-steps of the Q.K contraction
   static constexpr int DB = D / 32;           // 32-wide blocks of the head dim
@@ -103,17 +106,28 @@ __device__ __forceinline__ void map_block(int bid, const FwdParams& p, int& bh, 
   qblk = p.causal ? p.nqb - 1 - r : r;  // causal: longest rows first
 }
 
+// Online softmax with a reference that is raised only when needed. The exponentials of a
+// tile are taken against the row's reference m (log2 domain), p = 2^(s c - m). All terms of
+// a row share the reference, so any m gives the same softmax; m only has to keep p small.
+// Before a tile's exponentials are formed, m is raised to that tile's row max -- rescaling O
+// and l -- if the max exceeds m by more than kRescaleSlack; so p <= 2^kRescaleSlack and the
+// 64 accumulator registers of a row block are rescaled only when a max really moves.
+constexpr float kRescaleSlack = 8.0f;
+
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa2_fwd_kernel(FwdParams p) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE];
-  lds_char* lds = (lds_char*)smem;
-  // stage s: K at lds + 2*s*TILE, V at lds + (2*s+1)*TILE
+  // Two K and two V stages in separate arrays: a DMA into one array and LDS reads of another
+  // are then provably independent, so reads never wait on an unrelated in-flight DMA.
+  __shared__ __attribute__((aligned(1024))) char k_st0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char k_st1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char v_st0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char v_st1[C::TILE];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int hf = lane >> 5;  // which half of the wave
+  const int hf = lane >> 5;
   const int l32 = lane & 31;
 
   int bh, qblk;
@@ -122,7 +136,7 @@ void fa2_fwd_kernel(FwdParams p) {
   const int hkv = hq / (p.Hq / p.Hkv);
   const int N = p.N;
   const int q0 = qblk * C::BM;
-  const int qlo = q0 + wave * C::QPW;  // this wave's first query row
+  const int qlo = q0 + wave * C::QPW;
 
   const uint32_t head_bytes = (uint32_t)N * C::ROWB;
   const size_t qoff = (size_t)bh * N * D;
@@ -131,35 +145,39 @@ void fa2_fwd_kernel(FwdParams p) {
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + kvoff, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + kvoff, head_bytes);
 
+  // Tiles of the workgroup, tiles this wave computes (causal: up to its last row), and the
+  // leading tiles that need no mask for this wave.
   const int qend = min(q0 + C::BM, N);
   const int ntiles = p.causal ? (qend + C::BN - 1) / C::BN : (N + C::BN - 1) / C::BN;
+  const int nmine = p.causal ? min(ntiles, (qlo + C::QPW - 1) / C::BN + 1) : ntiles;
+  const int nfree = min(nmine, p.causal ? (qlo + 1) / C::BN : N / C::BN);
 
-  // Start the first K/V tile while Q is fetched into registers.
-  load_tile<D, false>(rk, lds, 0, wave, lane);
-  load_tile<D, true>(rv, lds + C::TILE, 0, wave, lane);
+  // K and V of tile t are fetched one tile ahead into stage t % 2.
+  auto fetch_k = [&](int t) {
+    if (t < ntiles) load_tile<D, false>(rk, (t & 1) ? (lds_char*)k_st1 : (lds_char*)k_st0, t * C::BN, wave, lane);
+  };
+  auto fetch_v = [&](int t) {
+    if (t < ntiles) load_tile<D, true>(rv, (t & 1) ? (lds_char*)v_st1 : (lds_char*)v_st0, t * C::BN, wave, lane);
+  };
 
   // Q as the B operand of S^T = K Q^T: lane holds query l32, head-dim k = 16*ks + 8*hf + e.
-  u32x4 qf[2][C::KS];
+  u32x4 qf[C::NQB][C::KS];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < C::NQB; ++qb) {
     const uint32_t row = (uint32_t)(qlo + qb * 32 + l32);
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      u32x4 x = buffer_load16(rq, row * C::ROWB + (16 * ks + 8 * hf) * 2);
-      qf[qb][ks] = x ^ p.qneg;
-    }
+    for (int ks = 0; ks < C::KS; ++ks)
+      qf[qb][ks] = buffer_load16(rq, row * C::ROWB + (16 * ks + 8 * hf) * 2) ^ p.qneg;
   }
+  fetch_k(0);
+  fetch_v(0);
 
-  // Per-lane LDS read offsets (the swizzles depend on the lane, not on the tile).
-  int koff[C::KS];  // K A-operand row l32 (+32 per key block), chunk 2*ks + hf
+  int koff[C::KS];  // K A-operand: row l32 (+32 per key block), chunk 2*ks + hf
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-    const int r = l32;  // swz_k(r + 32) == swz_k(r) for both head dims
-    koff[ks] = r * C::ROWB + (((2 * ks + hf) ^ swz_k<D>(r)) << 4);
-  }
-  int voff[C::DB];  // V^T A-operand: transposing read base for each 32-wide head-dim block
+  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = l32 * C::ROWB + (((2 * ks + hf) ^ swz_k<D>(l32)) << 4);
+  int voff[C::DB];  // V^T A-operand: transposing read base per 32-wide head-dim block
   {
-    const int r = 4 * hf + ((lane & 15) >> 2);  // + 32*kb + 16*h (+8): swz_v unchanged
+    const int r = 4 * hf + ((lane & 15) >> 2);  // + 32*kb + 16*h (+8) leaves swz_v unchanged
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
       const int d = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -167,118 +185,155 @@ void fa2_fwd_kernel(FwdParams p) {
     }
   }
 
-  f32x16 acc[2][C::DB];
+  f32x16 acc[C::NQB][C::DB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) acc[qb][db] = f32x16{};
-  float m[2] = {-INFINITY, -INFINITY};
-  float l[2] = {0.f, 0.f};
+  float m[C::NQB];        // reference (log2 domain) per query row, -inf before tile 0
+  float l[C::NQB];        // this lane's partial row sum relative to m
+#pragma unroll
+  for (int qb = 0; qb < C::NQB; ++qb) {
+    l[qb] = 0.f;
+    m[qb] = -INFINITY;
+  }
   const float c = p.c;
 
-  wait_vmem_all();
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int st = t & 1;
-    const lds_char* kt = lds + (2 * st) * C::TILE;
-    const lds_char* vt = lds + (2 * st + 1) * C::TILE;
-    if (t + 1 < ntiles) {
-      lds_char* kn = lds + (2 * (st ^ 1)) * C::TILE;
-      load_tile<D, false>(rk, kn, (t + 1) * C::BN, wave, lane);
-      load_tile<D, true>(rv, kn + C::TILE, (t + 1) * C::BN, wave, lane);
-    }
-    const int j0 = t * C::BN;
-    const bool skip = p.causal && j0 > qlo + C::QPW - 1;
-    if (!skip) {
-      // ---- S^T = K_j Q^T : [qb][kb] blocks of 32 keys x 32 queries ----
-      f32x16 s[2][2];
+  auto s_tile = [&](const lds_char* kt, f32x16 (&s)[C::NQB][2]) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[qb][kb] = f32x16{};
+      for (int kb = 0; kb < 2; ++kb) s[qb][kb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
+    for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 kf = lds_read16(kt + koff[ks] + kb * 32 * C::ROWB);
+      for (int kb = 0; kb < 2; ++kb) {
+        const u32x4 kf = lds_read16(kt + koff[ks] + kb * 32 * C::ROWB);
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) s[qb][kb] = mfma32x32x16(kf, qf[qb][ks], s[qb][kb]);
-        }
+        for (int qb = 0; qb < C::NQB; ++qb) s[qb][kb] = mfma32x32x16(kf, qf[qb][ks], s[qb][kb]);
       }
-      // ---- mask: only tiles crossing the diagonal or the end of the sequence ----
-      const bool need_mask = (j0 + C::BN > N) || (p.causal && j0 + C::BN - 1 > qlo);
-      if (need_mask) {
+  };
+  // Row max of a tile's scores (log2 domain, both wave halves), masking first if asked.
+  auto max_tile = [&](f32x16 (&s)[C::NQB][2], bool mask, int j0, float (&mt)[C::NQB]) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int qi = qlo + qb * 32 + l32;
-          const int lim = p.causal ? min(qi, N - 1) : N - 1;  // last visible key
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-              if (key > lim) s[qb][kb][r] = -INFINITY;
-            }
-        }
-      }
-      // ---- online softmax; P^T packed to bf16 pairs ----
-      unsigned pk[2][2][8];  // [qb][kb][pair]
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float mt = s[qb][0][0];
+    for (int qb = 0; qb < C::NQB; ++qb) {
+      if (mask) {
+        const int qi = qlo + qb * 32 + l32;
+        const int lim = p.causal ? min(qi, N - 1) : N - 1;  // last visible key
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[qb][kb][r]);
-        mt = max_halves(mt);
-        const float mnew = fmaxf(m[qb], mt * c);
-        const float alpha = fast_exp2(m[qb] - mnew);
-        m[qb] = mnew;
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            const float p0 = fast_exp2(__builtin_fmaf(s[qb][kb][r], c, -mnew));
-            const float p1 = fast_exp2(__builtin_fmaf(s[qb][kb][r + 1], c, -mnew));
-            rs += p0 + p1;
-            pk[qb][kb][r >> 1] = pack_bf16(p0, p1);
+          for (int r = 0; r < 16; ++r) {
+            const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (key > lim) s[qb][kb][r] = -INFINITY;
           }
-        l[qb] = l[qb] * alpha + rs;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) acc[qb][db] *= alpha;
-        }
       }
-      // ---- O^T += V_j^T P^T ----
+      float x = s[qb][0][0];
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const lds_char* base = vt + voff[db] + (32 * kb + 16 * h) * C::ROWB;
-            const u32x2 lo = lds_read8_tr(base);
-            const u32x2 hi = lds_read8_tr(base + 8 * C::ROWB);
-            const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-              const u32x4 pf = {pk[qb][kb][4 * h], pk[qb][kb][4 * h + 1], pk[qb][kb][4 * h + 2],
-                                pk[qb][kb][4 * h + 3]};
-              acc[qb][db] = mfma32x32x16(vf, pf, acc[qb][db]);
-            }
-          }
-        }
-      }
+        for (int r = 0; r < 16; ++r) x = fmaxf(x, s[qb][kb][r]);
+      mt[qb] = max_halves(x) * c;
     }
+  };
+  auto exp_tile = [&](f32x16 (&s)[C::NQB][2], unsigned (&pk)[C::NQB][2][8]) {
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) {
+      float sum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(__builtin_fmaf(s[qb][kb][r], c, -m[qb]));
+          const float p1 = fast_exp2(__builtin_fmaf(s[qb][kb][r + 1], c, -m[qb]));
+          sum += p0 + p1;
+          pk[qb][kb][r >> 1] = pack_bf16(p0, p1);
+        }
+      l[qb] += sum;
+    }
+  };
+  auto pv_tile = [&](const lds_char* vt, unsigned (&pk)[C::NQB][2][8]) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      // One opaque base per head-dim block: each read is base + a constant folded into the
+      // instruction's offset field, not a hoisted address register.
+      const lds_char* vb = opaque(vt + voff[db]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const lds_char* base = vb + (32 * kb + 16 * h) * C::ROWB;
+          const u32x2 lo = lds_read8_tr(base);
+          const u32x2 hi = lds_read8_tr(base + 8 * C::ROWB);
+          const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+          for (int qb = 0; qb < C::NQB; ++qb) {
+            const u32x4 pf = {pk[qb][kb][4 * h], pk[qb][kb][4 * h + 1], pk[qb][kb][4 * h + 2],
+                              pk[qb][kb][4 * h + 3]};
+            acc[qb][db] = mfma32x32x16(vf, pf, acc[qb][db]);
+          }
+        }
+    }
+  };
+  auto sync_stage = [&]() {
     wait_vmem_all();
     __syncthreads();
+  };
+
+  // One tile: fetch tile t+1 into the other stage, S = K Q^T, mask (diagonal / ragged tiles
+  // only), row max, raise the reference if the max moved past the slack, P, O += P V.
+  auto step = [&](auto par_tag, auto mask_tag, int t) {
+    constexpr int PAR = decltype(par_tag)::value;  // t % 2
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const lds_char* kt = (const lds_char*)(PAR ? k_st1 : k_st0);
+    const lds_char* vt = (const lds_char*)(PAR ? v_st1 : v_st0);
+    fetch_k(t + 1);
+    fetch_v(t + 1);
+    f32x16 s[C::NQB][2];
+    s_tile(kt, s);
+    float mt[C::NQB];
+    max_tile(s, MASK, t * C::BN, mt);
+    bool grow = false;
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) grow |= mt[qb] > m[qb] + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+      for (int qb = 0; qb < C::NQB; ++qb) {
+        const float mnew = fmaxf(m[qb], mt[qb]);
+        const float alpha = fast_exp2(m[qb] - mnew);  // 0 on the first tile (m = -inf)
+        m[qb] = mnew;
+        l[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) acc[qb][db] *= alpha;
+      }
+    }
+    unsigned pk[C::NQB][2][8];
+    exp_tile(s, pk);
+    pv_tile(vt, pk);
+    sync_stage();
+  };
+
+  sync_stage();  // Q, K(0), V(0) have landed
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  int t = 0;
+  for (; t < nfree; ++t) {
+    if (t & 1) step(P1{}, std::false_type{}, t);
+    else step(P0{}, std::false_type{}, t);
+  }
+  for (; t < nmine; ++t) {
+    if (t & 1) step(P1{}, std::true_type{}, t);
+    else step(P0{}, std::true_type{}, t);
+  }
+  for (; t < ntiles; ++t) {  // tiles above this wave's rows: keep the shared fetch cadence
+    fetch_k(t + 1);
+    fetch_v(t + 1);
+    sync_stage();
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < C::NQB; ++qb) {
     const float lt = sum_halves(l[qb]);
     const float inv = 1.0f / lt;
     const int row = qlo + qb * 32 + l32;
@@ -315,7 +370,7 @@ hipError_t launch_forward(const void* q, const void* k, const void* v, float* o,
   const int BM = FwdCfg<128>::BM;
   p.nqb = (s.N + BM - 1) / BM;
   p.xcd_remap = ((s.B * s.Hq) % 8) == 0;
-  const dim3 grid((unsigned)(s.B * s.Hq * p.nqb)), block(256);
+  const dim3 grid((unsigned)(s.B * s.Hq * p.nqb)), block(FwdCfg<128>::WAVES * 64);
   if (s.d == 128)
     hipLaunchKernelGGL(fa2_fwd_kernel<128>, grid, block, 0, stream, p);
   else
