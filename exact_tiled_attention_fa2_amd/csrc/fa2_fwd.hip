@@ -199,19 +199,31 @@ void fa2_fwd_kernel(FwdParams p) {
   }
   const float c = p.c;
 
+  // S^T = K Q^T. K fragments are read one k-step ahead of the MFMAs that use them; the
+  // scheduling fences keep that order (left alone, the scheduler serialises each read with
+  // its MFMAs to save registers and exposes the full LDS latency every k-step).
   auto s_tile = [&](const lds_char* kt, f32x16 (&s)[C::NQB][2]) {
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[qb][kb] = f32x16{};
+    u32x4 kf[2][2];
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
+    for (int kb = 0; kb < 2; ++kb) kf[0][kb] = lds_read16(kt + koff[0] + kb * 32 * C::ROWB);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 kf = lds_read16(kt + koff[ks] + kb * 32 * C::ROWB);
+    for (int ks = 0; ks < C::KS; ++ks) {
+      if (ks + 1 < C::KS) {
 #pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb) s[qb][kb] = mfma32x32x16(kf, qf[qb][ks], s[qb][kb]);
+        for (int kb = 0; kb < 2; ++kb)
+          kf[(ks + 1) & 1][kb] = lds_read16(kt + koff[ks + 1] + kb * 32 * C::ROWB);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) s[qb][kb] = mfma32x32x16(kf[ks & 1][kb], qf[qb][ks], s[qb][kb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   // Row max of a tile's scores (log2 domain, both wave halves), masking first if asked.
   auto max_tile = [&](f32x16 (&s)[C::NQB][2], bool mask, int j0, float (&mt)[C::NQB]) {
@@ -236,7 +248,10 @@ void fa2_fwd_kernel(FwdParams p) {
       mt[qb] = max_halves(x) * c;
     }
   };
-  auto exp_tile = [&](f32x16 (&s)[C::NQB][2], unsigned (&pk)[C::NQB][2][8]) {
+  // P^T of a tile as MFMA B operands [qb][kb][h] (16 keys x 32 queries, packed bf16), built in
+  // place so the MFMAs read them without register copies.
+  typedef u32x4 PTile[C::NQB][2][2];
+  auto exp_tile = [&](f32x16 (&s)[C::NQB][2], PTile& pk) {
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) {
       float sum = 0.f;
@@ -247,32 +262,32 @@ void fa2_fwd_kernel(FwdParams p) {
           const float p0 = fast_exp2(__builtin_fmaf(s[qb][kb][r], c, -m[qb]));
           const float p1 = fast_exp2(__builtin_fmaf(s[qb][kb][r + 1], c, -m[qb]));
           sum += p0 + p1;
-          pk[qb][kb][r >> 1] = pack_bf16(p0, p1);
+          pk[qb][kb][r >> 3][(r >> 1) & 3] = pack_bf16(p0, p1);
         }
       l[qb] += sum;
     }
   };
-  auto pv_tile = [&](const lds_char* vt, unsigned (&pk)[C::NQB][2][8]) {
+  // O^T += V^T P^T. The V^T fragment of the next (db, kb, h) step is read while the MFMAs
+  // of the current one run; fences keep that order.
+  auto pv_tile = [&](const lds_char* vt, PTile& pk) {
+    constexpr int NSTEP = C::DB * 4;
+    auto vread = [&](int i) {
+      const int db = i >> 2, kb = (i >> 1) & 1, h = i & 1;
+      const lds_char* base = vt + voff[db] + (32 * kb + 16 * h) * C::ROWB;
+      const u32x2 lo = lds_read8_tr(base);
+      const u32x2 hi = lds_read8_tr(base + 8 * C::ROWB);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4 vf[2];
+    vf[0] = vread(0);
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-      // One opaque base per head-dim block: each read is base + a constant folded into the
-      // instruction's offset field, not a hoisted address register.
-      const lds_char* vb = opaque(vt + voff[db]);
+    for (int i = 0; i < NSTEP; ++i) {
+      if (i + 1 < NSTEP) vf[(i + 1) & 1] = vread(i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const int db = i >> 2, kb = (i >> 1) & 1, h = i & 1;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const lds_char* base = vb + (32 * kb + 16 * h) * C::ROWB;
-          const u32x2 lo = lds_read8_tr(base);
-          const u32x2 hi = lds_read8_tr(base + 8 * C::ROWB);
-          const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-          for (int qb = 0; qb < C::NQB; ++qb) {
-            const u32x4 pf = {pk[qb][kb][4 * h], pk[qb][kb][4 * h + 1], pk[qb][kb][4 * h + 2],
-                              pk[qb][kb][4 * h + 3]};
-            acc[qb][db] = mfma32x32x16(vf, pf, acc[qb][db]);
-          }
-        }
+      for (int qb = 0; qb < C::NQB; ++qb) acc[qb][db] = mfma32x32x16(vf[i & 1], pk[qb][kb][h], acc[qb][db]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   auto sync_stage = [&]() {
@@ -303,11 +318,14 @@ void fa2_fwd_kernel(FwdParams p) {
         const float alpha = fast_exp2(m[qb] - mnew);  // 0 on the first tile (m = -inf)
         m[qb] = mnew;
         l[qb] *= alpha;
+        // Scaled through a zero-operand MFMA: every definition of an accumulator is then an
+        // MFMA result, and the allocator keeps one register home for it around this branch.
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) acc[qb][db] *= alpha;
+        for (int db = 0; db < C::DB; ++db)
+          acc[qb][db] = mfma32x32x16(u32x4{}, u32x4{}, acc[qb][db] * alpha);
       }
     }
-    unsigned pk[C::NQB][2][8];
+    PTile pk;
     exp_tile(s, pk);
     pv_tile(vt, pk);
     sync_stage();
@@ -316,14 +334,22 @@ void fa2_fwd_kernel(FwdParams p) {
   sync_stage();  // Q, K(0), V(0) have landed
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
+  // Steps run in pairs (stage 0 then stage 1) so each step names its LDS arrays statically and
+  // no branch merges the accumulators; a masked step on an unmasked tile is merely slower, so
+  // an odd unmasked count hands its last tile to the masked loop.
   int t = 0;
-  for (; t < nfree; ++t) {
-    if (t & 1) step(P1{}, std::false_type{}, t);
-    else step(P0{}, std::false_type{}, t);
+  const int nfree_even = nfree & ~1;
+  for (; t < nfree_even; t += 2) {
+    step(P0{}, std::false_type{}, t);
+    step(P1{}, std::false_type{}, t + 1);
   }
-  for (; t < nmine; ++t) {
-    if (t & 1) step(P1{}, std::true_type{}, t);
-    else step(P0{}, std::true_type{}, t);
+  for (; t + 1 < nmine; t += 2) {
+    step(P0{}, std::true_type{}, t);
+    step(P1{}, std::true_type{}, t + 1);
+  }
+  if (t < nmine) {
+    step(P0{}, std::true_type{}, t);
+    ++t;
   }
   for (; t < ntiles; ++t) {  // tiles above this wave's rows: keep the shared fetch cadence
     fetch_k(t + 1);
