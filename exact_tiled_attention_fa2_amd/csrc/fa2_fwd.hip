@@ -152,7 +152,7 @@ void fa2_fwd_kernel(FwdParams p) {
   const int nmine = p.causal ? min(ntiles, (qlo + C::QPW - 1) / C::BN + 1) : ntiles;
   const int nfree = min(nmine, p.causal ? (qlo + 1) / C::BN : N / C::BN);
 
-  // K and V of tile t are fetched one tile ahead into stage t % 2.
+  // Tile t goes to stage t % 2: K two tiles ahead of its use, V one tile ahead.
   auto fetch_k = [&](int t) {
     if (t < ntiles) load_tile<D, false>(rk, (t & 1) ? (lds_char*)k_st1 : (lds_char*)k_st0, t * C::BN, wave, lane);
   };
@@ -171,6 +171,7 @@ void fa2_fwd_kernel(FwdParams p) {
   }
   fetch_k(0);
   fetch_v(0);
+  fetch_k(1);
 
   int koff[C::KS];  // K A-operand: row l32 (+32 per key block), chunk 2*ks + hf
 #pragma unroll
@@ -199,123 +200,109 @@ void fa2_fwd_kernel(FwdParams p) {
   }
   const float c = p.c;
 
-  // S^T = K Q^T. K fragments are read one k-step ahead of the MFMAs that use them; the
-  // scheduling fences keep that order (left alone, the scheduler serialises each read with
-  // its MFMAs to save registers and exposes the full LDS latency every k-step).
-  auto s_tile = [&](const lds_char* kt, f32x16 (&s)[C::NQB][2]) {
+  // Scores of one tile: S^T blocks [qb][kb] of 32 keys x 32 queries.
+  typedef f32x16 STile[C::NQB][2];
+  // P^T of a tile as MFMA B operands [qb][kb][h] (16 keys x 32 queries, packed bf16), built in
+  // place so the MFMAs read them without register copies.
+  typedef u32x4 PTile[C::NQB][2][2];
+  constexpr int NPV = 4 * C::DB;  // PV MFMA steps per tile (per query block)
+  constexpr int EXP_SLICE = 32 / C::KS;  // score elements exponentiated per S k-step
+  constexpr int MAX_SLICE = 32 / NPV;    // score elements max-reduced per PV step
+
+  auto kread = [&](const lds_char* kt, int ks, int kb) {
+    return lds_read16(kt + koff[ks] + kb * 32 * C::ROWB);
+  };
+  // PV step i covers (kb, h, db) with db fastest, so consecutive MFMAs update different
+  // accumulators.
+  auto vread = [&](const lds_char* vt, int i) {
+    const int db = i % C::DB, kb = i / (2 * C::DB), h = (i / C::DB) & 1;
+    const lds_char* base = vt + voff[db] + (32 * kb + 16 * h) * C::ROWB;
+    const u32x2 lo = lds_read8_tr(base);
+    const u32x2 hi = lds_read8_tr(base + 8 * C::ROWB);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  // Elements e = 16*kb + r of a lane's 32 scores per query block.
+  auto exp_slice = [&](STile& sc, PTile& pf, float (&sum)[C::NQB], int e0) {
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[qb][kb] = f32x16{};
+      for (int e = e0; e < e0 + EXP_SLICE; e += 2) {
+        const int kb = e >> 4, r = e & 15;
+        const float p0 = fast_exp2(__builtin_fmaf(sc[qb][kb][r], c, -m[qb]));
+        const float p1 = fast_exp2(__builtin_fmaf(sc[qb][kb][r + 1], c, -m[qb]));
+        sum[qb] += p0 + p1;
+        pf[qb][kb][r >> 3][(r >> 1) & 3] = pack_bf16(p0, p1);
+      }
+  };
+  auto max_slice = [&](STile& sn, float (&mx)[C::NQB], int e0, bool mask, int j0) {
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) {
+      const int qi = qlo + qb * 32 + l32;
+      const int lim = p.causal ? min(qi, N - 1) : N - 1;  // last visible key
+#pragma unroll
+      for (int e = e0; e < e0 + MAX_SLICE; ++e) {
+        const int kb = e >> 4, r = e & 15;
+        if (mask) {
+          const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          sn[qb][kb][r] = key > lim ? -INFINITY : sn[qb][kb][r];
+        }
+        mx[qb] = fmaxf(mx[qb], sn[qb][kb][r]);
+      }
+    }
+  };
+  // S^T(next) = K Q^T with K fragments read one k-step ahead; `also(ks)` is VALU work slotted
+  // between the MFMA groups. Scheduling fences keep this order.
+  auto s_tile = [&](const lds_char* kt, STile& sn, auto&& also) {
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sn[qb][kb] = f32x16{};
     u32x4 kf[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) kf[0][kb] = lds_read16(kt + koff[0] + kb * 32 * C::ROWB);
+    for (int kb = 0; kb < 2; ++kb) kf[0][kb] = kread(kt, 0, kb);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       if (ks + 1 < C::KS) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          kf[(ks + 1) & 1][kb] = lds_read16(kt + koff[ks + 1] + kb * 32 * C::ROWB);
+        for (int kb = 0; kb < 2; ++kb) kf[(ks + 1) & 1][kb] = kread(kt, ks + 1, kb);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb) s[qb][kb] = mfma32x32x16(kf[ks & 1][kb], qf[qb][ks], s[qb][kb]);
+        for (int qb = 0; qb < C::NQB; ++qb) sn[qb][kb] = mfma32x32x16(kf[ks & 1][kb], qf[qb][ks], sn[qb][kb]);
+      also(ks);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Row max of a tile's scores (log2 domain, both wave halves), masking first if asked.
-  auto max_tile = [&](f32x16 (&s)[C::NQB][2], bool mask, int j0, float (&mt)[C::NQB]) {
-#pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) {
-      if (mask) {
-        const int qi = qlo + qb * 32 + l32;
-        const int lim = p.causal ? min(qi, N - 1) : N - 1;  // last visible key
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (key > lim) s[qb][kb][r] = -INFINITY;
-          }
-      }
-      float x = s[qb][0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x = fmaxf(x, s[qb][kb][r]);
-      mt[qb] = max_halves(x) * c;
-    }
-  };
-  // P^T of a tile as MFMA B operands [qb][kb][h] (16 keys x 32 queries, packed bf16), built in
-  // place so the MFMAs read them without register copies.
-  typedef u32x4 PTile[C::NQB][2][2];
-  auto exp_tile = [&](f32x16 (&s)[C::NQB][2], PTile& pk) {
-#pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) {
-      float sum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(__builtin_fmaf(s[qb][kb][r], c, -m[qb]));
-          const float p1 = fast_exp2(__builtin_fmaf(s[qb][kb][r + 1], c, -m[qb]));
-          sum += p0 + p1;
-          pk[qb][kb][r >> 3][(r >> 1) & 3] = pack_bf16(p0, p1);
-        }
-      l[qb] += sum;
-    }
-  };
-  // O^T += V^T P^T. The V^T fragment of the next (db, kb, h) step is read while the MFMAs
-  // of the current one run; fences keep that order.
-  auto pv_tile = [&](const lds_char* vt, PTile& pk) {
-    constexpr int NSTEP = C::DB * 4;
-    auto vread = [&](int i) {
-      const int db = i >> 2, kb = (i >> 1) & 1, h = i & 1;
-      const lds_char* base = vt + voff[db] + (32 * kb + 16 * h) * C::ROWB;
-      const u32x2 lo = lds_read8_tr(base);
-      const u32x2 hi = lds_read8_tr(base + 8 * C::ROWB);
-      return u32x4{lo[0], lo[1], hi[0], hi[1]};
-    };
+  // O^T += V^T P^T with V^T fragments read one step ahead; `also(i)` slotted likewise.
+  auto pv_tile = [&](const lds_char* vt, PTile& pf, auto&& also) {
     u32x4 vf[2];
-    vf[0] = vread(0);
+    vf[0] = vread(vt, 0);
 #pragma unroll
-    for (int i = 0; i < NSTEP; ++i) {
-      if (i + 1 < NSTEP) vf[(i + 1) & 1] = vread(i + 1);
+    for (int i = 0; i < NPV; ++i) {
+      if (i + 1 < NPV) vf[(i + 1) & 1] = vread(vt, i + 1);
       __builtin_amdgcn_sched_barrier(0);
-      const int db = i >> 2, kb = (i >> 1) & 1, h = i & 1;
+      const int db = i % C::DB, kb = i / (2 * C::DB), h = (i / C::DB) & 1;
 #pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb) acc[qb][db] = mfma32x32x16(vf[i & 1], pk[qb][kb][h], acc[qb][db]);
+      for (int qb = 0; qb < C::NQB; ++qb) acc[qb][db] = mfma32x32x16(vf[i & 1], pf[qb][kb][h], acc[qb][db]);
+      also(i);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto sync_stage = [&]() {
-    wait_vmem_all();
-    __syncthreads();
-  };
-
-  // One tile: fetch tile t+1 into the other stage, S = K Q^T, mask (diagonal / ragged tiles
-  // only), row max, raise the reference if the max moved past the slack, P, O += P V.
-  auto step = [&](auto par_tag, auto mask_tag, int t) {
-    constexpr int PAR = decltype(par_tag)::value;  // t % 2
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const lds_char* kt = (const lds_char*)(PAR ? k_st1 : k_st0);
-    const lds_char* vt = (const lds_char*)(PAR ? v_st1 : v_st0);
-    fetch_k(t + 1);
-    fetch_v(t + 1);
-    f32x16 s[C::NQB][2];
-    s_tile(kt, s);
+  auto rescale_if_needed = [&](const float (&mx)[C::NQB]) {
     float mt[C::NQB];
-    max_tile(s, MASK, t * C::BN, mt);
     bool grow = false;
 #pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) grow |= mt[qb] > m[qb] + kRescaleSlack;
+    for (int qb = 0; qb < C::NQB; ++qb) {
+      mt[qb] = max_halves(mx[qb]) * c;
+      grow |= mt[qb] > m[qb] + kRescaleSlack;
+    }
     if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
       for (int qb = 0; qb < C::NQB; ++qb) {
         const float mnew = fmaxf(m[qb], mt[qb]);
-        const float alpha = fast_exp2(m[qb] - mnew);  // 0 on the first tile (m = -inf)
+        const float alpha = fast_exp2(m[qb] - mnew);  // 0 before the first tile (m = -inf)
         m[qb] = mnew;
         l[qb] *= alpha;
         // Scaled through a zero-operand MFMA: every definition of an accumulator is then an
@@ -325,34 +312,93 @@ void fa2_fwd_kernel(FwdParams p) {
           acc[qb][db] = mfma32x32x16(u32x4{}, u32x4{}, acc[qb][db] * alpha);
       }
     }
-    PTile pk;
-    exp_tile(s, pk);
-    pv_tile(vt, pk);
+  };
+  auto sync_stage = [&]() {
+    wait_vmem_all();
+    __syncthreads();
+  };
+
+  // Software pipeline over tiles with two score buffers. Step t (PAR = t % 2): fetch K(t+2)
+  // and V(t+1); S(t+1) on the MFMA pipe while the VALU forms P(t) from S(t); PV(t) on the MFMA
+  // pipe while the VALU masks and max-reduces S(t+1); raise the reference before P(t+1) if
+  // the new max moved past the slack; one barrier.
+  STile sbuf[2];
+  auto step = [&](auto par_tag, auto mask_tag, int t) {
+    constexpr int PAR = decltype(par_tag)::value;
+    constexpr bool MASK_NEXT = decltype(mask_tag)::value;
+    const lds_char* k_next = (const lds_char*)(PAR ? k_st0 : k_st1);
+    const lds_char* v_cur = (const lds_char*)(PAR ? v_st1 : v_st0);
+    fetch_k(t + 2);
+    fetch_v(t + 1);
+    PTile pf;
+    float sum[C::NQB], mx[C::NQB];
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) {
+      sum[qb] = 0.f;
+      mx[qb] = -INFINITY;
+    }
+    s_tile(k_next, sbuf[PAR ^ 1], [&](int ks) { exp_slice(sbuf[PAR], pf, sum, ks * EXP_SLICE); });
+    pv_tile(v_cur, pf, [&](int i) {
+      max_slice(sbuf[PAR ^ 1], mx, i * MAX_SLICE, MASK_NEXT, (t + 1) * C::BN);
+    });
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) l[qb] += sum[qb];
+    rescale_if_needed(mx);
+    sync_stage();
+  };
+  auto last_step = [&](auto par_tag, int t) {  // t = nmine - 1: no next tile to prepare
+    constexpr int PAR = decltype(par_tag)::value;
+    const lds_char* v_cur = (const lds_char*)(PAR ? v_st1 : v_st0);
+    fetch_k(t + 2);
+    fetch_v(t + 1);
+    PTile pf;
+    float sum[C::NQB];
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) sum[qb] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) exp_slice(sbuf[PAR], pf, sum, ks * EXP_SLICE);
+    pv_tile(v_cur, pf, [&](int) {});
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) l[qb] += sum[qb];
     sync_stage();
   };
 
-  sync_stage();  // Q, K(0), V(0) have landed
+  sync_stage();  // Q, K(0), V(0), K(1) have landed
+  {
+    float mx[C::NQB];
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) mx[qb] = -INFINITY;
+    s_tile((const lds_char*)k_st0, sbuf[0], [&](int) {});
+    for (int i = 0; i < NPV; ++i) max_slice(sbuf[0], mx, i * MAX_SLICE, nfree == 0, 0);
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) m[qb] = -INFINITY;
+    rescale_if_needed(mx);  // sets the first reference; O and l are still zero
+  }
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
-  // Steps run in pairs (stage 0 then stage 1) so each step names its LDS arrays statically and
-  // no branch merges the accumulators; a masked step on an unmasked tile is merely slower, so
-  // an odd unmasked count hands its last tile to the masked loop.
+  // Steps run in pairs (stage 0, then stage 1) so each step names its arrays statically and no
+  // branch merges the accumulators. Step t masks tile t+1: unmasked steps are those with
+  // t + 1 < nfree; masking an unmasked tile is merely slower, so counts are rounded to pairs.
   int t = 0;
-  const int nfree_even = nfree & ~1;
-  for (; t < nfree_even; t += 2) {
+  const int nfree_steps = nfree > 0 ? ((nfree - 1) & ~1) : 0;
+  for (; t < nfree_steps; t += 2) {
     step(P0{}, std::false_type{}, t);
     step(P1{}, std::false_type{}, t + 1);
   }
-  for (; t + 1 < nmine; t += 2) {
+  for (; t + 2 < nmine; t += 2) {
     step(P0{}, std::true_type{}, t);
     step(P1{}, std::true_type{}, t + 1);
   }
-  if (t < nmine) {
+  // One or two steps remain (t even): t = nmine - 1, or t = nmine - 2 then t = nmine - 1.
+  if (t + 1 < nmine) {
     step(P0{}, std::true_type{}, t);
-    ++t;
+    last_step(P1{}, t + 1);
+  } else {
+    last_step(P0{}, t);
   }
+  t = nmine;
   for (; t < ntiles; ++t) {  // tiles above this wave's rows: keep the shared fetch cadence
-    fetch_k(t + 1);
+    fetch_k(t + 2);
     fetch_v(t + 1);
     sync_stage();
   }
