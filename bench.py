@@ -115,16 +115,18 @@ def main():
     dq = torch.empty_like(o)
     dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev)
     dv = torch.empty_like(dk)
-    delta = torch.empty(fa2.fa2_backward_workspace_size(B, Hq, N) // 4, dtype=torch.float32, device=dev)
+    ws_bytes = fa2.fa2_backward_workspace_size(B, Hq, N)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     names = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
 
     def step(events=None):
         calls = [
             lambda: fa2.fa2_forward(qd, kd, vd, o, lse, B, Hq, Hkv, N, d, causal, scale, stream),
-            lambda: fa2.fa2_backward_preprocess(o, dod, delta, B, Hq, N, d, stream),
-            lambda: fa2.fa2_backward_dkdv(qd, kd, vd, lse, delta, dod, dk, dv, B, Hq, Hkv, N, d, causal, scale, stream),
-            lambda: fa2.fa2_backward_dq(qd, kd, vd, lse, delta, dod, dq, B, Hq, Hkv, N, d, causal, scale, stream),
+            lambda: fa2.fa2_backward_preprocess(o, dod, lse, ws, ws_bytes, B, Hq, N, d, stream),
+            lambda: fa2.fa2_backward_dkdv(qd, kd, vd, dod, ws, ws_bytes, dk, dv, B, Hq, Hkv, N, d, causal, scale,
+                                          stream),
+            lambda: fa2.fa2_backward_dq(qd, kd, vd, dod, ws, ws_bytes, dq, B, Hq, Hkv, N, d, causal, scale, stream),
         ]
         for i, call in enumerate(calls):
             if events is not None:
@@ -167,7 +169,7 @@ def main():
     algo = {"fwd": ("mfma", pairs * 4 * d / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
             "bwd_dkdv": ("mfma", pairs * 8 * d / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
             "bwd_dq": ("mfma", pairs * 6 * d / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
-            "bwd_preprocess": ("hbm", B * Hq * N * (d * 6 + 4) / 1e9, "GB/s", PEAK_HBM_GBS)}
+            "bwd_preprocess": ("hbm", B * Hq * N * (d * 6 + 12) / 1e9, "GB/s", PEAK_HBM_GBS)}
     kernels = {}
     for n in names:
         bound, work, unit, peak = algo[n]

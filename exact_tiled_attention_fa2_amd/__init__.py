@@ -50,11 +50,12 @@ def load() -> ctypes.CDLL:
     lib.fa2_backward_workspace_size.restype = ctypes.c_size_t
     lib.fa2_backward_workspace_size.argtypes = [i, i, i]
     lib.fa2_backward_preprocess.restype = i
-    lib.fa2_backward_preprocess.argtypes = [p, p, p, i, i, i, i, p]
+    z = ctypes.c_size_t
+    lib.fa2_backward_preprocess.argtypes = [p, p, p, p, z, i, i, i, i, p]
     lib.fa2_backward_dkdv.restype = i
-    lib.fa2_backward_dkdv.argtypes = [p, p, p, p, p, p, p, p, i, i, i, i, i, i, f, p]
+    lib.fa2_backward_dkdv.argtypes = [p, p, p, p, p, z, p, p, i, i, i, i, i, i, f, p]
     lib.fa2_backward_dq.restype = i
-    lib.fa2_backward_dq.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i, f, p]
+    lib.fa2_backward_dq.argtypes = [p, p, p, p, p, z, p, i, i, i, i, i, i, f, p]
     lib.fa2_status_string.restype = ctypes.c_char_p
     lib.fa2_status_string.argtypes = [i]
     _lib = lib
@@ -95,19 +96,23 @@ def fa2_backward(q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, N, d, causal, scal
                                _ptr(workspace), int(workspace_bytes), _stream(stream))
 
 
-def fa2_backward_preprocess(o, dO, delta, B, Hq, N, d, stream=None) -> int:
-    return load().fa2_backward_preprocess(_ptr(o), _ptr(dO), _ptr(delta), B, Hq, N, d, _stream(stream))
+def fa2_backward_preprocess(o, dO, lse, workspace, workspace_bytes, B, Hq, N, d, stream=None) -> int:
+    return load().fa2_backward_preprocess(_ptr(o), _ptr(dO), _ptr(lse), _ptr(workspace), int(workspace_bytes),
+                                          B, Hq, N, d, _stream(stream))
 
 
-def fa2_backward_dkdv(q, k, v, lse, delta, dO, dk, dv, B, Hq, Hkv, N, d, causal, scale, stream=None) -> int:
-    return load().fa2_backward_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(delta), _ptr(dO), _ptr(dk),
-                                    _ptr(dv), B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
+def fa2_backward_dkdv(q, k, v, dO, workspace, workspace_bytes, dk, dv, B, Hq, Hkv, N, d, causal, scale,
+                      stream=None) -> int:
+    return load().fa2_backward_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(workspace), int(workspace_bytes),
+                                    _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
                                     _stream(stream))
 
 
-def fa2_backward_dq(q, k, v, lse, delta, dO, dq, B, Hq, Hkv, N, d, causal, scale, stream=None) -> int:
-    return load().fa2_backward_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(delta), _ptr(dO), _ptr(dq),
-                                  B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _stream(stream))
+def fa2_backward_dq(q, k, v, dO, workspace, workspace_bytes, dq, B, Hq, Hkv, N, d, causal, scale,
+                    stream=None) -> int:
+    return load().fa2_backward_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(workspace), int(workspace_bytes),
+                                  _ptr(dq), B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
+                                  _stream(stream))
 
 
 def fa2_status_string(status: int) -> str:

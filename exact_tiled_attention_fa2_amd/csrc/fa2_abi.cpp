@@ -107,9 +107,19 @@ int fa2_forward(const void* q, const void* k, const void* v, float* o, float* ls
 
 size_t fa2_backward_workspace_size(int B, int Hq, int N) {
   if (B <= 0 || Hq <= 0 || N <= 0) return 0;
-  uint64_t bytes = (uint64_t)B * Hq * N * 4;
+  uint64_t bytes = (uint64_t)B * Hq * N * 8;
   return (size_t)((bytes + 255) & ~(uint64_t)255);
 }
+
+namespace {
+
+// The workspace is written by the preprocess and read by the other two steps.
+int check_workspace(const void* ws, size_t ws_bytes, int B, int Hq, int N) {
+  if (!ws || ws_bytes < fa2_backward_workspace_size(B, Hq, N)) return FA2_ERR_WORKSPACE;
+  return FA2_OK;
+}
+
+}  // namespace
 
 int fa2_backward(const void* q, const void* k, const void* v, const float* o, const float* lse,
                  const void* dO, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int N,
@@ -124,64 +134,74 @@ int fa2_backward(const void* q, const void* k, const void* v, const float* o, co
   const Buf out[3] = {{dq, rq * d * 4}, {dk, rkv * d * 4}, {dv, rkv * d * 4}};
   st = check_buffers(in, 6, out, 3);
   if (st != FA2_OK) return st;
-  if (!workspace || workspace_bytes < fa2_backward_workspace_size(B, Hq, N))
-    return FA2_ERR_WORKSPACE;
+  st = check_workspace(workspace, workspace_bytes, B, Hq, N);
+  if (st != FA2_OK) return st;
   const Buf all_in[9] = {in[0], in[1], in[2], in[3], in[4], in[5], out[0], out[1], out[2]};
   const Buf ws[1] = {{workspace, fa2_backward_workspace_size(B, Hq, N)}};
   st = check_buffers(all_in, 9, ws, 1);
   if (st != FA2_OK) return st;
   fa2::AttnShape s{B, Hq, Hkv, N, d, causal != 0, scale};
-  float* delta = static_cast<float*>(workspace);
-  hipError_t e = fa2::launch_bwd_preprocess(o, dO, delta, s, stream);
-  if (e == hipSuccess) e = fa2::launch_bwd_dkdv(q, k, v, lse, delta, dO, dk, dv, s, stream);
-  if (e == hipSuccess) e = fa2::launch_bwd_dq(q, k, v, lse, delta, dO, dq, s, stream);
+  float* w = static_cast<float*>(workspace);
+  hipError_t e = fa2::launch_bwd_preprocess(o, dO, lse, w, s, stream);
+  if (e == hipSuccess) e = fa2::launch_bwd_dkdv(q, k, v, dO, w, dk, dv, s, stream);
+  if (e == hipSuccess) e = fa2::launch_bwd_dq(q, k, v, dO, w, dq, s, stream);
   return hip_status(e);
 }
 
-int fa2_backward_preprocess(const float* o, const void* dO, float* delta, int B, int Hq, int N,
-                            int d, hipStream_t stream) {
+int fa2_backward_preprocess(const float* o, const void* dO, const float* lse, void* workspace,
+                            size_t workspace_bytes, int B, int Hq, int N, int d,
+                            hipStream_t stream) {
   bool empty = false;
   int st = check_shape(B, Hq, 1, N, d, 1.0f, &empty);
   if (st != FA2_OK || empty) return st;
   const uint64_t rq = (uint64_t)B * Hq * N;
-  const Buf in[2] = {{o, rq * d * 4}, {dO, rq * d * 2}};
-  const Buf out[1] = {{delta, rq * 4}};
-  st = check_buffers(in, 2, out, 1);
+  const Buf in[3] = {{o, rq * d * 4}, {dO, rq * d * 2}, {lse, rq * 4}};
+  st = check_buffers(in, 3, nullptr, 0);
+  if (st != FA2_OK) return st;
+  st = check_workspace(workspace, workspace_bytes, B, Hq, N);
+  if (st != FA2_OK) return st;
+  const Buf ws[1] = {{workspace, fa2_backward_workspace_size(B, Hq, N)}};
+  st = check_buffers(in, 3, ws, 1);
   if (st != FA2_OK) return st;
   fa2::AttnShape s{B, Hq, 1, N, d, 0, 1.0f};
-  return hip_status(fa2::launch_bwd_preprocess(o, dO, delta, s, stream));
+  return hip_status(fa2::launch_bwd_preprocess(o, dO, lse, static_cast<float*>(workspace), s, stream));
 }
 
-int fa2_backward_dkdv(const void* q, const void* k, const void* v, const float* lse,
-                      const float* delta, const void* dO, float* dk, float* dv, int B, int Hq,
-                      int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
+int fa2_backward_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                      const void* workspace, size_t workspace_bytes, float* dk, float* dv,
+                      int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                      hipStream_t stream) {
   bool empty = false;
   int st = check_shape(B, Hq, Hkv, N, d, scale, &empty);
   if (st != FA2_OK || empty) return st;
+  st = check_workspace(workspace, workspace_bytes, B, Hq, N);
+  if (st != FA2_OK) return st;
   const uint64_t rq = (uint64_t)B * Hq * N, rkv = (uint64_t)B * Hkv * N;
-  const Buf in[6] = {{q, rq * d * 2}, {k, rkv * d * 2}, {v, rkv * d * 2},
-                     {lse, rq * 4},   {delta, rq * 4},  {dO, rq * d * 2}};
+  const Buf in[5] = {{q, rq * d * 2}, {k, rkv * d * 2}, {v, rkv * d * 2}, {dO, rq * d * 2},
+                     {workspace, fa2_backward_workspace_size(B, Hq, N)}};
   const Buf out[2] = {{dk, rkv * d * 4}, {dv, rkv * d * 4}};
-  st = check_buffers(in, 6, out, 2);
+  st = check_buffers(in, 5, out, 2);
   if (st != FA2_OK) return st;
   fa2::AttnShape s{B, Hq, Hkv, N, d, causal != 0, scale};
-  return hip_status(fa2::launch_bwd_dkdv(q, k, v, lse, delta, dO, dk, dv, s, stream));
+  return hip_status(fa2::launch_bwd_dkdv(q, k, v, dO, static_cast<const float*>(workspace), dk, dv, s, stream));
 }
 
-int fa2_backward_dq(const void* q, const void* k, const void* v, const float* lse,
-                    const float* delta, const void* dO, float* dq, int B, int Hq, int Hkv,
-                    int N, int d, int causal, float scale, hipStream_t stream) {
+int fa2_backward_dq(const void* q, const void* k, const void* v, const void* dO,
+                    const void* workspace, size_t workspace_bytes, float* dq, int B, int Hq,
+                    int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
   bool empty = false;
   int st = check_shape(B, Hq, Hkv, N, d, scale, &empty);
   if (st != FA2_OK || empty) return st;
+  st = check_workspace(workspace, workspace_bytes, B, Hq, N);
+  if (st != FA2_OK) return st;
   const uint64_t rq = (uint64_t)B * Hq * N, rkv = (uint64_t)B * Hkv * N;
-  const Buf in[6] = {{q, rq * d * 2}, {k, rkv * d * 2}, {v, rkv * d * 2},
-                     {lse, rq * 4},   {delta, rq * 4},  {dO, rq * d * 2}};
+  const Buf in[5] = {{q, rq * d * 2}, {k, rkv * d * 2}, {v, rkv * d * 2}, {dO, rq * d * 2},
+                     {workspace, fa2_backward_workspace_size(B, Hq, N)}};
   const Buf out[1] = {{dq, rq * d * 4}};
-  st = check_buffers(in, 6, out, 1);
+  st = check_buffers(in, 5, out, 1);
   if (st != FA2_OK) return st;
   fa2::AttnShape s{B, Hq, Hkv, N, d, causal != 0, scale};
-  return hip_status(fa2::launch_bwd_dq(q, k, v, lse, delta, dO, dq, s, stream));
+  return hip_status(fa2::launch_bwd_dq(q, k, v, dO, static_cast<const float*>(workspace), dq, s, stream));
 }
 
 }  // extern "C"

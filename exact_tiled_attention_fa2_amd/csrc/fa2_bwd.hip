@@ -17,6 +17,8 @@
 // Q/dO (dK/dV kernel) and K/V (dQ kernel) tiles stream into LDS by buffer_load ... lds,
 // double buffered, in a layout that serves both 16-byte row reads and the transposing
 // ds_read_b64_tr_b16 reads without bank conflicts.
+#include <type_traits>
+
 #include "fa2_device.h"
 #include "fa2_launch.h"
 
@@ -26,13 +28,12 @@ struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  const float* o;
-  const float* lse;
   const uint16_t* dO;
   float* dq;
   float* dk;
   float* dv;
   float* delta;  // D, [B,Hq,N]
+  float* lse2;   // LSE * log2(e), [B,Hq,N]
   int B, Hq, Hkv, N;
   int causal;
   float c;        // |scale| * log2(e)
@@ -105,12 +106,16 @@ __device__ __forceinline__ u32x4 tr_pair(const lds_char* lo_base, const lds_char
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
-// ------------------------------------------------------------------ 1. preprocess: D_i
+// ------------------------------------------------------------------ 1. preprocess
 
+// delta[i] = D_i = sum_c dO_ic O_ic, and lse2[i] = LSE_i * log2(e) (so the kernels below form
+// P = 2^(s c - lse2) with one FMA and one exp2 per score).
 template <int D>
 __global__ __launch_bounds__(256) void fa2_bwd_pre_kernel(const float* __restrict__ o,
                                                           const uint16_t* __restrict__ dO,
-                                                          float* __restrict__ delta, long rows) {
+                                                          const float* __restrict__ lse,
+                                                          float* __restrict__ delta,
+                                                          float* __restrict__ lse2, long rows) {
   constexpr int LPR = D / 8;  // lanes per row, 8 elements each
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
   const long row = gid / LPR;
@@ -127,21 +132,37 @@ __global__ __launch_bounds__(256) void fa2_bwd_pre_kernel(const float* __restric
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-  if (row < rows && part == 0) delta[row] = acc;
+  if (row < rows && part == 0) {
+    delta[row] = acc;
+    lse2[row] = lse[row] * kLog2e;
+  }
 }
 
 // ------------------------------------------------------------------ 2. dK / dV
+
+// Q and dO tiles: stage s holds 64 query rows of Q, of dO, and [D | lse2] of those rows.
+template <int D>
+struct DkdvStage {
+  lds_char* q;
+  lds_char* dO;
+  lds_char* stat;  // D at +0 (64 floats), lse2 at +1024 bytes
+};
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fa2_bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
-  constexpr int STAGE = 2 * C::TILE + 2048;  // Q tile, dO tile, LSE[64] @0, D[64] @1024 B
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
-  lds_char* lds = (lds_char*)smem;
+  // Two stages, each in separate arrays (DMA into one stage never aliases reads of the other).
+  __shared__ __attribute__((aligned(1024))) char q_st0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char q_st1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char do_st0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char do_st1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char stat_st0[2048];
+  __shared__ __attribute__((aligned(1024))) char stat_st1[2048];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hf = lane >> 5, l32 = lane & 31;
+  agpr_accumulators_hint();
   const int N = p.N;
   const int bid = blockIdx.x;
   const int kblk = bid % p.nblk;  // causal: low key blocks see the most queries, go first
@@ -149,41 +170,45 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int G = p.Hq / p.Hkv;
   const int k0 = kblk * C::BR;
-  const int kw = k0 + wave * C::RPW;
+  const int kw = k0 + wave * C::RPW;  // this wave's first key
 
   const uint32_t head_bytes = (uint32_t)N * C::ROWB;
   const size_t kvoff = ((size_t)b * p.Hkv + g) * (size_t)N * D;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + kvoff, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + kvoff, head_bytes);
 
-  // Query tiles: all query heads of the group, tiles from the one holding key k0 onward.
+  // Query tiles: every query head of the group, tiles from the one holding key k0 onward.
   const int nqt_all = (N + C::BT - 1) / C::BT;
   const int qt0 = p.causal ? k0 / C::BT : 0;
   const int nqt = nqt_all - qt0;
   const int iters = G * nqt;
 
-  auto issue = [&](int it, int stage) {
+  auto stage = [&](int s) {
+    return s ? DkdvStage<D>{(lds_char*)q_st1, (lds_char*)do_st1, (lds_char*)stat_st1}
+             : DkdvStage<D>{(lds_char*)q_st0, (lds_char*)do_st0, (lds_char*)stat_st0};
+  };
+  auto fetch = [&](int it) {
+    if (it >= iters) return;
+    const DkdvStage<D> st = stage(it & 1);
     const int hq = g * G + it / nqt;
     const int qrow0 = (qt0 + it % nqt) * C::BT;
     const size_t qoff = ((size_t)b * p.Hq + hq) * (size_t)N * D;
-    lds_char* st = lds + stage * STAGE;
-    load_tile_dual<D>(make_rsrc(p.q + qoff, head_bytes), st, qrow0, wave, lane);
-    load_tile_dual<D>(make_rsrc(p.dO + qoff, head_bytes), st + C::TILE, qrow0, wave, lane);
+    load_tile_dual<D>(make_rsrc(p.q + qoff, head_bytes), st.q, qrow0, wave, lane);
+    load_tile_dual<D>(make_rsrc(p.dO + qoff, head_bytes), st.dO, qrow0, wave, lane);
     if (wave == 0) {
-      // LSE of the tile's 64 rows -> stat[0, 256 B); D -> stat[1024, 1280 B). Lanes past 15
-      // address one past the end of the buffer and fill the rest with zeros.
+      // D and lse2 of the tile's 64 rows; lanes past 15 read past the end (zeros).
       const size_t roff = ((size_t)b * p.Hq + hq) * (size_t)N;
       const uint32_t off = lane < 16 ? (uint32_t)(qrow0 + 4 * lane) * 4 : (uint32_t)N * 4;
-      buffer_load16_lds(make_rsrc(p.lse + roff, (uint32_t)N * 4), st + 2 * C::TILE, off);
-      buffer_load16_lds(make_rsrc(p.delta + roff, (uint32_t)N * 4), st + 2 * C::TILE + 1024, off);
+      buffer_load16_lds(make_rsrc(p.delta + roff, (uint32_t)N * 4), st.stat, off);
+      buffer_load16_lds(make_rsrc(p.lse2 + roff, (uint32_t)N * 4), st.stat + 1024, off);
     }
   };
 
-  if (iters > 0) issue(0, 0);
+  fetch(0);
 
   // K and V of this wave's 32 keys as B operands (lane = key, k = head dim).
   u32x4 kf[C::KS], vf[C::KS];
   {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + kvoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + kvoff, head_bytes);
     const uint32_t row = (uint32_t)(kw + l32);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
@@ -208,89 +233,123 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
     adv[db] = f32x16{};
   }
   const float c = p.c;
+  const int key = kw + l32;
 
-  wait_vmem_all();
-  __syncthreads();
-
-  for (int it = 0; it < iters; ++it) {
-    const int stage = it & 1;
-    if (it + 1 < iters) issue(it + 1, stage ^ 1);
-    const lds_char* qt = lds + stage * STAGE;
-    const lds_char* dot = qt + C::TILE;
-    const FA2_LDS float* rowstat = (const FA2_LDS float*)(qt + 2 * C::TILE);  // LSE @0, D @256 floats
-    const int qrow0 = (qt0 + it % nqt) * C::BT;
-
-    const bool skip = p.causal && qrow0 + C::BT - 1 < kw;
-    if (!skip) {
-      // ---- S = Q K^T and dP = dO V^T, [mb]: 32 queries x 32 keys ----
-      f32x16 s[2], dp[2];
+  // One query tile for this wave. MASK: the tile reaches the wave's diagonal or the end of
+  // the sequence. S/dP MFMAs with operands read one step ahead; P and dS on the VALU; then
+  // dV^T += dO^T P and dK^T += Q^T dS with transposed operands read one step ahead.
+  auto tile = [&](const DkdvStage<D>& st, int qrow0, bool mask) __attribute__((always_inline)) {
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      s[mb] = f32x16{};
+      dp[mb] = f32x16{};
+    }
+    {
+      u32x4 qa[2][2], da[2][2];  // [buffer][mb]
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        s[mb] = f32x16{};
-        dp[mb] = f32x16{};
+        qa[0][mb] = lds_read16(st.q + roff[0] + mb * 32 * C::ROWB);
+        da[0][mb] = lds_read16(st.dO + roff[0] + mb * 32 * C::ROWB);
       }
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
+        if (ks + 1 < C::KS) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const u32x4 qa = lds_read16(qt + roff[ks] + mb * 32 * C::ROWB);
-          s[mb] = mfma32x32x16(qa, kf[ks], s[mb]);
-          const u32x4 da = lds_read16(dot + roff[ks] + mb * 32 * C::ROWB);
-          dp[mb] = mfma32x32x16(da, vf[ks], dp[mb]);
-        }
-      }
-      // ---- P = 2^(S c - LSE log2 e), dS = P (dP - D); registers hold query rows ----
-      const bool need_mask = (p.causal && qrow0 < kw + C::RPW - 1) || (qrow0 + C::BT > N);
-      const int key = kw + l32;
-      unsigned pp[2][8], pd[2][8];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int r0 = 32 * mb + 8 * rq + 4 * hf;  // tile rows r0..r0+3
-          const f32x4 lse4 = *(const FA2_LDS f32x4*)(rowstat + r0);
-          const f32x4 del4 = *(const FA2_LDS f32x4*)(rowstat + 256 + r0);
-          float pv[4], dsv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float pe = fast_exp2(__builtin_fmaf(s[mb][4 * rq + e], c, -lse4[e] * kLog2e));
-            if (need_mask) {
-              const int qi = qrow0 + r0 + e;
-              if (qi >= N || (p.causal && key > qi)) pe = 0.f;
-            }
-            pv[e] = pe;
-            dsv[e] = pe * (dp[mb][4 * rq + e] - del4[e]);
-          }
-          pp[mb][2 * rq] = pack_bf16(pv[0], pv[1]);
-          pp[mb][2 * rq + 1] = pack_bf16(pv[2], pv[3]);
-          pd[mb][2 * rq] = pack_bf16(dsv[0], dsv[1]);
-          pd[mb][2 * rq + 1] = pack_bf16(dsv[2], dsv[3]);
-        }
-      }
-      // ---- dV^T += dO^T P, dK^T += Q^T dS (contraction over the tile's 64 queries) ----
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int rowsel = (32 * mb + 16 * h) * C::ROWB;
-            const u32x4 dta = tr_pair(dot + toff[db] + rowsel, dot + toff8[db] + rowsel);
-            const u32x4 pb = {pp[mb][4 * h], pp[mb][4 * h + 1], pp[mb][4 * h + 2], pp[mb][4 * h + 3]};
-            adv[db] = mfma32x32x16(dta, pb, adv[db]);
-            const u32x4 qta = tr_pair(qt + toff[db] + rowsel, qt + toff8[db] + rowsel);
-            const u32x4 sb = {pd[mb][4 * h], pd[mb][4 * h + 1], pd[mb][4 * h + 2], pd[mb][4 * h + 3]};
-            adk[db] = mfma32x32x16(qta, sb, adk[db]);
+          for (int mb = 0; mb < 2; ++mb) {
+            qa[(ks + 1) & 1][mb] = lds_read16(st.q + roff[ks + 1] + mb * 32 * C::ROWB);
+            da[(ks + 1) & 1][mb] = lds_read16(st.dO + roff[ks + 1] + mb * 32 * C::ROWB);
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          s[mb] = mfma32x32x16(qa[ks & 1][mb], kf[ks], s[mb]);
+          dp[mb] = mfma32x32x16(da[ks & 1][mb], vf[ks], dp[mb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // P = 2^(S c - lse2), dS = P (dP - D); registers hold query rows 32mb + 8rq + 4hf + e.
+    u32x4 pp[2][2], pd[2][2];  // B operands [mb][h]: 16 queries x 32 keys, packed bf16
+    const FA2_LDS float* dstat = (const FA2_LDS float*)st.stat;
+    const FA2_LDS float* lstat = (const FA2_LDS float*)(st.stat + 1024);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int r0 = 32 * mb + 8 * rq + 4 * hf;
+        const f32x4 l4 = *(const FA2_LDS f32x4*)(lstat + r0);
+        const f32x4 d4 = *(const FA2_LDS f32x4*)(dstat + r0);
+        float pv[4], dsv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pe = fast_exp2(__builtin_fmaf(s[mb][4 * rq + e], c, -l4[e]));
+          if (mask) {
+            const int qi = qrow0 + r0 + e;
+            pe = (qi >= N || (p.causal && key > qi)) ? 0.f : pe;
+          }
+          pv[e] = pe;
+          dsv[e] = pe * (dp[mb][4 * rq + e] - d4[e]);
+        }
+        pp[mb][rq >> 1][2 * (rq & 1)] = pack_bf16(pv[0], pv[1]);
+        pp[mb][rq >> 1][2 * (rq & 1) + 1] = pack_bf16(pv[2], pv[3]);
+        pd[mb][rq >> 1][2 * (rq & 1)] = pack_bf16(dsv[0], dsv[1]);
+        pd[mb][rq >> 1][2 * (rq & 1) + 1] = pack_bf16(dsv[2], dsv[3]);
+      }
+    // Contraction over the tile's 64 queries; step i = (mb, h, db) with db fastest.
+    {
+      constexpr int NSTEP = 4 * C::DB;
+      auto trread = [&](const lds_char* base, int i) {
+        const int db = i % C::DB, mb = i / (2 * C::DB), h = (i / C::DB) & 1;
+        const int rowsel = (32 * mb + 16 * h) * C::ROWB;
+        return tr_pair(base + toff[db] + rowsel, base + toff8[db] + rowsel);
+      };
+      u32x4 ta[2][2];  // [buffer][dO^T, Q^T]
+      ta[0][0] = trread(st.dO, 0);
+      ta[0][1] = trread(st.q, 0);
+#pragma unroll
+      for (int i = 0; i < NSTEP; ++i) {
+        if (i + 1 < NSTEP) {
+          ta[(i + 1) & 1][0] = trread(st.dO, i + 1);
+          ta[(i + 1) & 1][1] = trread(st.q, i + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int db = i % C::DB, mb = i / (2 * C::DB), h = (i / C::DB) & 1;
+        adv[db] = mfma32x32x16(ta[i & 1][0], pp[mb][h], adv[db]);
+        adk[db] = mfma32x32x16(ta[i & 1][1], pd[mb][h], adk[db]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  auto sync_stage = [&]() {
     wait_vmem_all();
     __syncthreads();
+  };
+  auto step = [&](auto par_tag, int it) {
+    constexpr int PAR = decltype(par_tag)::value;  // it % 2
+    fetch(it + 1);
+    const DkdvStage<D> st = stage(PAR);
+    const int qrow0 = (qt0 + it % nqt) * C::BT;
+    // Causal: skip tiles wholly above this wave's keys; mask tiles crossing its diagonal.
+    if (!(p.causal && qrow0 + C::BT - 1 < kw)) {
+      const bool mask = (p.causal && qrow0 < kw + C::RPW - 1) || (qrow0 + C::BT > N);
+      tile(st, qrow0, mask);
+    }
+    sync_stage();
+  };
+
+  sync_stage();
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  int it = 0;
+  for (; it + 1 < iters; it += 2) {
+    step(P0{}, it);
+    step(P1{}, it + 1);
   }
+  if (it < iters) step(P0{}, it);
 
   // ---- store dK = scale dK^T^T, dV: lane = key, registers = head dim ----
-  const int key = kw + l32;
   if (key < N) {
     float* dkrow = p.dk + kvoff + (size_t)key * D;
     float* dvrow = p.dv + kvoff + (size_t)key * D;
@@ -310,12 +369,24 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
 // ------------------------------------------------------------------ 3. dQ
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+struct DqCfg {
+  static constexpr int WAVES = 8;           // two waves per SIMD
+  static constexpr int RPW = 32;            // query rows per wave
+  static constexpr int BR = WAVES * RPW;    // query rows per workgroup
+  static constexpr int BT = 64;             // keys per streamed tile
+  static constexpr int TILE = BT * D * 2;
+  static constexpr int LPW = TILE / 1024 / WAVES;
+};
+
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa2_bwd_dq_kernel(BwdParams p) {
   using C = BwdCfg<D>;
-  constexpr int STAGE = 2 * C::TILE;  // K tile, V tile
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
-  lds_char* lds = (lds_char*)smem;
+  using Q = DqCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char k_st0[Q::TILE];
+  __shared__ __attribute__((aligned(1024))) char k_st1[Q::TILE];
+  __shared__ __attribute__((aligned(1024))) char v_st0[Q::TILE];
+  __shared__ __attribute__((aligned(1024))) char v_st1[Q::TILE];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hf = lane >> 5, l32 = lane & 31;
@@ -326,8 +397,8 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   const int qblk = p.causal ? p.nblk - 1 - r : r;  // longest rows first
   const int b = bh / p.Hq, hq = bh % p.Hq;
   const int hkv = hq / (p.Hq / p.Hkv);
-  const int q0 = qblk * C::BR;
-  const int qw = q0 + wave * C::RPW;
+  const int q0 = qblk * Q::BR;
+  const int qw = q0 + wave * Q::RPW;
 
   const uint32_t head_bytes = (uint32_t)N * C::ROWB;
   const size_t qoff = (size_t)bh * N * D;
@@ -335,11 +406,27 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + kvoff, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + kvoff, head_bytes);
 
-  const int qend = min(q0 + C::BR, N);
-  const int ntiles = p.causal ? (qend + C::BT - 1) / C::BT : (N + C::BT - 1) / C::BT;
+  const int qend = min(q0 + Q::BR, N);
+  const int ntiles = p.causal ? (qend + Q::BT - 1) / Q::BT : (N + Q::BT - 1) / Q::BT;
+  // Tiles this wave computes (causal: up to its last row).
+  const int nmine = p.causal ? min(ntiles, (qw + Q::RPW - 1) / Q::BT + 1) : ntiles;
 
-  load_tile_dual<D>(rk, lds, 0, wave, lane);
-  load_tile_dual<D>(rv, lds + C::TILE, 0, wave, lane);
+  auto fetch = [&](int t) {
+    if (t >= ntiles) return;
+    lds_char* kd = (t & 1) ? (lds_char*)k_st1 : (lds_char*)k_st0;
+    lds_char* vd = (t & 1) ? (lds_char*)v_st1 : (lds_char*)v_st0;
+#pragma unroll
+    for (int i = 0; i < Q::LPW; ++i) {
+      const int blk = wave * Q::LPW + i;
+      const int pos = blk * 1024 + lane * 16;
+      const int rr = pos / C::ROWB;
+      const int cp = (pos % C::ROWB) / 16;
+      const uint32_t off = (uint32_t)(t * Q::BT + rr) * C::ROWB + ((cp ^ swz_dual<D>(rr)) << 4);
+      buffer_load16_lds(rk, kd + blk * 1024, off);
+      buffer_load16_lds(rv, vd + blk * 1024, off);
+    }
+  };
+  fetch(0);
 
   // Q and dO of this wave's 32 queries as B operands (lane = query, k = head dim).
   u32x4 qf[C::KS], df[C::KS];
@@ -354,7 +441,7 @@ void fa2_bwd_dq_kernel(BwdParams p) {
       df[ks] = buffer_load16(rd, off);
     }
   }
-  const float lse2 = (qi < N ? p.lse[(size_t)bh * N + qi] : 0.f) * kLog2e;
+  const float lse2 = qi < N ? p.lse2[(size_t)bh * N + qi] : 0.f;
   const float dlt = qi < N ? p.delta[(size_t)bh * N + qi] : 0.f;
 
   int roff[C::KS], toff[C::DB], toff8[C::DB];
@@ -371,73 +458,87 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   for (int db = 0; db < C::DB; ++db) adq[db] = f32x16{};
   const float c = p.c;
 
-  wait_vmem_all();
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int stage = t & 1;
-    if (t + 1 < ntiles) {
-      lds_char* nx = lds + (stage ^ 1) * STAGE;
-      load_tile_dual<D>(rk, nx, (t + 1) * C::BT, wave, lane);
-      load_tile_dual<D>(rv, nx + C::TILE, (t + 1) * C::BT, wave, lane);
-    }
-    const lds_char* kt = lds + stage * STAGE;
-    const lds_char* vt = kt + C::TILE;
-    const int j0 = t * C::BT;
-    const bool skip = p.causal && j0 > qw + C::RPW - 1;
-    if (!skip) {
-      // ---- S^T = K Q^T and dP^T = V dO^T, [kb]: 32 keys x 32 queries ----
-      f32x16 s[2], dp[2];
+  // One K/V tile, as two halves of 32 keys (kb) processed in turn to bound register use:
+  // S^T = K Q^T and dP^T = V dO^T (operands one step ahead), dS^T = P^T (dP^T - D) on the
+  // VALU, then dQ^T += K^T dS^T with the transposed K operands one step ahead.
+  auto tile = [&](const lds_char* kt, const lds_char* vt, int j0, bool mask) __attribute__((always_inline)) {
+    const int lim = p.causal ? min(qi, N - 1) : N - 1;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        dp[kb] = f32x16{};
-      }
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+      {
+        u32x4 ka[2], va[2];
+        ka[0] = lds_read16(kt + roff[0] + kb * 32 * C::ROWB);
+        va[0] = lds_read16(vt + roff[0] + kb * 32 * C::ROWB);
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 ka = lds_read16(kt + roff[ks] + kb * 32 * C::ROWB);
-          s[kb] = mfma32x32x16(ka, qf[ks], s[kb]);
-          const u32x4 va = lds_read16(vt + roff[ks] + kb * 32 * C::ROWB);
-          dp[kb] = mfma32x32x16(va, df[ks], dp[kb]);
+        for (int ks = 0; ks < C::KS; ++ks) {
+          if (ks + 1 < C::KS) {
+            ka[(ks + 1) & 1] = lds_read16(kt + roff[ks + 1] + kb * 32 * C::ROWB);
+            va[(ks + 1) & 1] = lds_read16(vt + roff[ks + 1] + kb * 32 * C::ROWB);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          s = mfma32x32x16(ka[ks & 1], qf[ks], s);
+          dp = mfma32x32x16(va[ks & 1], df[ks], dp);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      const bool need_mask = (p.causal && j0 + C::BT - 1 > qw) || (j0 + C::BT > N);
-      const int lim = p.causal ? min(qi, N - 1) : N - 1;
-      unsigned pd[2][8];
+      u32x4 pd[2];  // dS^T as B operands [h]: 16 keys x 32 queries, packed bf16
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int rr = 0; rr < 16; rr += 2) {
+        float ds2[2];
 #pragma unroll
-        for (int rr = 0; rr < 16; rr += 2) {
-          float ds2[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            float pe = fast_exp2(__builtin_fmaf(s[kb][rr + e], c, -lse2));
-            if (need_mask) {
-              const int key = j0 + 32 * kb + 8 * ((rr + e) >> 2) + 4 * hf + ((rr + e) & 3);
-              if (key > lim) pe = 0.f;
-            }
-            ds2[e] = pe * (dp[kb][rr + e] - dlt);
+        for (int e = 0; e < 2; ++e) {
+          float pe = fast_exp2(__builtin_fmaf(s[rr + e], c, -lse2));
+          if (mask) {
+            const int kj = j0 + 32 * kb + 8 * ((rr + e) >> 2) + 4 * hf + ((rr + e) & 3);
+            pe = kj > lim ? 0.f : pe;
           }
-          pd[kb][rr >> 1] = pack_bf16(ds2[0], ds2[1]);
+          ds2[e] = pe * (dp[rr + e] - dlt);
         }
-      // ---- dQ^T += K^T dS^T (contraction over the tile's 64 keys) ----
+        pd[rr >> 3][(rr >> 1) & 3] = pack_bf16(ds2[0], ds2[1]);
+      }
+      // step i = (h, db) with db fastest
+      constexpr int NSTEP = 2 * C::DB;
+      auto trread = [&](int i) {
+        const int db = i % C::DB, h = i / C::DB;
+        const int rowsel = (32 * kb + 16 * h) * C::ROWB;
+        return tr_pair(kt + toff[db] + rowsel, kt + toff8[db] + rowsel);
+      };
+      u32x4 ta[2];
+      ta[0] = trread(0);
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int rowsel = (32 * kb + 16 * h) * C::ROWB;
-            const u32x4 kta = tr_pair(kt + toff[db] + rowsel, kt + toff8[db] + rowsel);
-            const u32x4 sb = {pd[kb][4 * h], pd[kb][4 * h + 1], pd[kb][4 * h + 2], pd[kb][4 * h + 3]};
-            adq[db] = mfma32x32x16(kta, sb, adq[db]);
-          }
+      for (int i = 0; i < NSTEP; ++i) {
+        if (i + 1 < NSTEP) ta[(i + 1) & 1] = trread(i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        adq[i % C::DB] = mfma32x32x16(ta[i & 1], pd[i / C::DB], adq[i % C::DB]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+  };
+  auto sync_stage = [&]() {
     wait_vmem_all();
     __syncthreads();
+  };
+  auto step = [&](auto par_tag, int t) {
+    constexpr int PAR = decltype(par_tag)::value;
+    fetch(t + 1);
+    if (t < nmine) {
+      const int j0 = t * Q::BT;
+      const bool mask = (p.causal && j0 + Q::BT - 1 > qw) || (j0 + Q::BT > N);
+      tile((const lds_char*)(PAR ? k_st1 : k_st0), (const lds_char*)(PAR ? v_st1 : v_st0), j0, mask);
+    }
+    sync_stage();
+  };
+
+  sync_stage();
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(P0{}, t);
+    step(P1{}, t + 1);
   }
+  if (t < ntiles) step(P0{}, t);
 
   if (qi < N) {
     float* dqrow = p.dq + qoff + (size_t)qi * D;
@@ -452,15 +553,17 @@ void fa2_bwd_dq_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------ launchers
 
-static BwdParams make_params(const void* q, const void* k, const void* v, const float* lse,
-                             const float* delta, const void* dO, const AttnShape& s) {
+// Workspace layout: D at [0, R) and lse2 at [R, 2R) floats, R = B*Hq*N.
+static BwdParams make_params(const void* q, const void* k, const void* v, const void* dO,
+                             float* ws, const AttnShape& s) {
   BwdParams p = {};
+  const size_t R = (size_t)s.B * s.Hq * s.N;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
-  p.lse = lse;
   p.dO = static_cast<const uint16_t*>(dO);
-  p.delta = const_cast<float*>(delta);
+  p.delta = ws;
+  p.lse2 = ws + R;
   p.B = s.B;
   p.Hq = s.Hq;
   p.Hkv = s.Hkv;
@@ -472,26 +575,27 @@ static BwdParams make_params(const void* q, const void* k, const void* v, const 
   return p;
 }
 
-hipError_t launch_bwd_preprocess(const float* o, const void* dO, float* delta, const AttnShape& s,
-                                 hipStream_t stream) {
+hipError_t launch_bwd_preprocess(const float* o, const void* dO, const float* lse, float* ws,
+                                 const AttnShape& s, hipStream_t stream) {
   const long rows = (long)s.B * s.Hq * s.N;
   const long threads = rows * (s.d / 8);
   const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  float* lse2 = ws + rows;
   if (s.d == 128)
-    hipLaunchKernelGGL(fa2_bwd_pre_kernel<128>, grid, block, 0, stream, o, (const uint16_t*)dO, delta, rows);
+    hipLaunchKernelGGL(fa2_bwd_pre_kernel<128>, grid, block, 0, stream, o, (const uint16_t*)dO, lse, ws, lse2, rows);
   else
-    hipLaunchKernelGGL(fa2_bwd_pre_kernel<64>, grid, block, 0, stream, o, (const uint16_t*)dO, delta, rows);
+    hipLaunchKernelGGL(fa2_bwd_pre_kernel<64>, grid, block, 0, stream, o, (const uint16_t*)dO, lse, ws, lse2, rows);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
-                           const float* delta, const void* dO, float* dk, float* dv,
-                           const AttnShape& s, hipStream_t stream) {
-  BwdParams p = make_params(q, k, v, lse, delta, dO, s);
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                           const float* ws, float* dk, float* dv, const AttnShape& s,
+                           hipStream_t stream) {
+  BwdParams p = make_params(q, k, v, dO, const_cast<float*>(ws), s);
   p.dk = dk;
   p.dv = dv;
   p.nblk = (s.N + BwdCfg<128>::BR - 1) / BwdCfg<128>::BR;
-  const dim3 grid((unsigned)(s.B * s.Hkv * p.nblk)), block(256);
+  const dim3 grid((unsigned)(s.B * s.Hkv * p.nblk)), block(BwdCfg<128>::WAVES * 64);
   if (s.d == 128)
     hipLaunchKernelGGL(fa2_bwd_dkdv_kernel<128>, grid, block, 0, stream, p);
   else
@@ -499,13 +603,12 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const fl
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
-                         const float* delta, const void* dO, float* dq, const AttnShape& s,
-                         hipStream_t stream) {
-  BwdParams p = make_params(q, k, v, lse, delta, dO, s);
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
+                         const float* ws, float* dq, const AttnShape& s, hipStream_t stream) {
+  BwdParams p = make_params(q, k, v, dO, const_cast<float*>(ws), s);
   p.dq = dq;
-  p.nblk = (s.N + BwdCfg<128>::BR - 1) / BwdCfg<128>::BR;
-  const dim3 grid((unsigned)(s.B * s.Hq * p.nblk)), block(256);
+  p.nblk = (s.N + DqCfg<128>::BR - 1) / DqCfg<128>::BR;
+  const dim3 grid((unsigned)(s.B * s.Hq * p.nblk)), block(DqCfg<128>::WAVES * 64);
   if (s.d == 128)
     hipLaunchKernelGGL(fa2_bwd_dq_kernel<128>, grid, block, 0, stream, p);
   else

@@ -16,15 +16,15 @@ struct AttnShape {
 hipError_t launch_forward(const void* q, const void* k, const void* v, float* o, float* lse,
                           const AttnShape& s, hipStream_t stream);
 
-hipError_t launch_bwd_preprocess(const float* o, const void* dO, float* delta, const AttnShape& s,
-                                 hipStream_t stream);
+// Backward workspace: D at [0, R) and LSE*log2(e) at [R, 2R) floats, R = B*Hq*N.
+hipError_t launch_bwd_preprocess(const float* o, const void* dO, const float* lse, float* ws,
+                                 const AttnShape& s, hipStream_t stream);
 
-hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
-                           const float* delta, const void* dO, float* dk, float* dv,
-                           const AttnShape& s, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                           const float* ws, float* dk, float* dv, const AttnShape& s,
+                           hipStream_t stream);
 
-hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
-                         const float* delta, const void* dO, float* dq, const AttnShape& s,
-                         hipStream_t stream);
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
+                         const float* ws, float* dq, const AttnShape& s, hipStream_t stream);
 
 }  // namespace fa2

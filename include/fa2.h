@@ -75,8 +75,9 @@ int fa2_forward(const void* q, const void* k, const void* v, float* o, float* ls
                 int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                 hipStream_t stream);
 
-/* Bytes of device workspace fa2_backward needs: one float per query row (D = rowsum(dO*O)),
-   rounded up to 256 bytes. 0 for an empty problem or negative sizes. */
+/* Bytes of device workspace fa2_backward needs: two floats per query row (D = rowsum(dO*O)
+   and LSE*log2(e)), rounded up to 256 bytes. 0 for an empty problem or negative sizes.
+   Layout, with R = B*Hq*N: D at floats [0, R), LSE*log2(e) at floats [R, 2R). */
 size_t fa2_backward_workspace_size(int B, int Hq, int N);
 
 /*
@@ -101,24 +102,27 @@ int fa2_backward(const void* q, const void* k, const void* v, const float* o, co
 /*
  * The three steps of fa2_backward as separate calls, in the order fa2_backward runs them.
  * Each validates its own arguments like fa2_backward (same codes) and enqueues one kernel.
- * Running the three in order on one stream gives bitwise the results of fa2_backward.
+ * Running the three in order on one stream with one workspace gives bitwise the results of
+ * fa2_backward; `workspace` must be at least fa2_backward_workspace_size(B,Hq,N) bytes.
  *
- * fa2_backward_preprocess: delta[i] = sum_c dO[i][c] * o[i][c] for every query row.
- *   o f32 [B,Hq,N,d], dO bf16 [B,Hq,N,d] (read only); delta f32 [B,Hq,N] (written).
+ * fa2_backward_preprocess: fills the workspace from o f32 [B,Hq,N,d], dO bf16 [B,Hq,N,d] and
+ *   lse f32 [B,Hq,N] (all read only): D_i = sum_c dO_ic o_ic and LSE_i * log2(e).
  */
-int fa2_backward_preprocess(const float* o, const void* dO, float* delta, int B, int Hq, int N,
-                            int d, hipStream_t stream);
+int fa2_backward_preprocess(const float* o, const void* dO, const float* lse, void* workspace,
+                            size_t workspace_bytes, int B, int Hq, int N, int d,
+                            hipStream_t stream);
 
-/* fa2_backward_dkdv: dK, dV (f32 [B,Hkv,N,d], written) from q, k, v, lse, delta (the output of
-   fa2_backward_preprocess) and dO; recomputes P from lse, no atomics. */
-int fa2_backward_dkdv(const void* q, const void* k, const void* v, const float* lse,
-                      const float* delta, const void* dO, float* dk, float* dv, int B, int Hq,
-                      int Hkv, int N, int d, int causal, float scale, hipStream_t stream);
+/* fa2_backward_dkdv: dK, dV (f32 [B,Hkv,N,d], written) from q, k, v, dO and a workspace filled
+   by fa2_backward_preprocess (read only); recomputes P from the logsumexp, no atomics. */
+int fa2_backward_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                      const void* workspace, size_t workspace_bytes, float* dk, float* dv,
+                      int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                      hipStream_t stream);
 
 /* fa2_backward_dq: dQ (f32 [B,Hq,N,d], written) from the same inputs as fa2_backward_dkdv. */
-int fa2_backward_dq(const void* q, const void* k, const void* v, const float* lse,
-                    const float* delta, const void* dO, float* dq, int B, int Hq, int Hkv,
-                    int N, int d, int causal, float scale, hipStream_t stream);
+int fa2_backward_dq(const void* q, const void* k, const void* v, const void* dO,
+                    const void* workspace, size_t workspace_bytes, float* dq, int B, int Hq,
+                    int Hkv, int N, int d, int causal, float scale, hipStream_t stream);
 
 /* Static, human-readable name of a status code ("FA2_OK", ...); "FA2_UNKNOWN" otherwise. */
 const char* fa2_status_string(int status);

@@ -38,8 +38,9 @@ def test_status_strings(lib):
 
 
 def test_workspace_size(lib):
-    assert fa2.fa2_backward_workspace_size(4, 16, 4096) == 4 * 16 * 4096 * 4
+    assert fa2.fa2_backward_workspace_size(4, 16, 4096) == 4 * 16 * 4096 * 8
     assert fa2.fa2_backward_workspace_size(1, 1, 3) == 256
+    assert fa2.fa2_backward_workspace_size(1, 1, 33) == 512
     assert fa2.fa2_backward_workspace_size(0, 16, 4096) == 0
     assert fa2.fa2_backward_workspace_size(-1, 16, 4096) == 0
 
@@ -97,15 +98,20 @@ def test_backward_aliasing_and_workspace(lib):
 
 
 def test_phase_entry_points_validate(lib):
-    ok = dict(B=1, Hq=2, Hkv=1, N=64, d=64)
-    assert fa2.fa2_backward_preprocess(P(3), P(5), P(9), 1, 2, 64, 96) == 3
-    assert fa2.fa2_backward_preprocess(P(3), P(5), P(3) + 64, 1, 2, 64, 64) == 7
-    assert fa2.fa2_backward_preprocess(None, P(5), P(9), 1, 2, 64, 64) == 1
-    assert fa2.fa2_backward_preprocess(P(3), P(5), P(9), 0, 2, 64, 64) == 0
-    args = [P(0), P(1), P(2), P(4), P(9), P(5)]
+    W = fa2.fa2_backward_workspace_size(1, 2, 64)
+    pre = lambda **k: fa2.fa2_backward_preprocess(k.get("o", P(3)), k.get("dO", P(5)), k.get("lse", P(4)),
+                                                  k.get("ws", P(9)), k.get("wsb", W), 1, 2, 64, k.get("d", 64))
+    assert pre(d=96) == 3
+    assert pre(ws=P(3) + 64) == 7          # workspace overlaps o
+    assert pre(o=None) == 1
+    assert pre(ws=None) == 8 and pre(wsb=W - 1) == 8
+    assert fa2.fa2_backward_preprocess(P(3), P(5), P(4), P(9), W, 0, 2, 64, 64) == 0
+    args = [P(0), P(1), P(2), P(5), P(9), W]
     assert fa2.fa2_backward_dkdv(*args, P(7), P(8), 1, 2, 1, 64, 128, 1, float("nan")) == 5
     assert fa2.fa2_backward_dkdv(*args, P(7), P(7), 1, 2, 1, 64, 64, 1, 0.1) == 7
     assert fa2.fa2_backward_dkdv(*args, P(7), P(8), 1, 3, 2, 64, 64, 1, 0.1) == 4
+    assert fa2.fa2_backward_dkdv(P(0), P(1), P(2), P(5), P(9), W - 4, P(7), P(8), 1, 2, 1, 64, 64, 1, 0.1) == 8
     assert fa2.fa2_backward_dq(*args, P(0), 1, 2, 1, 64, 64, 1, 0.1) == 7
+    assert fa2.fa2_backward_dq(*args, P(9), 1, 2, 1, 64, 64, 1, 0.1) == 7   # dq over the workspace
     assert fa2.fa2_backward_dq(*args, P(6) + 4, 1, 2, 1, 64, 64, 1, 0.1) == 6
     assert fa2.fa2_backward_dq(*args, P(6), 1, 2, 1, 64, 32, 1, 0.1) == 3

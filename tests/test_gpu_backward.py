@@ -108,3 +108,21 @@ def test_backward_rejects_small_workspace():
     assert st == 8
     torch.cuda.synchronize()
     assert bool((dq == 3).all() and (dk == 3).all() and (dv == 3).all())
+
+
+def test_phases_match_composed_backward():
+    """The three phase entry points, in order on one stream, give fa2_backward's bits."""
+    import torch
+    B, Hq, Hkv, N, d = 1, 4, 2, 333, 128
+    q, k, v, dO = H.make_inputs(4400, B, Hq, Hkv, N, d, with_do=True)
+    qd, kd, vd, dod = H.to_dev(q), H.to_dev(k), H.to_dev(v), H.to_dev(dO)
+    o, lse = fa2.forward(qd, kd, vd, True, 0.09)
+    dq, dk, dv = fa2.backward(qd, kd, vd, o, lse, dod, True, 0.09)
+    W = fa2.fa2_backward_workspace_size(B, Hq, N)
+    ws = torch.empty(W, dtype=torch.uint8, device=qd.device)
+    dq2, dk2, dv2 = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
+    assert fa2.fa2_backward_preprocess(o, dod, lse, ws, W, B, Hq, N, d) == 0
+    assert fa2.fa2_backward_dkdv(qd, kd, vd, dod, ws, W, dk2, dv2, B, Hq, Hkv, N, d, True, 0.09) == 0
+    assert fa2.fa2_backward_dq(qd, kd, vd, dod, ws, W, dq2, B, Hq, Hkv, N, d, True, 0.09) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
