@@ -106,6 +106,20 @@ __device__ __forceinline__ u32x4 tr_pair(const lds_char* lo_base, const lds_char
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
+// Block id -> (head slice, block within head). Workgroups are dealt round-robin to the 8 XCDs
+// (bid & 7 is the XCD); when the slice count divides by 8, each XCD gets a contiguous range of
+// slices and walks their blocks in order, so the blocks of one slice share that XCD's L2.
+__device__ __forceinline__ void map_slice_block(int bid, int nslices, int nblk, int& slice, int& blk) {
+  if ((nslices & 7) == 0) {
+    const int x = bid & 7, s = bid >> 3;
+    slice = x * (nslices >> 3) + s / nblk;
+    blk = s % nblk;
+  } else {
+    slice = bid / nblk;
+    blk = bid % nblk;
+  }
+}
+
 // ------------------------------------------------------------------ 1. preprocess
 
 // delta[i] = D_i = sum_c dO_ic O_ic, and lse2[i] = LSE_i * log2(e) (so the kernels below form
@@ -164,9 +178,8 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
   const int hf = lane >> 5, l32 = lane & 31;
   agpr_accumulators_hint();
   const int N = p.N;
-  const int bid = blockIdx.x;
-  const int kblk = bid % p.nblk;  // causal: low key blocks see the most queries, go first
-  const int bg = bid / p.nblk;
+  int bg, kblk;  // causal: low key blocks see the most queries and go first
+  map_slice_block(blockIdx.x, p.B * p.Hkv, p.nblk, bg, kblk);
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int G = p.Hq / p.Hkv;
   const int k0 = kblk * C::BR;
@@ -175,11 +188,14 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
   const uint32_t head_bytes = (uint32_t)N * C::ROWB;
   const size_t kvoff = ((size_t)b * p.Hkv + g) * (size_t)N * D;
 
-  // Query tiles: every query head of the group, tiles from the one holding key k0 onward.
+  // Query tiles: every query head of the group, tiles from the one holding key k0 to the end,
+  // walked from the LAST tile down, so all key blocks of a head start on the same tiles and
+  // read them at about the same time (shared through L2 instead of each block from HBM).
   const int nqt_all = (N + C::BT - 1) / C::BT;
   const int qt0 = p.causal ? k0 / C::BT : 0;
   const int nqt = nqt_all - qt0;
   const int iters = G * nqt;
+  auto tile_row0 = [&](int it) { return (nqt_all - 1 - it % nqt) * C::BT; };
 
   auto stage = [&](int s) {
     return s ? DkdvStage<D>{(lds_char*)q_st1, (lds_char*)do_st1, (lds_char*)stat_st1}
@@ -189,7 +205,7 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
     if (it >= iters) return;
     const DkdvStage<D> st = stage(it & 1);
     const int hq = g * G + it / nqt;
-    const int qrow0 = (qt0 + it % nqt) * C::BT;
+    const int qrow0 = tile_row0(it);
     const size_t qoff = ((size_t)b * p.Hq + hq) * (size_t)N * D;
     load_tile_dual<D>(make_rsrc(p.q + qoff, head_bytes), st.q, qrow0, wave, lane);
     load_tile_dual<D>(make_rsrc(p.dO + qoff, head_bytes), st.dO, qrow0, wave, lane);
@@ -330,7 +346,7 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
     constexpr int PAR = decltype(par_tag)::value;  // it % 2
     fetch(it + 1);
     const DkdvStage<D> st = stage(PAR);
-    const int qrow0 = (qt0 + it % nqt) * C::BT;
+    const int qrow0 = tile_row0(it);
     // Causal: skip tiles wholly above this wave's keys; mask tiles crossing its diagonal.
     if (!(p.causal && qrow0 + C::BT - 1 < kw)) {
       const bool mask = (p.causal && qrow0 < kw + C::RPW - 1) || (qrow0 + C::BT > N);
@@ -391,9 +407,8 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hf = lane >> 5, l32 = lane & 31;
   const int N = p.N;
-  const int bid = blockIdx.x;
-  const int r = bid % p.nblk;
-  const int bh = bid / p.nblk;
+  int bh, r;
+  map_slice_block(blockIdx.x, p.B * p.Hq, p.nblk, bh, r);
   const int qblk = p.causal ? p.nblk - 1 - r : r;  // longest rows first
   const int b = bh / p.Hq, hq = bh % p.Hq;
   const int hkv = hq / (p.Hq / p.Hkv);
