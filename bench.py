@@ -34,6 +34,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE scaled by a plain copy's readings), or None when there is no entry or the kernel's
+    source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            entry = json.load(f)["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for name in (entry["source"], "fa2_device.h"):
+        with open(os.path.join(ROOT, "exact_tiled_attention_fa2_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return entry["hbm_bytes"] if h.hexdigest() == entry["source_sha256"] else None
+
+
 def counted_fwd_flops(B, Hq, N, d, causal):
     f = 4.0 * B * Hq * N * N * d
     return f / 2 if causal else f
@@ -191,7 +209,7 @@ def main():
     bound, work, unit, peak = algo[dom]
     achieved = work / (avg[dom] * 1e-3)
     roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom}
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(dom), "kernel": dom}
 
     cpu = None
     if not args.no_cpu_baseline:
