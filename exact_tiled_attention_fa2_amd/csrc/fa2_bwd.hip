@@ -106,6 +106,15 @@ __device__ __forceinline__ u32x4 tr_pair(const lds_char* lo_base, const lds_char
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1, fully unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // Block id -> (head slice, block within head). Workgroups are dealt round-robin to the 8 XCDs
 // (bid & 7 is the XCD); when the slice count divides by 8, each XCD gets a contiguous range of
 // slices and walks their blocks in order, so the blocks of one slice share that XCD's L2.
@@ -174,7 +183,8 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char stat_st0[2048];
   __shared__ __attribute__((aligned(1024))) char stat_st1[2048];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
   agpr_accumulators_hint();
   const int N = p.N;
@@ -251,92 +261,128 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
   const float c = p.c;
   const int key = kw + l32;
 
-  // One query tile for this wave. MASK: the tile reaches the wave's diagonal or the end of
-  // the sequence. S/dP MFMAs with operands read one step ahead; P and dS on the VALU; then
-  // dV^T += dO^T P and dK^T += Q^T dS with transposed operands read one step ahead.
-  auto tile = [&](const DkdvStage<D>& st, int qrow0, bool mask) __attribute__((always_inline)) {
+  // One query tile for this wave, as one unrolled sequence of NS MFMA steps:
+  //   S (Q K^T, row blocks mb = 0, 1) | dP (dO V^T) | dV^T += dO^T P | dK^T += Q^T dS.
+  // Each step issues the LDS read of the operand PF steps ahead, one MFMA, and a slice of
+  // VALU work whose inputs are complete by then: P = 2^(S c - lse2) of row block 0 while
+  // the S MFMAs of block 1 run, P of block 1 during dP of block 0, and dS = P (dP - D) of
+  // blocks 0 and 1 during dP of block 1 and the first dV steps. Scheduling fences keep the
+  // order, so the exponentials and products hide under the matrix pipe.
+  // Rows past the end of the sequence need no mask: their Q, dO, D and LSE read as zero, so
+  // P = 1 there but dO = 0 and dS = 1 * (0 - 0) = 0, and they add nothing to dV or dK.
+  // A tile crossing the wave's causal diagonal (diag) has P zeroed above the diagonal by a
+  // fix-up between the exponentials and the first dS.
+  constexpr int KS = C::KS, DB = C::DB;
+  constexpr int NS = 4 * KS + 8 * DB;  // MFMA steps per tile
+  constexpr int PF = 3;                // operand reads in flight ahead of the MFMA using them
+  constexpr int DL = 2;                // steps between an accumulator's last MFMA and its use
+  constexpr int EPS = 16 / KS;         // elements of one row block handled per VALU step
+  auto tile = [&](const DkdvStage<D>& st, int qrow0, bool diag) __attribute__((always_inline)) {
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       s[mb] = f32x16{};
       dp[mb] = f32x16{};
     }
-    {
-      u32x4 qa[2][2], da[2][2];  // [buffer][mb]
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        qa[0][mb] = lds_read16(st.q + roff[0] + mb * 32 * C::ROWB);
-        da[0][mb] = lds_read16(st.dO + roff[0] + mb * 32 * C::ROWB);
-      }
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        if (ks + 1 < C::KS) {
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            qa[(ks + 1) & 1][mb] = lds_read16(st.q + roff[ks + 1] + mb * 32 * C::ROWB);
-            da[(ks + 1) & 1][mb] = lds_read16(st.dO + roff[ks + 1] + mb * 32 * C::ROWB);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          s[mb] = mfma32x32x16(qa[ks & 1][mb], kf[ks], s[mb]);
-          dp[mb] = mfma32x32x16(da[ks & 1][mb], vf[ks], dp[mb]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // P = 2^(S c - lse2), dS = P (dP - D); registers hold query rows 32mb + 8rq + 4hf + e.
+    float pf[2][16];           // P in fp32, kept for dS
     u32x4 pp[2][2], pd[2][2];  // B operands [mb][h]: 16 queries x 32 keys, packed bf16
+    f32x4 lse4[2][4], d4[2][4];
     const FA2_LDS float* dstat = (const FA2_LDS float*)st.stat;
     const FA2_LDS float* lstat = (const FA2_LDS float*)(st.stat + 1024);
+    auto load_stats = [&](const FA2_LDS float* base, f32x4 (&dst)[2][4], int mb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int rq = 0; rq < 4; ++rq) dst[mb][rq] = *(const FA2_LDS f32x4*)(base + 32 * mb + 8 * rq + 4 * hf);
+    };
+    auto exp_part = [&](int mb, int part) __attribute__((always_inline)) {
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int r0 = 32 * mb + 8 * rq + 4 * hf;
-        const f32x4 l4 = *(const FA2_LDS f32x4*)(lstat + r0);
-        const f32x4 d4 = *(const FA2_LDS f32x4*)(dstat + r0);
-        float pv[4], dsv[4];
+      for (int r = part * EPS; r < (part + 1) * EPS; r += 2) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float pe = fast_exp2(__builtin_fmaf(s[mb][4 * rq + e], c, -l4[e]));
-          if (mask) {
-            const int qi = qrow0 + r0 + e;
-            pe = (qi >= N || (p.causal && key > qi)) ? 0.f : pe;
+        for (int u = 0; u < 2; ++u) {
+          const int rr = r + u;
+          pf[mb][rr] = fast_exp2(__builtin_fmaf(s[mb][rr], c, -lse4[mb][rr >> 2][rr & 3]));
+        }
+        pp[mb][r >> 3][(r >> 1) & 3] = pack_bf16(pf[mb][r], pf[mb][r + 1]);
+      }
+    };
+    // Registers hold query rows 32 mb + 8 (r / 4) + 4 hf + r % 4 of row block mb; the row is
+    // visible to this lane's key iff 32 mb + 8 (r / 4) + r % 4 >= lo.
+    auto causal_fixup = [&]() __attribute__((always_inline)) {
+      const int lo = key - qrow0 - 4 * hf;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int x = 32 * mb + 8 * ((r + u) >> 2) + ((r + u) & 3);
+            pf[mb][r + u] = x >= lo ? pf[mb][r + u] : 0.f;
           }
-          pv[e] = pe;
-          dsv[e] = pe * (dp[mb][4 * rq + e] - d4[e]);
+          pp[mb][r >> 3][(r >> 1) & 3] = pack_bf16(pf[mb][r], pf[mb][r + 1]);
         }
-        pp[mb][rq >> 1][2 * (rq & 1)] = pack_bf16(pv[0], pv[1]);
-        pp[mb][rq >> 1][2 * (rq & 1) + 1] = pack_bf16(pv[2], pv[3]);
-        pd[mb][rq >> 1][2 * (rq & 1)] = pack_bf16(dsv[0], dsv[1]);
-        pd[mb][rq >> 1][2 * (rq & 1) + 1] = pack_bf16(dsv[2], dsv[3]);
-      }
-    // Contraction over the tile's 64 queries; step i = (mb, h, db) with db fastest.
-    {
-      constexpr int NSTEP = 4 * C::DB;
-      auto trread = [&](const lds_char* base, int i) {
-        const int db = i % C::DB, mb = i / (2 * C::DB), h = (i / C::DB) & 1;
-        const int rowsel = (32 * mb + 16 * h) * C::ROWB;
-        return tr_pair(base + toff[db] + rowsel, base + toff8[db] + rowsel);
-      };
-      u32x4 ta[2][2];  // [buffer][dO^T, Q^T]
-      ta[0][0] = trread(st.dO, 0);
-      ta[0][1] = trread(st.q, 0);
+    };
+    auto ds_part = [&](int mb, int part) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < NSTEP; ++i) {
-        if (i + 1 < NSTEP) {
-          ta[(i + 1) & 1][0] = trread(st.dO, i + 1);
-          ta[(i + 1) & 1][1] = trread(st.q, i + 1);
+      for (int r = part * EPS; r < (part + 1) * EPS; r += 2) {
+        float dv2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int rr = r + u;
+          dv2[u] = pf[mb][rr] * (dp[mb][rr] - d4[mb][rr >> 2][rr & 3]);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        const int db = i % C::DB, mb = i / (2 * C::DB), h = (i / C::DB) & 1;
-        adv[db] = mfma32x32x16(ta[i & 1][0], pp[mb][h], adv[db]);
-        adk[db] = mfma32x32x16(ta[i & 1][1], pd[mb][h], adk[db]);
-        __builtin_amdgcn_sched_barrier(0);
+        pd[mb][r >> 3][(r >> 1) & 3] = pack_bf16(dv2[0], dv2[1]);
       }
-    }
+    };
+    auto trread = [&](const lds_char* base, int i) __attribute__((always_inline)) {
+      const int db = i % DB, mb = i / (2 * DB), h = (i / DB) & 1;
+      const int rowsel = (32 * mb + 16 * h) * C::ROWB;
+      return tr_pair(base + toff[db] + rowsel, base + toff8[db] + rowsel);
+    };
+    auto read_op = [&](auto J) __attribute__((always_inline)) -> u32x4 {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j < 2 * KS) return lds_read16(st.q + roff[j % KS] + (j / KS) * 32 * C::ROWB);
+      else if constexpr (j < 4 * KS) return lds_read16(st.dO + roff[j % KS] + ((j - 2 * KS) / KS) * 32 * C::ROWB);
+      else if constexpr (j < 4 * KS + 4 * DB) return trread(st.dO, j - 4 * KS);
+      else return trread(st.q, j - 4 * KS - 4 * DB);
+    };
+    auto mfma_step = [&](auto J, u32x4 a) __attribute__((always_inline)) {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j < 2 * KS) {
+        s[j / KS] = mfma32x32x16(a, kf[j % KS], s[j / KS]);
+      } else if constexpr (j < 4 * KS) {
+        constexpr int jj = j - 2 * KS;
+        dp[jj / KS] = mfma32x32x16(a, vf[jj % KS], dp[jj / KS]);
+      } else if constexpr (j < 4 * KS + 4 * DB) {
+        constexpr int i = j - 4 * KS, db = i % DB, mb = i / (2 * DB), h = (i / DB) & 1;
+        adv[db] = mfma32x32x16(a, pp[mb][h], adv[db]);
+      } else {
+        constexpr int i = j - 4 * KS - 4 * DB, db = i % DB, mb = i / (2 * DB), h = (i / DB) & 1;
+        adk[db] = mfma32x32x16(a, pd[mb][h], adk[db]);
+      }
+    };
+    auto valu_step = [&](auto J) __attribute__((always_inline)) {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j == 0) load_stats(lstat, lse4, 0);
+      if constexpr (j == KS) load_stats(lstat, lse4, 1);
+      if constexpr (j == 2 * KS) load_stats(dstat, d4, 0);
+      if constexpr (j == 3 * KS) load_stats(dstat, d4, 1);
+      if constexpr (j >= KS + DL && j < 2 * KS + DL) exp_part(0, j - KS - DL);
+      if constexpr (j >= 2 * KS + DL && j < 3 * KS + DL) exp_part(1, j - 2 * KS - DL);
+      if constexpr (j == 3 * KS + DL) {
+        if (diag) causal_fixup();
+      }
+      if constexpr (j >= 3 * KS + DL && j < 4 * KS + DL) ds_part(0, j - 3 * KS - DL);
+      if constexpr (j >= 4 * KS + DL && j < 5 * KS + DL) ds_part(1, j - 4 * KS - DL);
+    };
+    u32x4 ring[PF + 1];
+    static_for<0, PF>([&](auto J) __attribute__((always_inline)) { ring[decltype(J)::value] = read_op(J); });
+    static_for<0, NS>([&](auto J) __attribute__((always_inline)) {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j + PF < NS) ring[(j + PF) % (PF + 1)] = read_op(std::integral_constant<int, j + PF>{});
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(J, ring[j % (PF + 1)]);
+      valu_step(J);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
   auto sync_stage = [&]() {
     wait_vmem_all();
@@ -347,11 +393,8 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
     fetch(it + 1);
     const DkdvStage<D> st = stage(PAR);
     const int qrow0 = tile_row0(it);
-    // Causal: skip tiles wholly above this wave's keys; mask tiles crossing its diagonal.
-    if (!(p.causal && qrow0 + C::BT - 1 < kw)) {
-      const bool mask = (p.causal && qrow0 < kw + C::RPW - 1) || (qrow0 + C::BT > N);
-      tile(st, qrow0, mask);
-    }
+    // Causal: skip tiles wholly above this wave's keys; fix up tiles crossing its diagonal.
+    if (!(p.causal && qrow0 + C::BT - 1 < kw)) tile(st, qrow0, p.causal && qrow0 < kw + C::RPW - 1);
     sync_stage();
   };
 
