@@ -429,26 +429,32 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
 
 template <int D>
 struct DqCfg {
-  static constexpr int WAVES = 8;           // two waves per SIMD
-  static constexpr int RPW = 32;            // query rows per wave
+  static constexpr int WAVES = 4;           // one wave per SIMD
+  static constexpr int RPW = 64;            // query rows per wave: two 32-row blocks qb
   static constexpr int BR = WAVES * RPW;    // query rows per workgroup
-  static constexpr int BT = 64;             // keys per streamed tile
+  static constexpr int BT = 64;             // keys per streamed tile: two 32-key halves
   static constexpr int TILE = BT * D * 2;
-  static constexpr int LPW = TILE / 1024 / WAVES;
 };
 
 template <int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fa2_bwd_dq_kernel(BwdParams p) {
   using C = BwdCfg<D>;
   using Q = DqCfg<D>;
+  static_assert(Q::WAVES == C::WAVES && Q::BT == C::BT, "tiles are loaded by load_tile_dual");
+  constexpr int KS = C::KS, DB = C::DB;
+  // Three stages of K and V, in separate arrays (a DMA into one never aliases reads of another).
   __shared__ __attribute__((aligned(1024))) char k_st0[Q::TILE];
   __shared__ __attribute__((aligned(1024))) char k_st1[Q::TILE];
+  __shared__ __attribute__((aligned(1024))) char k_st2[Q::TILE];
   __shared__ __attribute__((aligned(1024))) char v_st0[Q::TILE];
   __shared__ __attribute__((aligned(1024))) char v_st1[Q::TILE];
+  __shared__ __attribute__((aligned(1024))) char v_st2[Q::TILE];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
+  agpr_accumulators_hint();
   const int N = p.N;
   int bh, r;
   map_slice_block(blockIdx.x, p.B * p.Hq, p.nblk, bh, r);
@@ -456,7 +462,7 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   const int b = bh / p.Hq, hq = bh % p.Hq;
   const int hkv = hq / (p.Hq / p.Hkv);
   const int q0 = qblk * Q::BR;
-  const int qw = q0 + wave * Q::RPW;
+  const int qw = q0 + wave * Q::RPW;  // this wave's first query
 
   const uint32_t head_bytes = (uint32_t)N * C::ROWB;
   const size_t qoff = (size_t)bh * N * D;
@@ -464,148 +470,225 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + kvoff, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + kvoff, head_bytes);
 
+  // Key tiles of the workgroup (causal: up to its last row); halves u = 0 .. 2 ntiles - 1.
   const int qend = min(q0 + Q::BR, N);
   const int ntiles = p.causal ? (qend + Q::BT - 1) / Q::BT : (N + Q::BT - 1) / Q::BT;
-  // Tiles this wave computes (causal: up to its last row).
-  const int nmine = p.causal ? min(ntiles, (qw + Q::RPW - 1) / Q::BT + 1) : ntiles;
+  // Last half this wave computes (causal: the one holding its last row); -1 if it has no rows.
+  const int my_last = qw >= N ? -1 : (p.causal ? min(2 * ntiles - 1, (qw + Q::RPW - 1) / 32) : 2 * ntiles - 1);
 
-  auto fetch = [&](int t) {
-    if (t >= ntiles) return;
-    lds_char* kd = (t & 1) ? (lds_char*)k_st1 : (lds_char*)k_st0;
-    lds_char* vd = (t & 1) ? (lds_char*)v_st1 : (lds_char*)v_st0;
-#pragma unroll
-    for (int i = 0; i < Q::LPW; ++i) {
-      const int blk = wave * Q::LPW + i;
-      const int pos = blk * 1024 + lane * 16;
-      const int rr = pos / C::ROWB;
-      const int cp = (pos % C::ROWB) / 16;
-      const uint32_t off = (uint32_t)(t * Q::BT + rr) * C::ROWB + ((cp ^ swz_dual<D>(rr)) << 4);
-      buffer_load16_lds(rk, kd + blk * 1024, off);
-      buffer_load16_lds(rv, vd + blk * 1024, off);
-    }
+  auto kst = [&](auto S) __attribute__((always_inline)) {
+    constexpr int s = decltype(S)::value;
+    return (lds_char*)(s == 0 ? k_st0 : s == 1 ? k_st1 : k_st2);
   };
-  fetch(0);
+  auto vst = [&](auto S) __attribute__((always_inline)) {
+    constexpr int s = decltype(S)::value;
+    return (lds_char*)(s == 0 ? v_st0 : s == 1 ? v_st1 : v_st2);
+  };
+  // Tile t <= ntiles (tile ntiles only feeds the look-ahead half of the last step; rows past
+  // the end read as zero).
+  auto fetch = [&](auto S, int t) __attribute__((always_inline)) {
+    if (t > ntiles) return;
+    load_tile_dual<D>(rk, kst(S), t * Q::BT, wave, lane);
+    load_tile_dual<D>(rv, vst(S), t * Q::BT, wave, lane);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  fetch(I0{}, 0);
+  fetch(I1{}, 1);
 
-  // Q and dO of this wave's 32 queries as B operands (lane = query, k = head dim).
-  u32x4 qf[C::KS], df[C::KS];
-  const int qi = qw + l32;
+  // Q and dO of this wave's 64 queries as B operands (lane = query, k = head dim).
+  u32x4 qf[2][KS], df[2][KS];
+  float lse2v[2], dltv[2];
   {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + qoff, head_bytes);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dO + qoff, head_bytes);
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const uint32_t off = (uint32_t)qi * C::ROWB + (16 * ks + 8 * hf) * 2;
-      qf[ks] = buffer_load16(rq, off) ^ p.kneg;
-      df[ks] = buffer_load16(rd, off);
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qi = qw + 32 * qb + l32;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t off = (uint32_t)qi * C::ROWB + (16 * ks + 8 * hf) * 2;
+        qf[qb][ks] = buffer_load16(rq, off) ^ p.kneg;
+        df[qb][ks] = buffer_load16(rd, off);
+      }
+      lse2v[qb] = qi < N ? p.lse2[(size_t)bh * N + qi] : 0.f;
+      dltv[qb] = qi < N ? p.delta[(size_t)bh * N + qi] : 0.f;
     }
   }
-  const float lse2 = qi < N ? p.lse2[(size_t)bh * N + qi] : 0.f;
-  const float dlt = qi < N ? p.delta[(size_t)bh * N + qi] : 0.f;
 
-  int roff[C::KS], toff[C::DB], toff8[C::DB];
+  int roff[KS], toff[DB], toff8[DB];
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) roff[ks] = row_read_off<D>(lane, ks);
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = row_read_off<D>(lane, ks);
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) {
+  for (int db = 0; db < DB; ++db) {
     toff[db] = tr_read_off<D>(lane, db, 0);
     toff8[db] = tr_read_off<D>(lane, db, 1);
   }
 
-  f32x16 adq[C::DB];  // dQ^T: rows = head dim, columns = queries (lanes)
+  f32x16 adq[2][DB];  // dQ^T per row block: rows = head dim, columns = queries (lanes)
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) adq[db] = f32x16{};
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) adq[qb][db] = f32x16{};
   const float c = p.c;
 
-  // One K/V tile, as two halves of 32 keys (kb) processed in turn to bound register use:
-  // S^T = K Q^T and dP^T = V dO^T (operands one step ahead), dS^T = P^T (dP^T - D) on the
-  // VALU, then dQ^T += K^T dS^T with the transposed K operands one step ahead.
-  auto tile = [&](const lds_char* kt, const lds_char* vt, int j0, bool mask) __attribute__((always_inline)) {
-    const int lim = p.causal ? min(qi, N - 1) : N - 1;
+  // Per 32-key half u: S^T = K Q^T and dP^T = V dO^T (32 keys x 32 queries per row block;
+  // register r holds key 8 (r / 4) + 4 hf + r % 4 of the half, lane = query),
+  // P^T = 2^(S^T c - lse2), dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
+  // The work is software-pipelined across halves. Step u runs S(u+1) MFMAs beside dS(u),
+  // then dQ(u) MFMAs beside P(u+1), then dP(u+1) MFMAs beside the rest of P(u+1).
+  // Each step reads one A operand (shared by both row blocks) PF steps ahead.
+  f32x16 s[2], dp[2];
+  float pf[2][16];      // P^T of the half in flight, fp32
+  u32x4 pd[2][2];       // dS^T as B operands [qb][h]: 16 keys x 32 queries, packed bf16
+  constexpr int NST = 2 * KS + 2 * DB;  // steps per half
+  constexpr int PF = 3;
+  constexpr int DL = 2;                 // steps between an accumulator's last MFMA and its use
+  constexpr int EXP0 = KS + DL, EXPN = NST - EXP0;  // steps carrying P(u+1)
+
+  auto exp_el = [&](int e) __attribute__((always_inline)) {
+    const int qb = e >> 4, rr = e & 15;
+    pf[qb][rr] = fast_exp2(__builtin_fmaf(s[qb][rr], c, -lse2v[qb]));
+  };
+  // dS elements in h-major order, so pd[.][0] is complete before pd[.][1].
+  auto ds_pair = [&](int e) __attribute__((always_inline)) {
+    const int h = e >> 4, qb = (e >> 3) & 1, rr = 8 * h + (e & 7);
+    const float a = pf[qb][rr] * (dp[qb][rr] - dltv[qb]);
+    const float bb = pf[qb][rr + 1] * (dp[qb][rr + 1] - dltv[qb]);
+    pd[qb][h][(rr >> 1) & 3] = pack_bf16(a, bb);
+  };
+  // Causal: zero P^T where key > query (half u crossing this wave's diagonal).
+  auto causal_fixup = [&](int u) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-      {
-        u32x4 ka[2], va[2];
-        ka[0] = lds_read16(kt + roff[0] + kb * 32 * C::ROWB);
-        va[0] = lds_read16(vt + roff[0] + kb * 32 * C::ROWB);
+    for (int qb = 0; qb < 2; ++qb) {
+      const int lim = qw + 32 * qb + l32 - 32 * u - 4 * hf;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          if (ks + 1 < C::KS) {
-            ka[(ks + 1) & 1] = lds_read16(kt + roff[ks + 1] + kb * 32 * C::ROWB);
-            va[(ks + 1) & 1] = lds_read16(vt + roff[ks + 1] + kb * 32 * C::ROWB);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          s = mfma32x32x16(ka[ks & 1], qf[ks], s);
-          dp = mfma32x32x16(va[ks & 1], df[ks], dp);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      u32x4 pd[2];  // dS^T as B operands [h]: 16 keys x 32 queries, packed bf16
-#pragma unroll
-      for (int rr = 0; rr < 16; rr += 2) {
-        float ds2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          float pe = fast_exp2(__builtin_fmaf(s[rr + e], c, -lse2));
-          if (mask) {
-            const int kj = j0 + 32 * kb + 8 * ((rr + e) >> 2) + 4 * hf + ((rr + e) & 3);
-            pe = kj > lim ? 0.f : pe;
-          }
-          ds2[e] = pe * (dp[rr + e] - dlt);
-        }
-        pd[rr >> 3][(rr >> 1) & 3] = pack_bf16(ds2[0], ds2[1]);
-      }
-      // step i = (h, db) with db fastest
-      constexpr int NSTEP = 2 * C::DB;
-      auto trread = [&](int i) {
-        const int db = i % C::DB, h = i / C::DB;
-        const int rowsel = (32 * kb + 16 * h) * C::ROWB;
-        return tr_pair(kt + toff[db] + rowsel, kt + toff8[db] + rowsel);
-      };
-      u32x4 ta[2];
-      ta[0] = trread(0);
-#pragma unroll
-      for (int i = 0; i < NSTEP; ++i) {
-        if (i + 1 < NSTEP) ta[(i + 1) & 1] = trread(i + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        adq[i % C::DB] = mfma32x32x16(ta[i & 1], pd[i / C::DB], adq[i % C::DB]);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int rr = 0; rr < 16; ++rr) {
+        const int x = 8 * (rr >> 2) + (rr & 3);
+        pf[qb][rr] = x > lim ? 0.f : pf[qb][rr];
       }
     }
   };
-  auto sync_stage = [&]() {
+
+  auto half = [&](auto SC, auto KBC, auto SN, auto KBN, int u) __attribute__((always_inline)) {
+    constexpr int kbc = decltype(KBC)::value, kbn = decltype(KBN)::value;
+    const lds_char* kc = kst(SC) + kbc * 32 * C::ROWB;
+    const lds_char* kn = kst(SN) + kbn * 32 * C::ROWB;
+    const lds_char* vn = vst(SN) + kbn * 32 * C::ROWB;
+    const bool diag = p.causal && 32 * u + 31 > qw;
+    auto read_op = [&](auto J) __attribute__((always_inline)) -> u32x4 {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j < KS) {
+        return lds_read16(kn + roff[j]);
+      } else if constexpr (j < KS + 2 * DB) {
+        constexpr int i = j - KS, db = i % DB, h = i / DB;
+        return tr_pair(kc + toff[db] + 16 * h * C::ROWB, kc + toff8[db] + 16 * h * C::ROWB);
+      } else {
+        return lds_read16(vn + roff[j - KS - 2 * DB]);
+      }
+    };
+    auto mfma_step = [&](auto J, u32x4 a) __attribute__((always_inline)) {
+      constexpr int j = decltype(J)::value;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        // S(u+1) and dP(u+1) start from zero; dP(u) stays live until dS(u) is done.
+        if constexpr (j < KS) {
+          s[qb] = mfma32x32x16(a, qf[qb][j], j == 0 ? f32x16{} : s[qb]);
+        } else if constexpr (j < KS + 2 * DB) {
+          constexpr int i = j - KS, db = i % DB, h = i / DB;
+          adq[qb][db] = mfma32x32x16(a, pd[qb][h], adq[qb][db]);
+        } else {
+          constexpr int ks = j - KS - 2 * DB;
+          dp[qb] = mfma32x32x16(a, df[qb][ks], ks == 0 ? f32x16{} : dp[qb]);
+        }
+      }
+    };
+    auto valu_step = [&](auto J) __attribute__((always_inline)) {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j == 0) {
+        if (diag) causal_fixup(u);
+      }
+      if constexpr (j >= DL && j < DL + KS) {
+        constexpr int per = 16 / KS;  // element pairs per step
+#pragma unroll
+        for (int e = (j - DL) * per; e < (j - DL + 1) * per; ++e) ds_pair(2 * e);
+      }
+      if constexpr (j >= EXP0) {
+        constexpr int e0 = (32 * (j - EXP0)) / EXPN, e1 = (32 * (j - EXP0 + 1)) / EXPN;
+#pragma unroll
+        for (int e = e0; e < e1; ++e) exp_el(e);
+      }
+    };
+    u32x4 ring[PF + 1];
+    static_for<0, PF>([&](auto J) __attribute__((always_inline)) { ring[decltype(J)::value] = read_op(J); });
+    static_for<0, NST>([&](auto J) __attribute__((always_inline)) {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j + PF < NST) ring[(j + PF) % (PF + 1)] = read_op(std::integral_constant<int, j + PF>{});
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(J, ring[j % (PF + 1)]);
+      valu_step(J);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  wait_vmem_all();
+  __syncthreads();
+  // Prologue: S(0), dP(0) and P(0) from the first half of tile 0.
+  if (my_last >= 0) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      s[qb] = f32x16{};
+      dp[qb] = f32x16{};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 ka = lds_read16((const lds_char*)k_st0 + roff[ks]);
+      const u32x4 va = lds_read16((const lds_char*)v_st0 + roff[ks]);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        s[qb] = mfma32x32x16(ka, qf[qb][ks], s[qb]);
+        dp[qb] = mfma32x32x16(va, df[qb][ks], dp[qb]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) exp_el(e);
+  }
+
+  // Tile T: half 2T, then (all waves past their reads of tile T-1, tile T+1 landed) the DMA of
+  // tile T+2 into T-1's stage, then half 2T+1, which looks ahead into tile T+1.
+  auto tile_iter = [&](auto S, int T) __attribute__((always_inline)) {
+    constexpr int st = decltype(S)::value;
+    using SN = std::integral_constant<int, (st + 1) % 3>;
+    using SN2 = std::integral_constant<int, (st + 2) % 3>;
+    if (2 * T <= my_last) half(S, I0{}, S, I1{}, 2 * T);
     wait_vmem_all();
     __syncthreads();
+    fetch(SN2{}, T + 2);
+    if (2 * T + 1 <= my_last) half(S, I1{}, SN{}, I0{}, 2 * T + 1);
   };
-  auto step = [&](auto par_tag, int t) {
-    constexpr int PAR = decltype(par_tag)::value;
-    fetch(t + 1);
-    if (t < nmine) {
-      const int j0 = t * Q::BT;
-      const bool mask = (p.causal && j0 + Q::BT - 1 > qw) || (j0 + Q::BT > N);
-      tile((const lds_char*)(PAR ? k_st1 : k_st0), (const lds_char*)(PAR ? v_st1 : v_st0), j0, mask);
-    }
-    sync_stage();
-  };
-
-  sync_stage();
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
-    step(P0{}, t);
-    step(P1{}, t + 1);
+  int T = 0;
+  for (; T + 3 <= ntiles; T += 3) {
+    tile_iter(I0{}, T);
+    tile_iter(I1{}, T + 1);
+    tile_iter(I2{}, T + 2);
   }
-  if (t < ntiles) step(P0{}, t);
+  if (T < ntiles) tile_iter(I0{}, T);
+  if (T + 1 < ntiles) tile_iter(I1{}, T + 1);
 
-  if (qi < N) {
-    float* dqrow = p.dq + qoff + (size_t)qi * D;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qi = qw + 32 * qb + l32;
+    if (qi < N) {
+      float* dqrow = p.dq + qoff + (size_t)qi * D;
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq)
-        *(f32x4*)(dqrow + 32 * db + 8 * rq + 4 * hf) =
-            f32x4{adq[db][4 * rq], adq[db][4 * rq + 1], adq[db][4 * rq + 2], adq[db][4 * rq + 3]} * p.scale;
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq)
+          *(f32x4*)(dqrow + 32 * db + 8 * rq + 4 * hf) =
+              f32x4{adq[qb][db][4 * rq], adq[qb][db][4 * rq + 1], adq[qb][db][4 * rq + 2],
+                    adq[qb][db][4 * rq + 3]} * p.scale;
+    }
   }
 }
 
