@@ -264,19 +264,23 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
   // One query tile for this wave, as one unrolled sequence of NS MFMA steps:
   //   S (Q K^T, row blocks mb = 0, 1) | dP (dO V^T) | dV^T += dO^T P | dK^T += Q^T dS.
   // Each step issues the LDS read of the operand PF steps ahead, one MFMA, and a slice of
-  // VALU work whose inputs are complete by then: P = 2^(S c - lse2) of row block 0 while
-  // the S MFMAs of block 1 run, P of block 1 during dP of block 0, and dS = P (dP - D) of
-  // blocks 0 and 1 during dP of block 1 and the first dV steps. Scheduling fences keep the
-  // order, so the exponentials and products hide under the matrix pipe.
+  // VALU work whose inputs are complete by then. The VALU work is spread at an even rate so
+  // that every step's share fits beside its MFMA: P = 2^(S c - lse2) of row block 0 from
+  // step KS + DL on (one element per step at d = 128), then P of block 1, then dS = P (dP - D)
+  // of blocks 0 and 1 (one pair per step); each packed operand is complete before the first
+  // MFMA that reads it. Scheduling fences keep the order.
   // Rows past the end of the sequence need no mask: their Q, dO, D and LSE read as zero, so
   // P = 1 there but dO = 0 and dS = 1 * (0 - 0) = 0, and they add nothing to dV or dK.
-  // A tile crossing the wave's causal diagonal (diag) has P zeroed above the diagonal by a
-  // fix-up between the exponentials and the first dS.
+  // A tile crossing the wave's causal diagonal (diag) has P zeroed above the diagonal, eight
+  // rows at a time, in the step that completes those rows' exponentials.
   constexpr int KS = C::KS, DB = C::DB;
   constexpr int NS = 4 * KS + 8 * DB;  // MFMA steps per tile
   constexpr int PF = 3;                // operand reads in flight ahead of the MFMA using them
   constexpr int DL = 2;                // steps between an accumulator's last MFMA and its use
-  constexpr int EPS = 16 / KS;         // elements of one row block handled per VALU step
+  constexpr int EXP_RATE = 8 / KS;     // P elements per step
+  constexpr int DS_RATE = 8 / KS;      // dS element pairs per step
+  auto exp_start = [](int mb) { return KS + DL + 2 * KS * mb; };  // 2 KS steps per row block
+  auto ds_start = [](int mb) { return 5 * KS + DL + KS * mb; };   // KS steps per row block
   auto tile = [&](const DkdvStage<D>& st, int qrow0, bool diag) __attribute__((always_inline)) {
     f32x16 s[2], dp[2];
 #pragma unroll
@@ -293,42 +297,36 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) dst[mb][rq] = *(const FA2_LDS f32x4*)(base + 32 * mb + 8 * rq + 4 * hf);
     };
-    auto exp_part = [&](int mb, int part) __attribute__((always_inline)) {
-#pragma unroll
-      for (int r = part * EPS; r < (part + 1) * EPS; r += 2) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int rr = r + u;
-          pf[mb][rr] = fast_exp2(__builtin_fmaf(s[mb][rr], c, -lse4[mb][rr >> 2][rr & 3]));
-        }
-        pp[mb][r >> 3][(r >> 1) & 3] = pack_bf16(pf[mb][r], pf[mb][r + 1]);
-      }
-    };
     // Registers hold query rows 32 mb + 8 (r / 4) + 4 hf + r % 4 of row block mb; the row is
-    // visible to this lane's key iff 32 mb + 8 (r / 4) + r % 4 >= lo.
-    auto causal_fixup = [&]() __attribute__((always_inline)) {
+    // visible to this lane's key iff 32 mb + 8 (r / 4) + r % 4 >= key - qrow0 - 4 hf.
+    auto causal_fixup = [&](int mb, int h) __attribute__((always_inline)) {
       const int lo = key - qrow0 - 4 * hf;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int x = 32 * mb + 8 * ((r + u) >> 2) + ((r + u) & 3);
-            pf[mb][r + u] = x >= lo ? pf[mb][r + u] : 0.f;
-          }
-          pp[mb][r >> 3][(r >> 1) & 3] = pack_bf16(pf[mb][r], pf[mb][r + 1]);
-        }
-    };
-    auto ds_part = [&](int mb, int part) __attribute__((always_inline)) {
-#pragma unroll
-      for (int r = part * EPS; r < (part + 1) * EPS; r += 2) {
-        float dv2[2];
+      for (int r = 8 * h; r < 8 * h + 8; r += 2) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int rr = r + u;
-          dv2[u] = pf[mb][rr] * (dp[mb][rr] - d4[mb][rr >> 2][rr & 3]);
+          const int x = 32 * mb + 8 * ((r + u) >> 2) + ((r + u) & 3);
+          pf[mb][r + u] = x >= lo ? pf[mb][r + u] : 0.f;
         }
+        pp[mb][h][(r >> 1) & 3] = pack_bf16(pf[mb][r], pf[mb][r + 1]);
+      }
+    };
+    // P elements [e0, e1) of row block mb; a pair is packed once both halves exist.
+    auto exp_part = [&](int mb, int e0, int e1) __attribute__((always_inline)) {
+#pragma unroll
+      for (int rr = e0; rr < e1; ++rr) {
+        pf[mb][rr] = fast_exp2(__builtin_fmaf(s[mb][rr], c, -lse4[mb][rr >> 2][rr & 3]));
+        if (rr & 1) pp[mb][rr >> 3][(rr >> 1) & 3] = pack_bf16(pf[mb][rr - 1], pf[mb][rr]);
+      }
+    };
+    // dS element pairs [q0, q1) of row block mb.
+    auto ds_part = [&](int mb, int q0, int q1) __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = q0; q < q1; ++q) {
+        const int r = 2 * q;
+        float dv2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) dv2[u] = pf[mb][r + u] * (dp[mb][r + u] - d4[mb][(r + u) >> 2][(r + u) & 3]);
         pd[mb][r >> 3][(r >> 1) & 3] = pack_bf16(dv2[0], dv2[1]);
       }
     };
@@ -362,16 +360,22 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
     auto valu_step = [&](auto J) __attribute__((always_inline)) {
       constexpr int j = decltype(J)::value;
       if constexpr (j == 0) load_stats(lstat, lse4, 0);
-      if constexpr (j == KS) load_stats(lstat, lse4, 1);
-      if constexpr (j == 2 * KS) load_stats(dstat, d4, 0);
-      if constexpr (j == 3 * KS) load_stats(dstat, d4, 1);
-      if constexpr (j >= KS + DL && j < 2 * KS + DL) exp_part(0, j - KS - DL);
-      if constexpr (j >= 2 * KS + DL && j < 3 * KS + DL) exp_part(1, j - 2 * KS - DL);
-      if constexpr (j == 3 * KS + DL) {
-        if (diag) causal_fixup();
-      }
-      if constexpr (j >= 3 * KS + DL && j < 4 * KS + DL) ds_part(0, j - 3 * KS - DL);
-      if constexpr (j >= 4 * KS + DL && j < 5 * KS + DL) ds_part(1, j - 4 * KS - DL);
+      if constexpr (j == exp_start(1) - 8) load_stats(lstat, lse4, 1);
+      if constexpr (j == ds_start(0) - 8) load_stats(dstat, d4, 0);
+      if constexpr (j == ds_start(1) - 8) load_stats(dstat, d4, 1);
+      static_for<0, 2>([&](auto MB) __attribute__((always_inline)) {
+        constexpr int mb = decltype(MB)::value;
+        constexpr int t = j - exp_start(mb);
+        if constexpr (t >= 0 && t < 2 * KS) {
+          constexpr int e0 = t * EXP_RATE, e1 = e0 + EXP_RATE;
+          exp_part(mb, e0, e1);
+          if constexpr (e1 % 8 == 0) {
+            if (diag) causal_fixup(mb, e1 / 8 - 1);
+          }
+        }
+        constexpr int u = j - ds_start(mb);
+        if constexpr (u >= 0 && u < KS) ds_part(mb, u * DS_RATE, (u + 1) * DS_RATE);
+      });
     };
     u32x4 ring[PF + 1];
     static_for<0, PF>([&](auto J) __attribute__((always_inline)) { ring[decltype(J)::value] = read_op(J); });
