@@ -41,14 +41,15 @@ def _bind(path: str):
     lib = ctypes.CDLL(path)
     i64, p, dbl, cint = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double, ctypes.c_int
     lib.oracle_forward.restype = cint
-    lib.oracle_forward.argtypes = [p, p, p, i64, i64, i64, i64, i64, cint, dbl, p, i64, p, p, cint]
+    lib.oracle_forward.argtypes = [p, p, p, i64, i64, i64, i64, i64, cint, i64, dbl, p, i64, p, p, cint]
     lib.oracle_row_stats.restype = cint
-    lib.oracle_row_stats.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, cint, dbl, p, p, p, cint]
+    lib.oracle_row_stats.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, cint, i64, dbl, p, p, p, cint]
     lib.oracle_backward_dq.restype = cint
-    lib.oracle_backward_dq.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, cint, dbl, p, p, i64, p, cint]
+    lib.oracle_backward_dq.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, cint, i64, dbl, p, p, i64, p,
+                                       cint]
     lib.oracle_backward_dkdv.restype = cint
-    lib.oracle_backward_dkdv.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, cint, dbl, p, p, p, p, i64,
-                                         p, p, cint]
+    lib.oracle_backward_dkdv.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, cint, i64, dbl, p, p, p, p,
+                                         i64, p, p, cint]
     return lib
 
 
@@ -91,10 +92,12 @@ class Oracle:
     def __init__(self, lib_path: str):
         self.lib = _bind(lib_path)
 
-    def forward(self, q, k, v, causal: bool, scale: float, rows=None, threads: int | None = None):
+    def forward(self, q, k, v, causal: bool, scale: float, rows=None, threads: int | None = None,
+                window: int = -1):
         """O [B,Hq,R,d] and LSE [B,Hq,R] (natural log) for query rows ``rows`` (all if None).
 
-        ``rows`` is [R] (same rows in every (b,hq) slice) or [B*Hq, R].
+        ``rows`` is [R] (same rows in every (b,hq) slice) or [B*Hq, R]. ``window`` >= 0 (with
+        ``causal``) restricts row i to keys i - window .. i.
         """
         q, k, v = _f64(q), _f64(k), _f64(v)
         B, Hq, Hkv, N, d = _shapes(q, k)
@@ -103,19 +106,20 @@ class Oracle:
         o = np.empty((B, Hq, R, d), dtype=np.float64)
         lse = np.empty((B, Hq, R), dtype=np.float64)
         rc = self.lib.oracle_forward(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, Hq, Hkv, N, d,
-                                    int(bool(causal)), float(scale), r.ctypes.data, R,
+                                    int(bool(causal)), int(window), float(scale), r.ctypes.data, R,
                                     o.ctypes.data, lse.ctypes.data, threads or default_threads())
         if rc:
             raise RuntimeError("oracle_forward failed (%d)" % rc)
         return o, lse
 
-    def row_stats(self, q, k, v, dO, causal: bool, scale: float, threads: int | None = None):
+    def row_stats(self, q, k, v, dO, causal: bool, scale: float, threads: int | None = None,
+                  window: int = -1):
         """(m, l, D), each [B,Hq,N]: row max, softmax denominator, and sum_j P_ij dP_ij."""
         q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
         B, Hq, Hkv, N, d = _shapes(q, k)
         m = np.empty((B, Hq, N)); l = np.empty((B, Hq, N)); D = np.empty((B, Hq, N))
         rc = self.lib.oracle_row_stats(q.ctypes.data, k.ctypes.data, v.ctypes.data, dO.ctypes.data,
-                                      B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
+                                      B, Hq, Hkv, N, d, int(bool(causal)), int(window), float(scale),
                                       m.ctypes.data, l.ctypes.data, D.ctypes.data,
                                       threads or default_threads())
         if rc:
@@ -123,7 +127,7 @@ class Oracle:
         return m, l, D
 
     def backward(self, q, k, v, dO, causal: bool, scale: float, qrows=None, krows=None,
-                 threads: int | None = None, stats=None):
+                 threads: int | None = None, stats=None, window: int = -1):
         """dQ [B,Hq,Rq,d] for query rows ``qrows``; dK, dV [B,Hkv,Rk,d] for key rows ``krows``.
 
         Row arguments take the same forms as in :func:`forward` (slices are (b,hq) for qrows and
@@ -133,7 +137,7 @@ class Oracle:
         B, Hq, Hkv, N, d = _shapes(q, k)
         nt = threads or default_threads()
         if stats is None:
-            stats = self.row_stats(q, k, v, dO, causal, scale, threads=nt)
+            stats = self.row_stats(q, k, v, dO, causal, scale, threads=nt, window=window)
         m, l, D = (np.ascontiguousarray(x, dtype=np.float64) for x in stats)
         rq = _rows(qrows, B * Hq, N)
         rk = _rows(krows, B * Hkv, N)
@@ -142,12 +146,13 @@ class Oracle:
         dv = np.empty((B, Hkv, rk.shape[1], d))
         lib = self.lib
         rc = lib.oracle_backward_dq(q.ctypes.data, k.ctypes.data, v.ctypes.data, dO.ctypes.data,
-                                    B, Hq, Hkv, N, d, int(bool(causal)), float(scale), D.ctypes.data,
+                                    B, Hq, Hkv, N, d, int(bool(causal)), int(window), float(scale),
+                                    D.ctypes.data,
                                     rq.ctypes.data, rq.shape[1], dq.ctypes.data, nt)
         if rc:
             raise RuntimeError("oracle_backward_dq failed (%d)" % rc)
         rc = lib.oracle_backward_dkdv(q.ctypes.data, k.ctypes.data, v.ctypes.data, dO.ctypes.data,
-                                      B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
+                                      B, Hq, Hkv, N, d, int(bool(causal)), int(window), float(scale),
                                       m.ctypes.data, l.ctypes.data, D.ctypes.data,
                                       rk.ctypes.data, rk.shape[1], dk.ctypes.data, dv.ctypes.data, nt)
         if rc:
@@ -167,18 +172,18 @@ def default() -> Oracle:
     return _default
 
 
-def forward(q, k, v, causal: bool, scale: float, rows=None, threads: int | None = None):
-    return default().forward(q, k, v, causal, scale, rows=rows, threads=threads)
+def forward(q, k, v, causal: bool, scale: float, rows=None, threads: int | None = None, window: int = -1):
+    return default().forward(q, k, v, causal, scale, rows=rows, threads=threads, window=window)
 
 
-def row_stats(q, k, v, dO, causal: bool, scale: float, threads: int | None = None):
-    return default().row_stats(q, k, v, dO, causal, scale, threads=threads)
+def row_stats(q, k, v, dO, causal: bool, scale: float, threads: int | None = None, window: int = -1):
+    return default().row_stats(q, k, v, dO, causal, scale, threads=threads, window=window)
 
 
 def backward(q, k, v, dO, causal: bool, scale: float, qrows=None, krows=None,
-             threads: int | None = None, stats=None):
+             threads: int | None = None, stats=None, window: int = -1):
     return default().backward(q, k, v, dO, causal, scale, qrows=qrows, krows=krows,
-                              threads=threads, stats=stats)
+                              threads=threads, stats=stats, window=window)
 
 
 def forward_flops(B: int, Hq: int, N: int, d: int, causal: bool, nrows: int | None = None) -> float:

@@ -18,6 +18,10 @@
  *   O_i   = sum_j p_ij v_j / l_i,           LSE_i = m_i + ln l_i     (natural log)
  *
  * Visible keys: all j when not causal; j <= i when causal (square Q/K, top-left aligned).
+ * Sliding window W >= 0 (causal only): j is visible to i iff i - W <= j <= i, the local
+ * attention of the sliding-window models that "Flash Attention 2: attivarla (llama.cpp,
+ * Ollama, vLLM)" names in its section on the cases where the method does not help; the page
+ * gives no formula, so the window is read as W keys before the query plus the query itself.
  * Grouped-query heads: query head hq reads key/value head hq / (Hq / Hkv).
  *
  * Backward (textbook chain rule of L = sum O . dO, the "recomputation" section of the
@@ -45,6 +49,7 @@ typedef struct {
   const double *q, *k, *v, *dO;
   int64_t B, Hq, Hkv, N, d;
   int causal;
+  int64_t window; /* < 0: no window */
   double scale;
   const int32_t* rows; /* query rows (forward, dq) or key rows (dkdv), per slice */
   int64_t nrows;
@@ -64,25 +69,34 @@ static double dot(const double* a, const double* b, int64_t d) {
   return s;
 }
 
+/* Visible keys of query row i are first_key(i) <= j < visible_keys(i). */
 static int64_t visible_keys(const job_t* J, int64_t i) { return J->causal ? i + 1 : J->N; }
+static int64_t first_key(const job_t* J, int64_t i) {
+  return (J->window >= 0 && i > J->window) ? i - J->window : 0;
+}
+/* Query rows that see key j are first_query(j) <= i < last_query(j). */
+static int64_t last_query(const job_t* J, int64_t j) {
+  return (J->window >= 0 && j + J->window + 1 < J->N) ? j + J->window + 1 : J->N;
+}
 
 /* Scores, stable softmax numerators and row statistics of query row i.
-   On return s[j] = p_ij = exp(s_ij - m) for j < nvis; *m_out, *l_out set. */
+   On return s[j] = p_ij = exp(s_ij - m) for *j0_out <= j < nvis; *m_out, *l_out set. */
 static int64_t softmax_row(const job_t* J, const double* qi, const double* Kh, int64_t i,
-                           double* s, double* m_out, double* l_out) {
-  int64_t nvis = visible_keys(J, i);
+                           double* s, double* m_out, double* l_out, int64_t* j0_out) {
+  int64_t nvis = visible_keys(J, i), j0 = first_key(J, i);
   double m = -INFINITY;
-  for (int64_t j = 0; j < nvis; ++j) {
+  for (int64_t j = j0; j < nvis; ++j) {
     s[j] = J->scale * dot(qi, Kh + j * J->d, J->d);
     if (s[j] > m) m = s[j];
   }
   double l = 0.0;
-  for (int64_t j = 0; j < nvis; ++j) {
+  for (int64_t j = j0; j < nvis; ++j) {
     s[j] = exp(s[j] - m);
     l += s[j];
   }
   *m_out = m;
   *l_out = l;
+  *j0_out = j0;
   return nvis;
 }
 
@@ -96,10 +110,11 @@ static void do_item(job_t* J, int64_t item, double* s, double* acc) {
     const double* Kh = J->k + (b * J->Hkv + g) * N * d;
     const double* Vh = J->v + (b * J->Hkv + g) * N * d;
     double m, l;
-    int64_t nvis = softmax_row(J, qi, Kh, i, s, &m, &l);
+    int64_t j0;
+    int64_t nvis = softmax_row(J, qi, Kh, i, s, &m, &l, &j0);
     if (J->kind == K_FWD) {
       for (int64_t c = 0; c < d; ++c) acc[c] = 0.0;
-      for (int64_t j = 0; j < nvis; ++j)
+      for (int64_t j = j0; j < nvis; ++j)
         for (int64_t c = 0; c < d; ++c) acc[c] += s[j] * Vh[j * d + c];
       double* o = J->out0 + (slice * J->nrows + r) * d;
       for (int64_t c = 0; c < d; ++c) o[c] = acc[c] / l;
@@ -108,7 +123,7 @@ static void do_item(job_t* J, int64_t item, double* s, double* acc) {
       const double* dOi = J->dO + (slice * N + i) * d;
       double Di = J->D[slice * N + i];
       for (int64_t c = 0; c < d; ++c) acc[c] = 0.0;
-      for (int64_t j = 0; j < nvis; ++j) {
+      for (int64_t j = j0; j < nvis; ++j) {
         double P = s[j] / l;
         double dP = dot(dOi, Vh + j * d, d);
         double dS = P * (dP - Di);
@@ -125,9 +140,10 @@ static void do_item(job_t* J, int64_t item, double* s, double* acc) {
     const double* Kh = J->k + (b * J->Hkv + g) * N * d;
     const double* Vh = J->v + (b * J->Hkv + g) * N * d;
     double m, l;
-    int64_t nvis = softmax_row(J, qi, Kh, i, s, &m, &l);
+    int64_t j0;
+    int64_t nvis = softmax_row(J, qi, Kh, i, s, &m, &l, &j0);
     double D = 0.0;
-    for (int64_t j = 0; j < nvis; ++j) D += (s[j] / l) * dot(dOi, Vh + j * d, d);
+    for (int64_t j = j0; j < nvis; ++j) D += (s[j] / l) * dot(dOi, Vh + j * d, d);
     J->out0[item] = m;
     J->out1[item] = l;
     J->out2[item] = D;
@@ -143,7 +159,8 @@ static void do_item(job_t* J, int64_t item, double* s, double* acc) {
     for (int64_t hq = g * group; hq < (g + 1) * group; ++hq) {
       int64_t slice = b * J->Hq + hq;
       int64_t i0 = J->causal ? j : 0; /* query rows that see key j */
-      for (int64_t i = i0; i < N; ++i) {
+      int64_t i1 = last_query(J, j);
+      for (int64_t i = i0; i < i1; ++i) {
         const double* qi = J->q + (slice * N + i) * d;
         const double* dOi = J->dO + (slice * N + i) * d;
         double sij = J->scale * dot(qi, kj, d);
@@ -201,8 +218,10 @@ static int run(job_t* J, int nthreads) {
   return J->error ? -2 : 0;
 }
 
-static int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d) {
+static int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal,
+                       int64_t window) {
   if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || d < 1) return -1;
+  if (window >= 0 && !causal) return -1; /* a window is defined for causal attention only */
   if (Hq % Hkv != 0) return -1;
   return 0;
 }
@@ -216,13 +235,13 @@ static int check_rows(const int32_t* rows, int64_t nslices, int64_t nrows, int64
 
 /* O [B,Hq,nrows,d] and LSE [B,Hq,nrows] for query rows rows[(b*Hq+hq)*nrows + r]. */
 int oracle_forward(const double* q, const double* k, const double* v, int64_t B, int64_t Hq,
-                   int64_t Hkv, int64_t N, int64_t d, int causal, double scale,
-                   const int32_t* rows, int64_t nrows, double* o, double* lse, int nthreads) {
-  if (check_shape(B, Hq, Hkv, N, d) || check_rows(rows, B * Hq, nrows, N)) return -1;
+                   int64_t Hkv, int64_t N, int64_t d, int causal, int64_t window,
+                   double scale, const int32_t* rows, int64_t nrows, double* o, double* lse, int nthreads) {
+  if (check_shape(B, Hq, Hkv, N, d, causal, window) || check_rows(rows, B * Hq, nrows, N)) return -1;
   job_t J;
   memset(&J, 0, sizeof J);
   J.q = q; J.k = k; J.v = v; J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.N = N; J.d = d;
-  J.causal = causal != 0; J.scale = scale; J.rows = rows; J.nrows = nrows;
+  J.causal = causal != 0; J.window = window < 0 ? -1 : window; J.scale = scale; J.rows = rows; J.nrows = nrows;
   J.out0 = o; J.out1 = lse; J.nitems = B * Hq * nrows; J.kind = K_FWD;
   return run(&J, nthreads);
 }
@@ -230,12 +249,12 @@ int oracle_forward(const double* q, const double* k, const double* v, int64_t B,
 /* Per-row statistics of every query row: m, l [B,Hq,N] and D = sum_j P_ij dP_ij [B,Hq,N]. */
 int oracle_row_stats(const double* q, const double* k, const double* v, const double* dO,
                      int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal,
-                     double scale, double* m, double* l, double* D, int nthreads) {
-  if (check_shape(B, Hq, Hkv, N, d)) return -1;
+                     int64_t window, double scale, double* m, double* l, double* D, int nthreads) {
+  if (check_shape(B, Hq, Hkv, N, d, causal, window)) return -1;
   job_t J;
   memset(&J, 0, sizeof J);
   J.q = q; J.k = k; J.v = v; J.dO = dO; J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.N = N; J.d = d;
-  J.causal = causal != 0; J.scale = scale;
+  J.causal = causal != 0; J.window = window < 0 ? -1 : window; J.scale = scale;
   J.out0 = m; J.out1 = l; J.out2 = D; J.nitems = B * Hq * N; J.kind = K_STATS;
   return run(&J, nthreads);
 }
@@ -243,13 +262,13 @@ int oracle_row_stats(const double* q, const double* k, const double* v, const do
 /* dQ [B,Hq,nrows,d] for query rows rows[(b*Hq+hq)*nrows + r]; needs D from oracle_row_stats. */
 int oracle_backward_dq(const double* q, const double* k, const double* v, const double* dO,
                        int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal,
-                       double scale, const double* D, const int32_t* rows, int64_t nrows,
+                       int64_t window, double scale, const double* D, const int32_t* rows, int64_t nrows,
                        double* dq, int nthreads) {
-  if (check_shape(B, Hq, Hkv, N, d) || check_rows(rows, B * Hq, nrows, N)) return -1;
+  if (check_shape(B, Hq, Hkv, N, d, causal, window) || check_rows(rows, B * Hq, nrows, N)) return -1;
   job_t J;
   memset(&J, 0, sizeof J);
   J.q = q; J.k = k; J.v = v; J.dO = dO; J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.N = N; J.d = d;
-  J.causal = causal != 0; J.scale = scale; J.D = D; J.rows = rows; J.nrows = nrows;
+  J.causal = causal != 0; J.window = window < 0 ? -1 : window; J.scale = scale; J.D = D; J.rows = rows; J.nrows = nrows;
   J.out0 = dq; J.nitems = B * Hq * nrows; J.kind = K_DQ;
   return run(&J, nthreads);
 }
@@ -257,14 +276,14 @@ int oracle_backward_dq(const double* q, const double* k, const double* v, const 
 /* dK, dV [B,Hkv,nrows,d] for key rows rows[(b*Hkv+g)*nrows + r]; needs m, l, D of all rows. */
 int oracle_backward_dkdv(const double* q, const double* k, const double* v, const double* dO,
                          int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal,
-                         double scale, const double* m, const double* l, const double* D,
+                         int64_t window, double scale, const double* m, const double* l, const double* D,
                          const int32_t* rows, int64_t nrows, double* dk, double* dv,
                          int nthreads) {
-  if (check_shape(B, Hq, Hkv, N, d) || check_rows(rows, B * Hkv, nrows, N)) return -1;
+  if (check_shape(B, Hq, Hkv, N, d, causal, window) || check_rows(rows, B * Hkv, nrows, N)) return -1;
   job_t J;
   memset(&J, 0, sizeof J);
   J.q = q; J.k = k; J.v = v; J.dO = dO; J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.N = N; J.d = d;
-  J.causal = causal != 0; J.scale = scale; J.m = m; J.l = l; J.D = D;
+  J.causal = causal != 0; J.window = window < 0 ? -1 : window; J.scale = scale; J.m = m; J.l = l; J.D = D;
   J.rows = rows; J.nrows = nrows;
   J.out0 = dk; J.out1 = dv; J.nitems = B * Hkv * nrows; J.kind = K_DKDV;
   return run(&J, nthreads);

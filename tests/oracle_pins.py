@@ -309,9 +309,88 @@ def pin_gqa_equals_expanded(orc):
         _close(dv1, dv2.reshape(B, Hkv, G, N, d).sum(axis=2), 1e-13, "gqa dV")
 
 
+# ------------------------------------------------------------------- sliding-window pins
+
+def _band_mask(N, window):
+    """True where key j is visible to query i: i - window <= j <= i."""
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    return (j <= i) & (j >= i - window)
+
+
+def pin_window_zero_and_one(orc):
+    """Window 0: row i sees only key i (O_i = V_i, LSE_i = s_ii). Window 1: two keys, the
+    logistic closed form O_i = w V_{i-1} + (1 - w) V_i with w = 1 / (1 + e^(s_ii - s_i,i-1))."""
+    rng = _rng(15)
+    B, Hq, Hkv, N, d = 1, 4, 2, 11, 6
+    q, k, v = (rng.standard_normal(s) for s in ((B, Hq, N, d), (B, Hkv, N, d), (B, Hkv, N, d)))
+    sc = 0.45
+    G = Hq // Hkv
+    o0, l0 = orc.forward(q, k, v, True, sc, window=0)
+    o1, l1 = orc.forward(q, k, v, True, sc, window=1)
+    for hq in range(Hq):
+        g = hq // G
+        for i in range(N):
+            sii = sc * float(q[0, hq, i] @ k[0, g, i])
+            _close(o0[0, hq, i], v[0, g, i], 1e-12, "window-0 O")
+            _close(l0[0, hq, i], sii, 1e-12, "window-0 LSE")
+            if i == 0:
+                _close(o1[0, hq, 0], v[0, g, 0], 1e-12, "window-1 row 0")
+                continue
+            sprev = sc * float(q[0, hq, i] @ k[0, g, i - 1])
+            w = 1.0 / (1.0 + math.exp(sii - sprev))
+            _close(o1[0, hq, i], w * v[0, g, i - 1] + (1 - w) * v[0, g, i], 1e-12, "window-1 O")
+            _close(l1[0, hq, i], math.log(math.exp(sii) + math.exp(sprev)), 1e-12, "window-1 LSE")
+
+
+def pin_window_torch(orc):
+    """Forward and backward with a window agree with torch fp64 attention and autograd under an
+    explicit band mask; a window of N - 1 or more is plain causal attention."""
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(16)
+    for (B, Hq, Hkv, N, d, W) in [(1, 4, 2, 23, 8, 5), (2, 2, 1, 17, 4, 3), (1, 2, 2, 9, 16, 8),
+                                  (1, 2, 2, 12, 4, 40)]:
+        q, k, v, dO = (rng.standard_normal(s) for s in ((B, Hq, N, d), (B, Hkv, N, d), (B, Hkv, N, d), (B, Hq, N, d)))
+        sc = 0.3
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        mask = torch.from_numpy(_band_mask(N, W))
+        ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=sc, enable_gqa=(Hq != Hkv))
+        (ref * torch.from_numpy(dO)).sum().backward()
+        o, lse = orc.forward(q, k, v, True, sc, window=W)
+        _close(o, ref.detach().numpy(), 1e-12, "window sdpa O")
+        kk = tk.detach().repeat_interleave(Hq // Hkv, dim=1)
+        s = torch.matmul(tq.detach(), kk.transpose(-1, -2).contiguous()) * sc
+        s = s.masked_fill(~mask, float("-inf"))
+        _close(lse, torch.logsumexp(s, dim=-1).numpy(), 1e-12, "window LSE")
+        dq, dk, dv, _ = orc.backward(q, k, v, dO, True, sc, window=W)
+        _close(dq, tq.grad.numpy(), 1e-12, "window autograd dQ")
+        _close(dk, tk.grad.numpy(), 1e-12, "window autograd dK")
+        _close(dv, tv.grad.numpy(), 1e-12, "window autograd dV")
+        if W >= N - 1:
+            oc, lc = orc.forward(q, k, v, True, sc)
+            assert np.array_equal(o, oc) and np.array_equal(lse, lc), "wide window != causal"
+
+
+def pin_window_locality(orc):
+    """Keys and values more than W positions before a query do not affect its output."""
+    rng = _rng(17)
+    B, Hq, Hkv, N, d, W = 1, 2, 1, 20, 5, 4
+    q, k, v = (rng.standard_normal(s) for s in ((B, Hq, N, d), (B, Hkv, N, d), (B, Hkv, N, d)))
+    o, lse = orc.forward(q, k, v, True, 0.6, window=W)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, :6] = rng.standard_normal((B, Hkv, 6, d)) * 5
+    v2[:, :, :6] = rng.standard_normal((B, Hkv, 6, d)) * 5
+    o2, lse2 = orc.forward(q, k2, v2, True, 0.6, window=W)
+    rows = np.arange(6 + W, N)  # rows whose window starts at key 6 or later
+    assert np.array_equal(o[:, :, rows], o2[:, :, rows]) and np.array_equal(lse[:, :, rows], lse2[:, :, rows])
+    assert not np.allclose(o[:, :, 6 + W - 1], o2[:, :, 6 + W - 1]), "row 5 + W must see key 5"
+
+
 FORWARD_PINS = [pin_constant_scores, pin_causal_first_row, pin_single_key, pin_two_keys_logistic,
                 pin_dominant_score, pin_joint_permutation, pin_key_shift, pin_value_affine,
                 pin_torch_sdpa]
 BACKWARD_PINS = [pin_backward_invariants, pin_torch_autograd, pin_gqa_equals_expanded]
 BOTH_PINS = [pin_hand_worked, pin_sampled_rows_match_full, pin_finite_differences]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS + BOTH_PINS
+WINDOW_PINS = [pin_window_zero_and_one, pin_window_torch, pin_window_locality]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + BOTH_PINS + WINDOW_PINS

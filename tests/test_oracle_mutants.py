@@ -38,6 +38,12 @@ MUTATIONS = [
      "for (int64_t hq = g * group; hq < g * group + 1; ++hq) {"),
     ("P without the row max", "double P = exp(sij - J->m[slice * N + i]) / J->l[slice * N + i];",
      "double P = exp(sij) / J->l[slice * N + i];"),
+    ("window start one key late", "return (J->window >= 0 && i > J->window) ? i - J->window : 0;",
+     "return (J->window >= 0 && i >= J->window) ? i - J->window + 1 : 0;"),
+    ("window start one key early", "return (J->window >= 0 && i > J->window) ? i - J->window : 0;",
+     "return (J->window >= 0 && i > J->window + 1) ? i - J->window - 1 : 0;"),
+    ("window ignored by dK/dV", "int64_t i1 = last_query(J, j);", "int64_t i1 = N;"),
+    ("dK/dV window end one row short", "? j + J->window + 1 : J->N;", "? j + J->window : J->N;"),
 ]
 
 
