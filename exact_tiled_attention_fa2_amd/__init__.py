@@ -20,10 +20,11 @@ FA2_OK = 0
 STATUS_NAMES = {
     0: "FA2_OK", 1: "FA2_ERR_NULL_POINTER", 2: "FA2_ERR_BAD_SHAPE", 3: "FA2_ERR_UNSUPPORTED_HEAD_DIM",
     4: "FA2_ERR_BAD_GQA", 5: "FA2_ERR_BAD_SCALE", 6: "FA2_ERR_MISALIGNED", 7: "FA2_ERR_ALIASING",
-    8: "FA2_ERR_WORKSPACE", 9: "FA2_ERR_HIP",
+    8: "FA2_ERR_WORKSPACE", 9: "FA2_ERR_HIP", 10: "FA2_ERR_BAD_WINDOW",
 }
 EXPORTED = ("fa2_forward", "fa2_backward", "fa2_backward_workspace_size", "fa2_backward_preprocess",
-            "fa2_backward_dkdv", "fa2_backward_dq", "fa2_status_string")
+            "fa2_backward_dkdv", "fa2_backward_dq", "fa2_forward_window", "fa2_backward_window",
+            "fa2_status_string")
 
 _lib = None
 
@@ -56,6 +57,10 @@ def load() -> ctypes.CDLL:
     lib.fa2_backward_dkdv.argtypes = [p, p, p, p, p, z, p, p, i, i, i, i, i, i, f, p]
     lib.fa2_backward_dq.restype = i
     lib.fa2_backward_dq.argtypes = [p, p, p, p, p, z, p, i, i, i, i, i, i, f, p]
+    lib.fa2_forward_window.restype = i
+    lib.fa2_forward_window.argtypes = [p, p, p, p, p, i, i, i, i, i, i, f, p]
+    lib.fa2_backward_window.restype = i
+    lib.fa2_backward_window.argtypes = [p, p, p, p, p, p, p, p, p, i, i, i, i, i, i, f, p, z, p]
     lib.fa2_status_string.restype = ctypes.c_char_p
     lib.fa2_status_string.argtypes = [i]
     _lib = lib
@@ -115,6 +120,18 @@ def fa2_backward_dq(q, k, v, dO, workspace, workspace_bytes, dq, B, Hq, Hkv, N, 
                                   _stream(stream))
 
 
+def fa2_forward_window(q, k, v, o, lse, B, Hq, Hkv, N, d, window, scale, stream=None) -> int:
+    return load().fa2_forward_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
+                                     int(window), float(scale), _stream(stream))
+
+
+def fa2_backward_window(q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, N, d, window, scale,
+                        workspace, workspace_bytes, stream=None) -> int:
+    return load().fa2_backward_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
+                                      _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d, int(window), float(scale),
+                                      _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
 def fa2_status_string(status: int) -> str:
     return load().fa2_status_string(int(status)).decode()
 
@@ -127,20 +144,28 @@ def _dims(q, k):
     return B, Hq, Hkv, N, d
 
 
-def forward(q, k, v, causal: bool, scale: float, stream=None):
-    """O (fp32) and LSE (fp32) for bf16 device tensors q [B,Hq,N,d], k/v [B,Hkv,N,d]."""
+def forward(q, k, v, causal: bool, scale: float, stream=None, window: int | None = None):
+    """O (fp32) and LSE (fp32) for bf16 device tensors q [B,Hq,N,d], k/v [B,Hkv,N,d].
+
+    ``window`` (with ``causal``): query i sees keys i - window .. i (fa2_forward_window)."""
     import torch
     B, Hq, Hkv, N, d = _dims(q, k)
     o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    st = fa2_forward(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream)
+    if window is None:
+        st = fa2_forward(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream)
+    else:
+        if not causal:
+            raise ValueError("a sliding window is defined for causal attention only")
+        st = fa2_forward_window(q, k, v, o, lse, B, Hq, Hkv, N, d, window, scale, stream)
     if st != FA2_OK:
-        raise Fa2Error(st, "fa2_forward")
+        raise Fa2Error(st, "fa2_forward" if window is None else "fa2_forward_window")
     return o, lse
 
 
-def backward(q, k, v, o, lse, dO, causal: bool, scale: float, stream=None, workspace=None):
-    """dQ, dK, dV (fp32) of sum(O * dO) for the outputs of :func:`forward`."""
+def backward(q, k, v, o, lse, dO, causal: bool, scale: float, stream=None, workspace=None,
+             window: int | None = None):
+    """dQ, dK, dV (fp32) of sum(O * dO) for the outputs of :func:`forward` (same ``window``)."""
     import torch
     B, Hq, Hkv, N, d = _dims(q, k)
     dq = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
@@ -149,8 +174,15 @@ def backward(q, k, v, o, lse, dO, causal: bool, scale: float, stream=None, works
     need = fa2_backward_workspace_size(B, Hq, N)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    st = fa2_backward(q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale,
-                      workspace, workspace.numel() * workspace.element_size(), stream)
+    wbytes = workspace.numel() * workspace.element_size()
+    if window is None:
+        st = fa2_backward(q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale,
+                          workspace, wbytes, stream)
+    else:
+        if not causal:
+            raise ValueError("a sliding window is defined for causal attention only")
+        st = fa2_backward_window(q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, N, d, window, scale,
+                                 workspace, wbytes, stream)
     if st != FA2_OK:
-        raise Fa2Error(st, "fa2_backward")
+        raise Fa2Error(st, "fa2_backward" if window is None else "fa2_backward_window")
     return dq, dk, dv

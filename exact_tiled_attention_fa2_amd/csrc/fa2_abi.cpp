@@ -87,12 +87,17 @@ const char* fa2_status_string(int status) {
     case FA2_ERR_ALIASING: return "FA2_ERR_ALIASING";
     case FA2_ERR_WORKSPACE: return "FA2_ERR_WORKSPACE";
     case FA2_ERR_HIP: return "FA2_ERR_HIP";
+    case FA2_ERR_BAD_WINDOW: return "FA2_ERR_BAD_WINDOW";
     default: return "FA2_UNKNOWN";
   }
 }
 
-int fa2_forward(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Hq,
-                int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int forward_impl(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Hq,
+                 int Hkv, int N, int d, int causal, int window, float scale, hipStream_t stream) {
   bool empty = false;
   int st = check_shape(B, Hq, Hkv, N, d, scale, &empty);
   if (st != FA2_OK || empty) return st;
@@ -101,8 +106,23 @@ int fa2_forward(const void* q, const void* k, const void* v, float* o, float* ls
   const Buf out[2] = {{o, rq * d * 4}, {lse, rq * 4}};
   st = check_buffers(in, 3, out, 2);
   if (st != FA2_OK) return st;
-  fa2::AttnShape s{B, Hq, Hkv, N, d, causal != 0, scale};
+  fa2::AttnShape s{B, Hq, Hkv, N, d, causal != 0, scale, window};
   return hip_status(fa2::launch_forward(q, k, v, o, lse, s, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa2_forward(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Hq,
+                int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
+  return forward_impl(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, -1, scale, stream);
+}
+
+int fa2_forward_window(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                       int Hq, int Hkv, int N, int d, int window, float scale, hipStream_t stream) {
+  if (window < 0) return FA2_ERR_BAD_WINDOW;
+  return forward_impl(q, k, v, o, lse, B, Hq, Hkv, N, d, 1, window, scale, stream);
 }
 
 size_t fa2_backward_workspace_size(int B, int Hq, int N) {
@@ -121,10 +141,14 @@ int check_workspace(const void* ws, size_t ws_bytes, int B, int Hq, int N) {
 
 }  // namespace
 
-int fa2_backward(const void* q, const void* k, const void* v, const float* o, const float* lse,
-                 const void* dO, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int N,
-                 int d, int causal, float scale, void* workspace, size_t workspace_bytes,
-                 hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int backward_impl(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                  const void* dO, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int N,
+                  int d, int causal, int window, float scale, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
   bool empty = false;
   int st = check_shape(B, Hq, Hkv, N, d, scale, &empty);
   if (st != FA2_OK || empty) return st;
@@ -140,12 +164,33 @@ int fa2_backward(const void* q, const void* k, const void* v, const float* o, co
   const Buf ws[1] = {{workspace, fa2_backward_workspace_size(B, Hq, N)}};
   st = check_buffers(all_in, 9, ws, 1);
   if (st != FA2_OK) return st;
-  fa2::AttnShape s{B, Hq, Hkv, N, d, causal != 0, scale};
+  fa2::AttnShape s{B, Hq, Hkv, N, d, causal != 0, scale, window};
   float* w = static_cast<float*>(workspace);
   hipError_t e = fa2::launch_bwd_preprocess(o, dO, lse, w, s, stream);
   if (e == hipSuccess) e = fa2::launch_bwd_dkdv(q, k, v, dO, w, dk, dv, s, stream);
   if (e == hipSuccess) e = fa2::launch_bwd_dq(q, k, v, dO, w, dq, s, stream);
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa2_backward(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                 const void* dO, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int N,
+                 int d, int causal, float scale, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, N, d, causal, -1, scale,
+                       workspace, workspace_bytes, stream);
+}
+
+int fa2_backward_window(const void* q, const void* k, const void* v, const float* o,
+                        const float* lse, const void* dO, float* dq, float* dk, float* dv, int B,
+                        int Hq, int Hkv, int N, int d, int window, float scale, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  if (window < 0) return FA2_ERR_BAD_WINDOW;
+  return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, N, d, 1, window, scale,
+                       workspace, workspace_bytes, stream);
 }
 
 int fa2_backward_preprocess(const float* o, const void* dO, const float* lse, void* workspace,

@@ -40,6 +40,7 @@ struct BwdParams {
   float scale;    // signed scale, applied to dQ and dK
   unsigned kneg;  // sign flip applied to the register-resident score operand when scale < 0
   int nblk;       // key blocks (dK/dV) or query blocks (dQ) per head
+  int window;     // causal window: query i sees keys i - window .. i (>= N: no window)
 };
 
 template <int D>
@@ -198,14 +199,17 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
   const uint32_t head_bytes = (uint32_t)N * C::ROWB;
   const size_t kvoff = ((size_t)b * p.Hkv + g) * (size_t)N * D;
 
-  // Query tiles: every query head of the group, tiles from the one holding key k0 to the end,
-  // walked from the LAST tile down, so all key blocks of a head start on the same tiles and
-  // read them at about the same time (shared through L2 instead of each block from HBM).
+  // Query tiles: every query head of the group, tiles from the one holding key k0 up to the
+  // last one that sees a key of the block (the end, unless a window stops earlier), walked
+  // from the TOP tile down, so all key blocks of a head start on the same tiles and read them
+  // at about the same time (shared through L2 instead of each block from HBM).
+  const int W = p.window;
   const int nqt_all = (N + C::BT - 1) / C::BT;
   const int qt0 = p.causal ? k0 / C::BT : 0;
-  const int nqt = nqt_all - qt0;
+  const int qt_top = min(nqt_all - 1, (k0 + C::BR - 1 + W) / C::BT);
+  const int nqt = qt_top - qt0 + 1;
   const int iters = G * nqt;
-  auto tile_row0 = [&](int it) { return (nqt_all - 1 - it % nqt) * C::BT; };
+  auto tile_row0 = [&](int it) { return (qt_top - it % nqt) * C::BT; };
 
   auto stage = [&](int s) {
     return s ? DkdvStage<D>{(lds_char*)q_st1, (lds_char*)do_st1, (lds_char*)stat_st1}
@@ -264,24 +268,26 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
   // One query tile for this wave, as one unrolled sequence of NS MFMA steps:
   //   S (Q K^T, row blocks mb = 0, 1) | dP (dO V^T) | dV^T += dO^T P | dK^T += Q^T dS.
   // Each step issues the LDS read of the operand PF steps ahead, one MFMA, and a slice of
-  // VALU work whose inputs are complete by then. The VALU work is spread at an even rate so
-  // that every step's share fits beside its MFMA: P = 2^(S c - lse2) of row block 0 from
-  // step KS + DL on (one element per step at d = 128), then P of block 1, then dS = P (dP - D)
-  // of blocks 0 and 1 (one pair per step); each packed operand is complete before the first
-  // MFMA that reads it. Scheduling fences keep the order.
+  // VALU work whose inputs are complete by then: P = 2^(S c - lse2) of row block 0 while the
+  // S MFMAs of block 1 run, P of block 1 during dP of block 0, and dS = P (dP - D) of blocks
+  // 0 and 1 during dP of block 1 and the first dV steps; each packed operand is complete
+  // before the first MFMA that reads it. (Spreading the same work evenly over the tile
+  // measured slower: finishing the exponentials early lets dS and the dV/dK MFMAs follow
+  // sooner.) Scheduling fences keep the order.
   // Rows past the end of the sequence need no mask: their Q, dO, D and LSE read as zero, so
   // P = 1 there but dO = 0 and dS = 1 * (0 - 0) = 0, and they add nothing to dV or dK.
-  // A tile crossing the wave's causal diagonal (diag) has P zeroed above the diagonal, eight
-  // rows at a time, in the step that completes those rows' exponentials.
+  // A tile crossing the wave's causal diagonal or the end of its keys' window (fix) has P
+  // zeroed outside key <= query <= key + window, eight rows at a time, in the step that
+  // completes those rows' exponentials.
   constexpr int KS = C::KS, DB = C::DB;
   constexpr int NS = 4 * KS + 8 * DB;  // MFMA steps per tile
   constexpr int PF = 3;                // operand reads in flight ahead of the MFMA using them
   constexpr int DL = 2;                // steps between an accumulator's last MFMA and its use
-  constexpr int EXP_RATE = 8 / KS;     // P elements per step
+  constexpr int EXP_RATE = 16 / KS;    // P elements per step
   constexpr int DS_RATE = 8 / KS;      // dS element pairs per step
-  auto exp_start = [](int mb) { return KS + DL + 2 * KS * mb; };  // 2 KS steps per row block
-  auto ds_start = [](int mb) { return 5 * KS + DL + KS * mb; };   // KS steps per row block
-  auto tile = [&](const DkdvStage<D>& st, int qrow0, bool diag) __attribute__((always_inline)) {
+  auto exp_start = [](int mb) { return KS + DL + KS * mb; };      // KS steps per row block
+  auto ds_start = [](int mb) { return 3 * KS + DL + KS * mb; };   // KS steps per row block
+  auto tile = [&](const DkdvStage<D>& st, int qrow0, bool fix) __attribute__((always_inline)) {
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -297,16 +303,17 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) dst[mb][rq] = *(const FA2_LDS f32x4*)(base + 32 * mb + 8 * rq + 4 * hf);
     };
-    // Registers hold query rows 32 mb + 8 (r / 4) + 4 hf + r % 4 of row block mb; the row is
-    // visible to this lane's key iff 32 mb + 8 (r / 4) + r % 4 >= key - qrow0 - 4 hf.
+    // Registers hold query rows 32 mb + 8 (r / 4) + 4 hf + r % 4 of row block mb; the row sees
+    // this lane's key iff lo <= 32 mb + 8 (r / 4) + r % 4 <= lo + window, lo = key - qrow0 - 4 hf.
     auto causal_fixup = [&](int mb, int h) __attribute__((always_inline)) {
       const int lo = key - qrow0 - 4 * hf;
+      const int hi = lo + W;
 #pragma unroll
       for (int r = 8 * h; r < 8 * h + 8; r += 2) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int x = 32 * mb + 8 * ((r + u) >> 2) + ((r + u) & 3);
-          pf[mb][r + u] = x >= lo ? pf[mb][r + u] : 0.f;
+          pf[mb][r + u] = (x >= lo && x <= hi) ? pf[mb][r + u] : 0.f;
         }
         pp[mb][h][(r >> 1) & 3] = pack_bf16(pf[mb][r], pf[mb][r + 1]);
       }
@@ -366,11 +373,11 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
       static_for<0, 2>([&](auto MB) __attribute__((always_inline)) {
         constexpr int mb = decltype(MB)::value;
         constexpr int t = j - exp_start(mb);
-        if constexpr (t >= 0 && t < 2 * KS) {
+        if constexpr (t >= 0 && t < KS) {
           constexpr int e0 = t * EXP_RATE, e1 = e0 + EXP_RATE;
           exp_part(mb, e0, e1);
           if constexpr (e1 % 8 == 0) {
-            if (diag) causal_fixup(mb, e1 / 8 - 1);
+            if (fix) causal_fixup(mb, e1 / 8 - 1);
           }
         }
         constexpr int u = j - ds_start(mb);
@@ -397,8 +404,10 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
     fetch(it + 1);
     const DkdvStage<D> st = stage(PAR);
     const int qrow0 = tile_row0(it);
-    // Causal: skip tiles wholly above this wave's keys; fix up tiles crossing its diagonal.
-    if (!(p.causal && qrow0 + C::BT - 1 < kw)) tile(st, qrow0, p.causal && qrow0 < kw + C::RPW - 1);
+    // Causal: skip tiles wholly above this wave's keys or past their window; fix up tiles
+    // crossing the diagonal or the window's end.
+    const bool skip = (p.causal && qrow0 + C::BT - 1 < kw) || qrow0 > kw + C::RPW - 1 + W;
+    if (!skip) tile(st, qrow0, (p.causal && qrow0 < kw + C::RPW - 1) || qrow0 + C::BT - 1 > kw + W);
     sync_stage();
   };
 
@@ -474,11 +483,16 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + kvoff, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + kvoff, head_bytes);
 
-  // Key tiles of the workgroup (causal: up to its last row); halves u = 0 .. 2 ntiles - 1.
+  // Key tiles of the workgroup, numbered from its first visible tile tbase (a window hides
+  // the keys before q0 - window) up to its last row (causal); halves u = 0 .. 2 ntiles - 1.
+  const int W = p.window;
+  const int tbase = q0 > W ? (q0 - W) / Q::BT : 0;
   const int qend = min(q0 + Q::BR, N);
-  const int ntiles = p.causal ? (qend + Q::BT - 1) / Q::BT : (N + Q::BT - 1) / Q::BT;
+  const int ntiles = (p.causal ? (qend + Q::BT - 1) / Q::BT : (N + Q::BT - 1) / Q::BT) - tbase;
   // Last half this wave computes (causal: the one holding its last row); -1 if it has no rows.
-  const int my_last = qw >= N ? -1 : (p.causal ? min(2 * ntiles - 1, (qw + Q::RPW - 1) / 32) : 2 * ntiles - 1);
+  const int my_last = qw >= N ? -1
+                              : (p.causal ? min(2 * ntiles - 1, (qw + Q::RPW - 1) / 32 - 2 * tbase)
+                                          : 2 * ntiles - 1);
 
   auto kst = [&](auto S) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::value;
@@ -492,8 +506,8 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   // the end read as zero).
   auto fetch = [&](auto S, int t) __attribute__((always_inline)) {
     if (t > ntiles) return;
-    load_tile_dual<D>(rk, kst(S), t * Q::BT, wave, lane);
-    load_tile_dual<D>(rv, vst(S), t * Q::BT, wave, lane);
+    load_tile_dual<D>(rk, kst(S), (tbase + t) * Q::BT, wave, lane);
+    load_tile_dual<D>(rv, vst(S), (tbase + t) * Q::BT, wave, lane);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -562,15 +576,16 @@ void fa2_bwd_dq_kernel(BwdParams p) {
     const float bb = pf[qb][rr + 1] * (dp[qb][rr + 1] - dltv[qb]);
     pd[qb][h][(rr >> 1) & 3] = pack_bf16(a, bb);
   };
-  // Causal: zero P^T where key > query (half u crossing this wave's diagonal).
-  auto causal_fixup = [&](int u) __attribute__((always_inline)) {
+  // Causal: zero P^T outside query - window <= key <= query, for a half (first key 32 ua)
+  // crossing this wave's diagonal or its window's start.
+  auto causal_fixup = [&](int ua) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int lim = qw + 32 * qb + l32 - 32 * u - 4 * hf;
+      const int lim = qw + 32 * qb + l32 - 32 * ua - 4 * hf;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         const int x = 8 * (rr >> 2) + (rr & 3);
-        pf[qb][rr] = x > lim ? 0.f : pf[qb][rr];
+        pf[qb][rr] = (x > lim || x < lim - W) ? 0.f : pf[qb][rr];
       }
     }
   };
@@ -580,7 +595,8 @@ void fa2_bwd_dq_kernel(BwdParams p) {
     const lds_char* kc = kst(SC) + kbc * 32 * C::ROWB;
     const lds_char* kn = kst(SN) + kbn * 32 * C::ROWB;
     const lds_char* vn = vst(SN) + kbn * 32 * C::ROWB;
-    const bool diag = p.causal && 32 * u + 31 > qw;
+    const int ua = u + 2 * tbase;  // the half's index from key 0
+    const bool fix = p.causal && (32 * ua + 31 > qw || 32 * ua < qw + Q::RPW - 1 - W);
     auto read_op = [&](auto J) __attribute__((always_inline)) -> u32x4 {
       constexpr int j = decltype(J)::value;
       if constexpr (j < KS) {
@@ -611,7 +627,7 @@ void fa2_bwd_dq_kernel(BwdParams p) {
     auto valu_step = [&](auto J) __attribute__((always_inline)) {
       constexpr int j = decltype(J)::value;
       if constexpr (j == 0) {
-        if (diag) causal_fixup(u);
+        if (fix) causal_fixup(ua);
       }
       if constexpr (j >= DL && j < DL + KS) {
         constexpr int per = 16 / KS;  // element pairs per step
@@ -717,6 +733,7 @@ static BwdParams make_params(const void* q, const void* k, const void* v, const 
   p.c = fabsf(s.scale) * kLog2e;
   p.scale = s.scale;
   p.kneg = s.scale < 0.f ? 0x80008000u : 0u;
+  p.window = s.window >= 0 ? s.window : kNoWindow;
   return p;
 }
 

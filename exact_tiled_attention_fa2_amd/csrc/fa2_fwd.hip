@@ -8,8 +8,8 @@
 // never stored. Only O and LSE = m + ln l reach HBM.
 //
 // gfx950 mapping (one workgroup per (batch, query head, 256-row query block)):
-//  * 4 waves; each wave owns 64 query rows (two 32-row MFMA blocks) for the whole pass, so
-//    the online-softmax state and all row reductions stay in that wave's registers.
+//  * 8 waves, two per SIMD; each wave owns 32 query rows for the whole pass, so the
+//    online-softmax state and all row reductions stay in that wave's registers.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: each lane then
 //    holds one query row and 16 keys, the row max/sum are in-register reductions plus one
 //    v_permlane32_swap, and S^T's accumulator is directly the B operand of O^T += V^T P^T.
@@ -19,6 +19,8 @@
 //  * Causal: K/V tiles above a wave's last row are skipped; only tiles that straddle the
 //    diagonal (or the ragged end of the sequence) are masked. Query blocks are scheduled
 //    heaviest first, and blocks of one head stay on one XCD so their K/V reads share an L2.
+//  * Sliding window (causal, keys i - W .. i): the workgroup starts at its first visible tile,
+//    and the leading tiles that cross the window's lower edge are masked too.
 //  * Scale folded into the exponent: p = 2^(s*c - m) with c = |scale|*log2(e); a negative
 //    scale flips the sign of the Q operand instead. The accumulator rescale is skipped when
 //    no row max in the wave changed.
@@ -41,6 +43,7 @@ struct FwdParams {
   unsigned qneg;  // 0x80008000 flips both bf16 signs of a packed pair when scale < 0
   int nqb;        // query blocks per head
   int xcd_remap;  // B*Hq divisible by 8: keep each head's blocks on one XCD
+  int window;     // causal window: query i sees keys i - window .. i (>= N: no window)
 };
 
 template <int D>
@@ -145,19 +148,30 @@ void fa2_fwd_kernel(FwdParams p) {
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + kvoff, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + kvoff, head_bytes);
 
-  // Tiles of the workgroup, tiles this wave computes (causal: up to its last row), and the
-  // leading tiles that need no mask for this wave.
+  // Tiles are numbered from the workgroup's first visible tile tbase (a window hides the keys
+  // before q0 - window). Counted from there: the workgroup's tiles, the tiles this wave
+  // computes (causal: up to its last row), the leading tiles that cross the window's lower
+  // edge for some row of this wave (masked), and the tiles wholly below its diagonal.
+  const int W = p.window;
+  const int tbase = q0 > W ? (q0 - W) / C::BN : 0;
   const int qend = min(q0 + C::BM, N);
-  const int ntiles = p.causal ? (qend + C::BN - 1) / C::BN : (N + C::BN - 1) / C::BN;
-  const int nmine = p.causal ? min(ntiles, (qlo + C::QPW - 1) / C::BN + 1) : ntiles;
-  const int nfree = min(nmine, p.causal ? (qlo + 1) / C::BN : N / C::BN);
+  const int ntiles_abs = p.causal ? (qend + C::BN - 1) / C::BN : (N + C::BN - 1) / C::BN;
+  const int nmine_abs = p.causal ? min(ntiles_abs, (qlo + C::QPW - 1) / C::BN + 1) : ntiles_abs;
+  const int nfree_abs = min(nmine_abs, p.causal ? (qlo + 1) / C::BN : N / C::BN);
+  const int ntiles = ntiles_abs - tbase;
+  const int nmine = nmine_abs - tbase;
+  const int nfree = max(0, nfree_abs - tbase);
+  const int edge = qlo + C::QPW - 1 - W;  // keys below this fall outside some row's window
+  const int nlead = edge > 0 ? max(0, (edge + C::BN - 1) / C::BN - tbase) : 0;
 
   // Tile t goes to stage t % 2: K two tiles ahead of its use, V one tile ahead.
   auto fetch_k = [&](int t) {
-    if (t < ntiles) load_tile<D, false>(rk, (t & 1) ? (lds_char*)k_st1 : (lds_char*)k_st0, t * C::BN, wave, lane);
+    if (t < ntiles)
+      load_tile<D, false>(rk, (t & 1) ? (lds_char*)k_st1 : (lds_char*)k_st0, (tbase + t) * C::BN, wave, lane);
   };
   auto fetch_v = [&](int t) {
-    if (t < ntiles) load_tile<D, true>(rv, (t & 1) ? (lds_char*)v_st1 : (lds_char*)v_st0, t * C::BN, wave, lane);
+    if (t < ntiles)
+      load_tile<D, true>(rv, (t & 1) ? (lds_char*)v_st1 : (lds_char*)v_st0, (tbase + t) * C::BN, wave, lane);
   };
 
   // Q as the B operand of S^T = K Q^T: lane holds query l32, head-dim k = 16*ks + 8*hf + e.
@@ -221,15 +235,18 @@ void fa2_fwd_kernel(FwdParams p) {
     const u32x2 hi = lds_read8_tr(base + 8 * C::ROWB);
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
-  // Elements e = 16*kb + r of a lane's 32 scores per query block.
+  // Elements e = 16*kb + r of a lane's 32 scores per query block. A row that has not met a
+  // visible key yet (possible under a window) still has m = -inf; its masked scores then use
+  // reference 0 and give p = 0.
   auto exp_slice = [&](STile& sc, PTile& pf, float (&sum)[C::NQB], int e0) {
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
       for (int e = e0; e < e0 + EXP_SLICE; e += 2) {
         const int kb = e >> 4, r = e & 15;
-        const float p0 = fast_exp2(__builtin_fmaf(sc[qb][kb][r], c, -m[qb]));
-        const float p1 = fast_exp2(__builtin_fmaf(sc[qb][kb][r + 1], c, -m[qb]));
+        const float mref = m[qb] == -INFINITY ? 0.f : m[qb];
+        const float p0 = fast_exp2(__builtin_fmaf(sc[qb][kb][r], c, -mref));
+        const float p1 = fast_exp2(__builtin_fmaf(sc[qb][kb][r + 1], c, -mref));
         sum[qb] += p0 + p1;
         pf[qb][kb][r >> 3][(r >> 1) & 3] = pack_bf16(p0, p1);
       }
@@ -239,12 +256,13 @@ void fa2_fwd_kernel(FwdParams p) {
     for (int qb = 0; qb < C::NQB; ++qb) {
       const int qi = qlo + qb * 32 + l32;
       const int lim = p.causal ? min(qi, N - 1) : N - 1;  // last visible key
+      const int lo = qi - W;                              // first visible key
 #pragma unroll
       for (int e = e0; e < e0 + MAX_SLICE; ++e) {
         const int kb = e >> 4, r = e & 15;
         if (mask) {
           const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-          sn[qb][kb][r] = key > lim ? -INFINITY : sn[qb][kb][r];
+          sn[qb][kb][r] = (key > lim || key < lo) ? -INFINITY : sn[qb][kb][r];
         }
         mx[qb] = fmaxf(mx[qb], sn[qb][kb][r]);
       }
@@ -302,7 +320,10 @@ void fa2_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int qb = 0; qb < C::NQB; ++qb) {
         const float mnew = fmaxf(m[qb], mt[qb]);
-        const float alpha = fast_exp2(m[qb] - mnew);  // 0 before the first tile (m = -inf)
+        // 0 when the row had no visible key before (m = -inf); 1 when its reference does not
+        // move -- also for a row that still has none (m = mnew = -inf), which another row of
+        // the wave brought into this branch.
+        const float alpha = m[qb] == mnew ? 1.f : fast_exp2(m[qb] - mnew);
         m[qb] = mnew;
         l[qb] *= alpha;
         // Scaled through a zero-operand MFMA: every definition of an accumulator is then an
@@ -339,7 +360,7 @@ void fa2_fwd_kernel(FwdParams p) {
     }
     s_tile(k_next, sbuf[PAR ^ 1], [&](int ks) { exp_slice(sbuf[PAR], pf, sum, ks * EXP_SLICE); });
     pv_tile(v_cur, pf, [&](int i) {
-      max_slice(sbuf[PAR ^ 1], mx, i * MAX_SLICE, MASK_NEXT, (t + 1) * C::BN);
+      max_slice(sbuf[PAR ^ 1], mx, i * MAX_SLICE, MASK_NEXT, (tbase + t + 1) * C::BN);
     });
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) l[qb] += sum[qb];
@@ -369,7 +390,7 @@ void fa2_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) mx[qb] = -INFINITY;
     s_tile((const lds_char*)k_st0, sbuf[0], [&](int) {});
-    for (int i = 0; i < NPV; ++i) max_slice(sbuf[0], mx, i * MAX_SLICE, nfree == 0, 0);
+    for (int i = 0; i < NPV; ++i) max_slice(sbuf[0], mx, i * MAX_SLICE, nfree == 0 || nlead > 0, tbase * C::BN);
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) m[qb] = -INFINITY;
     rescale_if_needed(mx);  // sets the first reference; O and l are still zero
@@ -378,8 +399,14 @@ void fa2_fwd_kernel(FwdParams p) {
   using P1 = std::integral_constant<int, 1>;
   // Steps run in pairs (stage 0, then stage 1) so each step names its arrays statically and no
   // branch merges the accumulators. Step t masks tile t+1: unmasked steps are those with
-  // t + 1 < nfree; masking an unmasked tile is merely slower, so counts are rounded to pairs.
+  // nlead <= t + 1 < nfree; masking an unmasked tile is merely slower, so the counts are
+  // rounded to pairs (the window's leading masked steps up, the unmasked ones down).
   int t = 0;
+  const int lead_steps = nlead & ~1;
+  for (; t < lead_steps && t + 2 < nmine; t += 2) {
+    step(P0{}, std::true_type{}, t);
+    step(P1{}, std::true_type{}, t + 1);
+  }
   const int nfree_steps = nfree > 0 ? ((nfree - 1) & ~1) : 0;
   for (; t < nfree_steps; t += 2) {
     step(P0{}, std::false_type{}, t);
@@ -442,6 +469,7 @@ hipError_t launch_forward(const void* q, const void* k, const void* v, float* o,
   const int BM = FwdCfg<128>::BM;
   p.nqb = (s.N + BM - 1) / BM;
   p.xcd_remap = ((s.B * s.Hq) % 8) == 0;
+  p.window = s.window >= 0 ? s.window : kNoWindow;
   const dim3 grid((unsigned)(s.B * s.Hq * p.nqb)), block(FwdCfg<128>::WAVES * 64);
   if (s.d == 128)
     hipLaunchKernelGGL(fa2_fwd_kernel<128>, grid, block, 0, stream, p);

@@ -11,7 +11,11 @@ struct AttnShape {
   int B, Hq, Hkv, N, d;
   int causal;
   float scale;
+  int window = -1;  // causal sliding window: query i sees keys i - window .. i; < 0: none
 };
+
+// Window value the kernels use when there is none: larger than any supported N.
+constexpr int kNoWindow = 0x3fffffff;
 
 hipError_t launch_forward(const void* q, const void* k, const void* v, float* o, float* lse,
                           const AttnShape& s, hipStream_t stream);

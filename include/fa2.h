@@ -58,7 +58,8 @@ typedef enum {
   FA2_ERR_MISALIGNED = 6,           /* a pointer is not 16-byte aligned                    */
   FA2_ERR_ALIASING = 7,             /* an output overlaps an input or another output       */
   FA2_ERR_WORKSPACE = 8,            /* workspace NULL or smaller than required             */
-  FA2_ERR_HIP = 9                   /* a kernel launch failed                              */
+  FA2_ERR_HIP = 9,                  /* a kernel launch failed                              */
+  FA2_ERR_BAD_WINDOW = 10           /* sliding window < 0                                  */
 } fa2_status;
 
 /*
@@ -123,6 +124,29 @@ int fa2_backward_dkdv(const void* q, const void* k, const void* v, const void* d
 int fa2_backward_dq(const void* q, const void* k, const void* v, const void* dO,
                     const void* workspace, size_t workspace_bytes, float* dq, int B, int Hq,
                     int Hkv, int N, int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * Sliding-window (local) causal attention: query row i attends to key rows j with
+ * max(0, i - window) <= j <= i, i.e. itself and the `window` keys before it. The pages name
+ * sliding-window models (Mistral variants, Gemma's local layers) as the case where FA2
+ * runtimes may fall back to another path ("Flash Attention 2: attivarla (llama.cpp, Ollama,
+ * vLLM)", section "Casi in cui non aiuta (o peggiora la situazione)"); they give no formula,
+ * and this is the plain reading of a window of `window` previous tokens.
+ *   window >= 0 (FA2_ERR_BAD_WINDOW otherwise, checked first); window >= N - 1 is exactly
+ *   fa2_forward / fa2_backward with causal = 1. All other arguments, layouts, checks and
+ *   guarantees are those of fa2_forward / fa2_backward (causal is implied). K/V tiles that lie
+ *   wholly outside every row's window are neither loaded nor computed, so the work is about
+ *   N * (window + 1) key visits per head instead of N^2 / 2.
+ * fa2_backward_window takes the o and lse written by fa2_forward_window with the same window.
+ */
+int fa2_forward_window(const void* q, const void* k, const void* v, float* o, float* lse,
+                       int B, int Hq, int Hkv, int N, int d, int window, float scale,
+                       hipStream_t stream);
+
+int fa2_backward_window(const void* q, const void* k, const void* v, const float* o,
+                        const float* lse, const void* dO, float* dq, float* dk, float* dv,
+                        int B, int Hq, int Hkv, int N, int d, int window, float scale,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, human-readable name of a status code ("FA2_OK", ...); "FA2_UNKNOWN" otherwise. */
 const char* fa2_status_string(int status);

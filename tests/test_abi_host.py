@@ -115,3 +115,33 @@ def test_phase_entry_points_validate(lib):
     assert fa2.fa2_backward_dq(*args, P(9), 1, 2, 1, 64, 64, 1, 0.1) == 7   # dq over the workspace
     assert fa2.fa2_backward_dq(*args, P(6) + 4, 1, 2, 1, 64, 64, 1, 0.1) == 6
     assert fa2.fa2_backward_dq(*args, P(6), 1, 2, 1, 64, 32, 1, 0.1) == 3
+
+
+def fwdw(**kw):
+    a = dict(q=P(0), k=P(1), v=P(2), o=P(3), lse=P(4), B=1, Hq=2, Hkv=1, N=128, d=64, window=16, scale=0.125)
+    a.update(kw)
+    return fa2.fa2_forward_window(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["N"],
+                                  a["d"], a["window"], a["scale"])
+
+
+def bwdw(**kw):
+    a = dict(q=P(0), k=P(1), v=P(2), o=P(3), lse=P(4), dO=P(5), dq=P(6), dk=P(7), dv=P(8),
+             B=1, Hq=2, Hkv=1, N=128, d=64, window=16, scale=0.125, ws=P(9), wsb=1 << 20)
+    a.update(kw)
+    return fa2.fa2_backward_window(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dO"], a["dq"], a["dk"],
+                                   a["dv"], a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["window"],
+                                   a["scale"], a["ws"], a["wsb"])
+
+
+@pytest.mark.parametrize("call", [fwdw, bwdw])
+def test_window_entry_points_validate(lib, call):
+    assert call(window=-1) == 10 and call(window=-100, d=96) == 10   # the window is checked first
+    assert call(d=96) == 3 and call(Hq=3, Hkv=2) == 4 and call(scale=0.0) == 5
+    assert call(q=P(0) + 8) == 6 and call(q=None) == 1
+    assert call(B=0) == 0 and call(N=0) == 0 and call(B=0, window=0) == 0
+    assert call(o=P(0)) == 7 if call is fwdw else call(dq=P(5)) == 7
+
+
+def test_window_backward_workspace(lib):
+    assert bwdw(ws=None) == 8
+    assert bwdw(wsb=fa2.fa2_backward_workspace_size(1, 2, 128) - 1) == 8
