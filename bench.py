@@ -57,6 +57,94 @@ def counted_fwd_flops(B, Hq, N, d, causal):
     return f / 2 if causal else f
 
 
+def visible_pairs(N, causal, window=None):
+    """(query, key) pairs per head that the mask leaves visible."""
+    if not causal:
+        return N * N
+    if window is None or window >= N - 1:
+        return N * (N + 1) // 2
+    W = window
+    return W * (W + 1) // 2 + (N - W) * (W + 1)
+
+
+def time_sequence(calls, steps, warmup, stream):
+    """Median (over steps) of each call's duration and of the whole sequence, in ms, from HIP
+    events recorded on ``stream`` between the calls."""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    for s in range(steps):
+        for i, c in enumerate(calls):
+            ev[s][i].record(stream)
+            c()
+        ev[s][len(calls)].record(stream)
+    torch.cuda.synchronize()
+    per = [float(np.median([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)])) for i in range(len(calls))]
+    total = float(np.median([ev[s][0].elapsed_time(ev[s][len(calls)]) for s in range(steps)]))
+    return per, total
+
+
+def extra_workloads(fa2, seedgen, dev, stream, steps):
+    """Non-headline measurements: the sliding-window path at the headline shape, and the other
+    workload shapes (forward-only prefill shapes, a training shape). Values are TFLOP/s of the
+    counted FLOPs over the visible (query, key) pairs: 4d per pair forward, 10d fwd+bwd."""
+    import numpy as np
+    import torch
+
+    def up(x):
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def check(st, what):
+        if st != 0:
+            raise fa2.Fa2Error(st, what)
+
+    out = {}
+    cases = [("window_W1024_B2_H32_N8192_d128", 2, 32, 32, 8192, 128, True, 1024, True, 0x5EED0006),
+             ("fwd_B4_H16_N2048_d64", 4, 16, 16, 2048, 64, False, None, False, 0x5EED0002),
+             ("fwd_B1_Hq32_Hkv8_N32768_d128_causal", 1, 32, 8, 32768, 128, True, None, False, 0x5EED0004),
+             ("fwdbwd_B4_H16_N4096_d128_causal", 4, 16, 16, 4096, 128, True, None, True, 0x5EED0005)]
+    for name, B, Hq, Hkv, N, d, causal, W, with_bwd, seed in cases:
+        if with_bwd:
+            q, k, v, dO = seedgen.attention_inputs(seed, B, Hq, Hkv, N, d, with_do=True)
+        else:
+            (q, k, v), dO = seedgen.attention_inputs(seed, B, Hq, Hkv, N, d), None
+        qd, kd, vd = up(q), up(k), up(v)
+        dod = up(dO) if with_bwd else None
+        o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+        dq = torch.empty_like(o)
+        dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev)
+        dv = torch.empty_like(dk)
+        wsb = fa2.fa2_backward_workspace_size(B, Hq, N)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        scale = 1.0 / math.sqrt(d)
+        if W is None:
+            fcall = lambda: check(fa2.fa2_forward(qd, kd, vd, o, lse, B, Hq, Hkv, N, d, causal, scale, stream), name)
+            bcall = lambda: check(fa2.fa2_backward(qd, kd, vd, o, lse, dod, dq, dk, dv, B, Hq, Hkv, N, d, causal,
+                                                   scale, ws, wsb, stream), name)
+        else:
+            fcall = lambda: check(fa2.fa2_forward_window(qd, kd, vd, o, lse, B, Hq, Hkv, N, d, W, scale, stream), name)
+            bcall = lambda: check(fa2.fa2_backward_window(qd, kd, vd, o, lse, dod, dq, dk, dv, B, Hq, Hkv, N, d, W,
+                                                          scale, ws, wsb, stream), name)
+        calls = [fcall, bcall] if with_bwd else [fcall]
+        per, total = time_sequence(calls, steps, 2, stream)
+        pairs = B * Hq * visible_pairs(N, causal, W)
+        r = {"B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "causal": causal, "window": W,
+             "fwd_ms": round(per[0], 4), "fwd_tflops": round(pairs * 4 * d / (per[0] * 1e-3) / 1e12, 1)}
+        if with_bwd:
+            r["bwd_ms"] = round(per[1], 4)
+            r["fwd_bwd_tflops"] = round(pairs * 10 * d / (total * 1e-3) / 1e12, 1)
+        out[name] = r
+        log("  extra %-38s %s" % (name, r))
+        del q, k, v, dO, qd, kd, vd, dod, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(q, k, v, dO, w, budget_s):
     """The fp64 oracle on a bounded sample: whole (b, h) heads of the workload, forward and
     backward in full, one head at a time until ``budget_s`` seconds have been spent."""
@@ -97,6 +185,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the non-headline workloads")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (5 times), for scaling "
@@ -211,6 +300,10 @@ def main():
     roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(dom), "kernel": dom}
 
+    extras = None
+    if not args.no_extras:
+        extras = extra_workloads(fa2, seedgen, dev, stream, max(5, args.steps))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(q, k, v, dO, w, args.cpu_seconds)
@@ -246,6 +339,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "extras": extras,
         "peak_tflops": PEAK_BF16_TFLOPS,
         "device": props.name,
     }
