@@ -50,6 +50,8 @@ def _bind(path: str):
     lib.oracle_backward_dkdv.restype = cint
     lib.oracle_backward_dkdv.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, cint, i64, dbl, p, p, p, p,
                                          i64, p, p, cint]
+    lib.oracle_decode.restype = cint
+    lib.oracle_decode.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, cint, dbl, p, p]
     return lib
 
 
@@ -160,6 +162,25 @@ class Oracle:
         return dq, dk, dv, (m, l, D)
 
 
+    def decode(self, q, k, v, causal: bool, scale: float):
+        """O [B,Hq,Nq,d] and LSE [B,Hq,Nq] of Nq query rows against Nk cached keys; causal rows
+        are aligned to the end of the cache (row i sees keys j <= Nk - Nq + i)."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        if q.ndim != 4 or k.ndim != 4 or v.shape != k.shape:
+            raise ValueError("q [B,Hq,Nq,d], k and v [B,Hkv,Nk,d]")
+        B, Hq, Nq, d = q.shape
+        Bk, Hkv, Nk, dk = k.shape
+        if (Bk, dk) != (B, d) or Hq % Hkv:
+            raise ValueError("inconsistent shapes q %s k %s" % (q.shape, k.shape))
+        o = np.empty((B, Hq, Nq, d))
+        lse = np.empty((B, Hq, Nq))
+        rc = self.lib.oracle_decode(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, Hq, Hkv, Nq, Nk, d,
+                                    int(bool(causal)), float(scale), o.ctypes.data, lse.ctypes.data)
+        if rc:
+            raise RuntimeError("oracle_decode failed (%d)" % rc)
+        return o, lse
+
+
 _default = None
 
 
@@ -184,6 +205,10 @@ def backward(q, k, v, dO, causal: bool, scale: float, qrows=None, krows=None,
              threads: int | None = None, stats=None, window: int = -1):
     return default().backward(q, k, v, dO, causal, scale, qrows=qrows, krows=krows,
                               threads=threads, stats=stats, window=window)
+
+
+def decode(q, k, v, causal: bool, scale: float):
+    return default().decode(q, k, v, causal, scale)
 
 
 def forward_flops(B: int, Hq: int, N: int, d: int, causal: bool, nrows: int | None = None) -> float:

@@ -288,3 +288,51 @@ int oracle_backward_dkdv(const double* q, const double* k, const double* v, cons
   J.out0 = dk; J.out1 = dv; J.nitems = B * Hkv * nrows; J.kind = K_DKDV;
   return run(&J, nthreads);
 }
+
+/*
+ * Decode-shaped attention: Nq query rows against a cache of Nk key/value rows (Nq <= Nk when
+ * causal). The causal mask is aligned to the END of the cache: query row i stands at cache
+ * position Nk - Nq + i and sees keys j <= Nk - Nq + i -- the rows being decoded are the newest
+ * tokens. This is the long-KV-cache inference shape of the decoding pages (FlashDecoding++ is
+ * in the wiki article's literature list; the qualellm.it guide centres on local inference
+ * with long contexts); they give no formula, so it is the plain definition with that
+ * alignment. q, o [B,Hq,Nq,d]; k, v [B,Hkv,Nk,d]; lse [B,Hq,Nq]; natural log.
+ */
+int oracle_decode(const double* q, const double* k, const double* v, int64_t B, int64_t Hq,
+                  int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, int causal, double scale,
+                  double* o, double* lse) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1 || Hq % Hkv) return -1;
+  if (causal && Nq > Nk) return -1;
+  const int64_t group = Hq / Hkv;
+  double* s = (double*)malloc(sizeof(double) * (size_t)Nk);
+  if (!s) return -2;
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t hq = 0; hq < Hq; ++hq) {
+      const int64_t g = hq / group;
+      const double* Kh = k + (b * Hkv + g) * Nk * d;
+      const double* Vh = v + (b * Hkv + g) * Nk * d;
+      for (int64_t i = 0; i < Nq; ++i) {
+        const double* qi = q + ((b * Hq + hq) * Nq + i) * d;
+        const int64_t nvis = causal ? Nk - Nq + i + 1 : Nk;
+        double m = -INFINITY;
+        for (int64_t j = 0; j < nvis; ++j) {
+          s[j] = scale * dot(qi, Kh + j * d, d);
+          if (s[j] > m) m = s[j];
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < nvis; ++j) {
+          s[j] = exp(s[j] - m);
+          l += s[j];
+        }
+        double* oi = o + ((b * Hq + hq) * Nq + i) * d;
+        for (int64_t c = 0; c < d; ++c) {
+          double acc = 0.0;
+          for (int64_t j = 0; j < nvis; ++j) acc += s[j] * Vh[j * d + c];
+          oi[c] = acc / l;
+        }
+        lse[(b * Hq + hq) * Nq + i] = m + log(l);
+      }
+    }
+  free(s);
+  return 0;
+}

@@ -387,10 +387,79 @@ def pin_window_locality(orc):
     assert not np.allclose(o[:, :, 6 + W - 1], o2[:, :, 6 + W - 1]), "row 5 + W must see key 5"
 
 
+# ----------------------------------------------------------------------------- decode pins
+
+def pin_decode_square_is_forward(orc):
+    """With Nq = Nk the decode alignment is the ordinary top-left one: decode equals forward."""
+    rng = _rng(18)
+    B, Hq, Hkv, N, d = 1, 4, 2, 13, 6
+    q, k, v = (rng.standard_normal(s) for s in ((B, Hq, N, d), (B, Hkv, N, d), (B, Hkv, N, d)))
+    for causal in (False, True):
+        o1, l1 = orc.decode(q, k, v, causal, 0.4)
+        o2, l2 = orc.forward(q, k, v, causal, 0.4)
+        _close(o1, o2, 1e-13, "decode square O")
+        _close(l1, l2, 1e-13, "decode square LSE")
+
+
+def pin_decode_torch(orc):
+    """Agreement with torch fp64 attention under an explicit end-aligned causal mask (query i
+    sees keys j <= Nk - Nq + i), grouped-query heads included."""
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(19)
+    for (B, Hq, Hkv, Nq, Nk, d) in [(2, 8, 2, 1, 37, 8), (1, 4, 4, 3, 20, 16), (1, 6, 2, 5, 5, 4),
+                                    (1, 2, 1, 4, 70, 32)]:
+        q = rng.standard_normal((B, Hq, Nq, d))
+        k, v = (rng.standard_normal((B, Hkv, Nk, d)) for _ in range(2))
+        sc = 0.35
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        mask = torch.from_numpy(np.arange(Nk)[None, :] <= (Nk - Nq + np.arange(Nq))[:, None])
+        for causal in (False, True):
+            ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask if causal else None, scale=sc,
+                                                 enable_gqa=(Hq != Hkv))
+            o, lse = orc.decode(q, k, v, causal, sc)
+            _close(o, ref.numpy(), 1e-12, "decode sdpa O")
+            s = torch.matmul(tq, tk.repeat_interleave(Hq // Hkv, dim=1).transpose(-1, -2).contiguous()) * sc
+            if causal:
+                s = s.masked_fill(~mask, float("-inf"))
+            _close(lse, torch.logsumexp(s, dim=-1).numpy(), 1e-12, "decode LSE")
+
+
+def pin_decode_single_rows(orc):
+    """One decoded row sees the whole cache, causal or not; a one-key cache returns V_0 and
+    LSE = scale <q, k_0>."""
+    rng = _rng(21)
+    q = rng.standard_normal((1, 2, 1, 5))
+    k, v = rng.standard_normal((1, 1, 9, 5)), rng.standard_normal((1, 1, 9, 5))
+    a = orc.decode(q, k, v, True, 0.7)
+    b = orc.decode(q, k, v, False, 0.7)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    o, lse = orc.decode(q, k[:, :, :1], v[:, :, :1], True, 0.7)
+    for h in range(2):
+        _close(o[0, h, 0], v[0, 0, 0], 1e-15, "one-key O")
+        _close(lse[0, h, 0], 0.7 * float(q[0, h, 0] @ k[0, 0, 0]), 1e-15, "one-key LSE")
+
+
+def pin_decode_split_merge(orc):
+    """Attention over a cache equals the logsumexp-weighted merge of attention over its two
+    halves: LSE = ln(e^LSE1 + e^LSE2), O = e^(LSE1-LSE) O1 + e^(LSE2-LSE) O2."""
+    rng = _rng(22)
+    B, Hq, Hkv, Nq, Nk, d = 1, 4, 2, 3, 40, 8
+    q = rng.standard_normal((B, Hq, Nq, d))
+    k, v = (rng.standard_normal((B, Hkv, Nk, d)) for _ in range(2))
+    o, lse = orc.decode(q, k, v, False, 0.5)
+    o1, l1 = orc.decode(q, k[:, :, :17], v[:, :, :17], False, 0.5)
+    o2, l2 = orc.decode(q, k[:, :, 17:], v[:, :, 17:], False, 0.5)
+    L = np.logaddexp(l1, l2)
+    _close(lse, L, 1e-12, "merged LSE")
+    _close(o, np.exp(l1 - L)[..., None] * o1 + np.exp(l2 - L)[..., None] * o2, 1e-12, "merged O")
+
+
 FORWARD_PINS = [pin_constant_scores, pin_causal_first_row, pin_single_key, pin_two_keys_logistic,
                 pin_dominant_score, pin_joint_permutation, pin_key_shift, pin_value_affine,
                 pin_torch_sdpa]
 BACKWARD_PINS = [pin_backward_invariants, pin_torch_autograd, pin_gqa_equals_expanded]
 BOTH_PINS = [pin_hand_worked, pin_sampled_rows_match_full, pin_finite_differences]
 WINDOW_PINS = [pin_window_zero_and_one, pin_window_torch, pin_window_locality]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS + BOTH_PINS + WINDOW_PINS
+DECODE_PINS = [pin_decode_square_is_forward, pin_decode_torch, pin_decode_single_rows, pin_decode_split_merge]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + BOTH_PINS + WINDOW_PINS + DECODE_PINS

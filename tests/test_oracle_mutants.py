@@ -21,7 +21,10 @@ MUTATIONS = [
     ("no softmax normalisation", "o[c] = acc[c] / l;", "o[c] = acc[c];"),
     ("LSE without the max", "J->out1[slice * J->nrows + r] = m + log(l);", "J->out1[slice * J->nrows + r] = log(l);"),
     ("LSE in base 2", "J->out1[slice * J->nrows + r] = m + log(l);", "J->out1[slice * J->nrows + r] = m + log2(l);"),
-    ("max subtracted with wrong sign", "s[j] = exp(s[j] - m);", "s[j] = exp(s[j] + m);"),
+    ("max subtracted with wrong sign", "for (int64_t j = j0; j < nvis; ++j) {\n    s[j] = exp(s[j] - m);",
+     "for (int64_t j = j0; j < nvis; ++j) {\n    s[j] = exp(s[j] + m);"),
+    ("decode max subtracted with wrong sign", "for (int64_t j = 0; j < nvis; ++j) {\n          s[j] = exp(s[j] - m);",
+     "for (int64_t j = 0; j < nvis; ++j) {\n          s[j] = exp(s[j] + m);"),
     ("value columns reversed", "acc[c] += s[j] * Vh[j * d + c];", "acc[c] += s[j] * Vh[j * d + (d - 1 - c)];"),
     ("GQA heads interleaved", "int64_t b = slice / J->Hq, hq = slice % J->Hq, g = hq / group;\n    int64_t i = J->rows",
      "int64_t b = slice / J->Hq, hq = slice % J->Hq, g = hq % J->Hkv;\n    int64_t i = J->rows"),
@@ -44,6 +47,13 @@ MUTATIONS = [
      "return (J->window >= 0 && i > J->window + 1) ? i - J->window - 1 : 0;"),
     ("window ignored by dK/dV", "int64_t i1 = last_query(J, j);", "int64_t i1 = N;"),
     ("dK/dV window end one row short", "? j + J->window + 1 : J->N;", "? j + J->window : J->N;"),
+    ("decode causal aligned to the start", "const int64_t nvis = causal ? Nk - Nq + i + 1 : Nk;",
+     "const int64_t nvis = causal ? i + 1 : Nk;"),
+    ("decode causal one key short", "const int64_t nvis = causal ? Nk - Nq + i + 1 : Nk;",
+     "const int64_t nvis = causal ? Nk - Nq + i : Nk;"),
+    ("decode without normalisation", "oi[c] = acc / l;", "oi[c] = acc;"),
+    ("decode GQA head mapping", "const int64_t g = hq / group;\n      const double* Kh = k + (b * Hkv + g) * Nk * d;",
+     "const int64_t g = hq % Hkv;\n      const double* Kh = k + (b * Hkv + g) * Nk * d;"),
 ]
 
 
