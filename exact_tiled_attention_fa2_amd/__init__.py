@@ -24,7 +24,7 @@ STATUS_NAMES = {
 }
 EXPORTED = ("fa2_forward", "fa2_backward", "fa2_backward_workspace_size", "fa2_backward_preprocess",
             "fa2_backward_dkdv", "fa2_backward_dq", "fa2_forward_window", "fa2_backward_window",
-            "fa2_status_string")
+            "fa2_decode_workspace_size", "fa2_decode", "fa2_status_string")
 
 _lib = None
 
@@ -61,6 +61,10 @@ def load() -> ctypes.CDLL:
     lib.fa2_forward_window.argtypes = [p, p, p, p, p, i, i, i, i, i, i, f, p]
     lib.fa2_backward_window.restype = i
     lib.fa2_backward_window.argtypes = [p, p, p, p, p, p, p, p, p, i, i, i, i, i, i, f, p, z, p]
+    lib.fa2_decode_workspace_size.restype = z
+    lib.fa2_decode_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.fa2_decode.restype = i
+    lib.fa2_decode.argtypes = [p, p, p, p, p, i, i, i, i, i, i, i, f, p, z, p]
     lib.fa2_status_string.restype = ctypes.c_char_p
     lib.fa2_status_string.argtypes = [i]
     _lib = lib
@@ -132,6 +136,17 @@ def fa2_backward_window(q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, N, d, windo
                                       _ptr(workspace), int(workspace_bytes), _stream(stream))
 
 
+def fa2_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d) -> int:
+    return int(load().fa2_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d))
+
+
+def fa2_decode(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, workspace, workspace_bytes,
+               stream=None) -> int:
+    return load().fa2_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                             int(bool(causal)), float(scale), _ptr(workspace), int(workspace_bytes),
+                             _stream(stream))
+
+
 def fa2_status_string(status: int) -> str:
     return load().fa2_status_string(int(status)).decode()
 
@@ -186,3 +201,21 @@ def backward(q, k, v, o, lse, dO, causal: bool, scale: float, stream=None, works
     if st != FA2_OK:
         raise Fa2Error(st, "fa2_backward" if window is None else "fa2_backward_window")
     return dq, dk, dv
+
+
+def decode(q, k, v, causal: bool, scale: float, stream=None, workspace=None):
+    """O (fp32) and LSE (fp32) of q [B,Hq,Nq,d] against the cache k, v [B,Hkv,Nk,d] (bf16);
+    causal rows are the newest tokens (row i sees keys j <= Nk - Nq + i)."""
+    import torch
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    o = torch.empty((B, Hq, Nq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    need = fa2_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = fa2_decode(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, workspace, wbytes, stream)
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_decode")
+    return o, lse

@@ -193,6 +193,42 @@ int fa2_backward_window(const void* q, const void* k, const void* v, const float
                        workspace, workspace_bytes, stream);
 }
 
+size_t fa2_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || Hq % Hkv || (d != 64 && d != 128)) return 0;
+  fa2::AttnShape s{B, Hq, Hkv, 0, d, 0, 1.0f};
+  return fa2::decode_workspace_bytes(s, Nq, Nk);
+}
+
+int fa2_decode(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Hq,
+               int Hkv, int Nq, int Nk, int d, int causal, float scale, void* workspace,
+               size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || Nq < 0 || Nk < 0 || Hq < 0 || Hkv < 0) return FA2_ERR_BAD_SHAPE;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return FA2_ERR_BAD_GQA;
+  if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED_HEAD_DIM;
+  if (!isfinite(scale) || scale == 0.0f) return FA2_ERR_BAD_SCALE;
+  if (B == 0 || Nq == 0) return FA2_OK;
+  if (Nk == 0 || (causal && Nq > Nk)) return FA2_ERR_BAD_SHAPE;  // some row would see no key
+  if ((int64_t)Nk * d * 4 >= ((int64_t)1 << 31)) return FA2_ERR_BAD_SHAPE;
+  if ((int64_t)(Hq / Hkv) * Nq * d * 4 >= ((int64_t)1 << 31)) return FA2_ERR_BAD_SHAPE;
+  if ((int64_t)B * Hq * Nq >= ((int64_t)1 << 28) || (int64_t)B * Hkv >= ((int64_t)1 << 24))
+    return FA2_ERR_BAD_SHAPE;
+  const uint64_t rq = (uint64_t)B * Hq * Nq, rkv = (uint64_t)B * Hkv * Nk;
+  const Buf in[3] = {{q, rq * d * 2}, {k, rkv * d * 2}, {v, rkv * d * 2}};
+  const Buf out[2] = {{o, rq * d * 4}, {lse, rq * 4}};
+  int st = check_buffers(in, 3, out, 2);
+  if (st != FA2_OK) return st;
+  const size_t need = fa2_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return FA2_ERR_WORKSPACE;
+    const Buf all[5] = {in[0], in[1], in[2], out[0], out[1]};
+    const Buf ws[1] = {{workspace, need}};
+    st = check_buffers(all, 5, ws, 1);
+    if (st != FA2_OK) return st;
+  }
+  fa2::AttnShape s{B, Hq, Hkv, 0, d, causal != 0, scale};
+  return hip_status(fa2::launch_decode(q, k, v, o, lse, s, Nq, Nk, static_cast<float*>(workspace), stream));
+}
+
 int fa2_backward_preprocess(const float* o, const void* dO, const float* lse, void* workspace,
                             size_t workspace_bytes, int B, int Hq, int N, int d,
                             hipStream_t stream) {

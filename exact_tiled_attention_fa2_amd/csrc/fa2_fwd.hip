@@ -62,21 +62,6 @@ struct FwdCfg {
   static constexpr int LPW = TILE / 1024 / WAVES;  // 1 KB direct-to-LDS loads per wave per tile
 };
 
-// K tile: 16-byte chunk c of row r is stored at chunk position c ^ swz_k(r). The 16 rows a
-// quarter-wave reads at one chunk then land in 16 different bank groups.
-template <int D>
-__device__ __forceinline__ int swz_k(int r) {
-  constexpr int CH = D / 8, RP = 16 / CH;
-  return (r / RP) & (CH - 1);
-}
-// V tile: chunk c of row r at c ^ swz_v(r). A transposing read touches 4 rows x 4 chunks
-// per half-wave; this XOR spreads them over all 16 bank groups.
-template <int D>
-__device__ __forceinline__ int swz_v(int r) {
-  constexpr int CH = D / 8, RP = 16 / CH;
-  return 4 * ((r / RP) & (CH / 4 - 1));
-}
-
 // Copy keys [j0, j0+64) of one head into a swizzled LDS tile. Rows past N read as zero.
 template <int D, bool IS_V>
 __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, lds_char* tile, int j0,

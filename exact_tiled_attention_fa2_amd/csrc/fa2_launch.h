@@ -31,4 +31,10 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
                          const float* ws, float* dq, const AttnShape& s, hipStream_t stream);
 
+// Decode: s.N is unused; Nq query rows against Nk cache rows. The workspace holds the partial
+// results of the cache chunks (decode_workspace_bytes, 0 when one chunk suffices).
+size_t decode_workspace_bytes(const AttnShape& s, int Nq, int Nk);
+hipError_t launch_decode(const void* q, const void* k, const void* v, float* o, float* lse,
+                         const AttnShape& s, int Nq, int Nk, float* ws, hipStream_t stream);
+
 }  // namespace fa2

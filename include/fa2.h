@@ -148,6 +148,30 @@ int fa2_backward_window(const void* q, const void* k, const void* v, const float
                         int B, int Hq, int Hkv, int N, int d, int window, float scale,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Decode-shaped attention: Nq query rows against a cache of Nk key/value rows (Nq << Nk), the
+ * long-context inference shape the pages centre on ("Flash Attention 2: attivarla (llama.cpp,
+ * Ollama, vLLM)", sections "Perché Flash Attention 2" and "Guadagno misurato in base alla
+ * dimensione del contesto"; FlashDecoding++ in the literature of the wiki article
+ * "FlashAttention-2"). Exact attention, as fa2_forward, over rectangular shapes:
+ *   q      bf16 [B,Hq,Nq,d]   k, v  bf16 [B,Hkv,Nk,d]      (read only)
+ *   o      f32  [B,Hq,Nq,d]   lse   f32  [B,Hq,Nq]         (written; natural log)
+ *   causal != 0: the rows are the newest tokens -- query i stands at cache position
+ *   Nk - Nq + i and sees keys j <= Nk - Nq + i (requires Nq <= Nk). causal == 0: all keys.
+ * The cache is split into chunks processed in parallel; each chunk yields a partial (O, LSE)
+ * and a second kernel merges them: LSE = ln sum_s e^LSE_s, O = sum_s e^(LSE_s - LSE) O_s.
+ * workspace: device scratch for the partial results, at least
+ * fa2_decode_workspace_size(B,Hq,Hkv,Nq,Nk,d) bytes (0 when a single chunk suffices; then
+ * workspace may be NULL); owned by the caller, contents on entry irrelevant; must not overlap
+ * any other argument. Checks as fa2_forward; additionally Nk == 0 with Nq > 0, and causal with
+ * Nq > Nk, are FA2_ERR_BAD_SHAPE. B == 0 or Nq == 0 is an empty problem (FA2_OK).
+ */
+size_t fa2_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+
+int fa2_decode(const void* q, const void* k, const void* v, float* o, float* lse,
+               int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable name of a status code ("FA2_OK", ...); "FA2_UNKNOWN" otherwise. */
 const char* fa2_status_string(int status);
 

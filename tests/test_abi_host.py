@@ -145,3 +145,31 @@ def test_window_entry_points_validate(lib, call):
 def test_window_backward_workspace(lib):
     assert bwdw(ws=None) == 8
     assert bwdw(wsb=fa2.fa2_backward_workspace_size(1, 2, 128) - 1) == 8
+
+
+def dec(**kw):
+    a = dict(q=P(0), k=P(1), v=P(2), o=P(3), lse=P(4), B=1, Hq=8, Hkv=2, Nq=1, Nk=4096, d=128, causal=1,
+             scale=0.1, ws=P(9), wsb=1 << 26)
+    a.update(kw)
+    return fa2.fa2_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"],
+                          a["d"], a["causal"], a["scale"], a["ws"], a["wsb"])
+
+
+def test_decode_validation(lib):
+    assert dec(d=96) == 3 and dec(Hq=6, Hkv=4) == 4 and dec(scale=float("nan")) == 5
+    assert dec(Nk=0) == 2 and dec(Nq=8, Nk=7) == 2 and dec(Nq=-1) == 2
+    assert dec(q=None) == 1 and dec(k=P(1) + 4) == 6 and dec(o=P(1)) == 7
+    assert dec(Nq=0) == 0 and dec(B=0) == 0
+    need = fa2.fa2_decode_workspace_size(1, 8, 2, 1, 4096, 128)
+    assert need > 0 and need % 256 == 0
+    assert dec(ws=None) == 8 and dec(wsb=need - 1) == 8 and dec(ws=P(3)) == 7
+
+
+def test_decode_workspace_size(lib):
+    # a short cache needs no partial results; degenerate shapes need none either
+    assert fa2.fa2_decode_workspace_size(64, 32, 8, 1, 64, 128) == 0
+    assert fa2.fa2_decode_workspace_size(1, 8, 2, 1, 0, 128) == 0
+    assert fa2.fa2_decode_workspace_size(1, 8, 3, 1, 100, 128) == 0
+    big = fa2.fa2_decode_workspace_size(1, 8, 2, 4, 1 << 16, 128)
+    R = 4 * 4
+    assert big >= 2 * R * 129 * 4 and big % 256 == 0
