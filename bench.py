@@ -142,6 +142,27 @@ def extra_workloads(fa2, seedgen, dev, stream, steps):
         log("  extra %-38s %s" % (name, r))
         del q, k, v, dO, qd, kd, vd, dod, o, lse, dq, dk, dv, ws
         torch.cuda.empty_cache()
+    # Decode: one new token per sequence against a 32K-token cache (grouped-query heads). The
+    # pass streams K and V once, so it is reported against HBM bandwidth.
+    B, Hq, Hkv, Nq, Nk, d = 8, 32, 8, 1, 32768, 128
+    q = seedgen.normal_bf16(0x5EED0007, seedgen.TENSOR_IDS["q"], (B, Hq, Nq, d))
+    kc = seedgen.normal_bf16(0x5EED0007, seedgen.TENSOR_IDS["k"], (B, Hkv, Nk, d))
+    vc = seedgen.normal_bf16(0x5EED0007, seedgen.TENSOR_IDS["v"], (B, Hkv, Nk, d))
+    qd, kd, vd = up(q), up(kc), up(vc)
+    o = torch.empty((B, Hq, Nq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+    wsb = fa2.fa2_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    call = lambda: check(fa2.fa2_decode(qd, kd, vd, o, lse, B, Hq, Hkv, Nq, Nk, d, True, scale, ws, wsb, stream),
+                         "fa2_decode")
+    per, total = time_sequence([call], max(20, steps), 3, stream)
+    nbytes = 2 * B * Hkv * Nk * d * 2 + B * Hq * Nq * d * (2 + 4) + B * Hq * Nq * 4
+    r = {"B": B, "Hq": Hq, "Hkv": Hkv, "Nq": Nq, "Nk": Nk, "d": d, "causal": True, "ms": round(total, 4),
+         "algorithmic_bytes": nbytes, "GBps": round(nbytes / (total * 1e-3) / 1e9, 1),
+         "hbm_frac": round(nbytes / (total * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    out["decode_B8_Hq32_Hkv8_Nq1_Nk32768_d128"] = r
+    log("  extra %-38s %s" % ("decode_B8_Hq32_Hkv8_Nq1_Nk32768_d128", r))
     return out
 
 
