@@ -24,12 +24,20 @@ Range range_of(const void* p, uint64_t bytes) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Head dims each entry point supports.
+enum HeadDims { DIMS_64_128, DIMS_64_128_256 };
+
+bool head_dim_ok(int d, HeadDims dims) {
+  return d == 64 || d == 128 || (dims == DIMS_64_128_256 && d == 256);
+}
+
 // Shared shape checks. Returns FA2_OK and sets *empty when nothing needs computing.
-int check_shape(int B, int Hq, int Hkv, int N, int d, float scale, bool* empty) {
+int check_shape(int B, int Hq, int Hkv, int N, int d, float scale, bool* empty,
+                HeadDims dims = DIMS_64_128) {
   *empty = false;
   if (B < 0 || N < 0 || Hq < 0 || Hkv < 0) return FA2_ERR_BAD_SHAPE;
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return FA2_ERR_BAD_GQA;
-  if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED_HEAD_DIM;
+  if (!head_dim_ok(d, dims)) return FA2_ERR_UNSUPPORTED_HEAD_DIM;
   if (!isfinite(scale) || scale == 0.0f) return FA2_ERR_BAD_SCALE;
   if (B == 0 || N == 0) {
     *empty = true;
@@ -99,7 +107,7 @@ namespace {
 int forward_impl(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Hq,
                  int Hkv, int N, int d, int causal, int window, float scale, hipStream_t stream) {
   bool empty = false;
-  int st = check_shape(B, Hq, Hkv, N, d, scale, &empty);
+  int st = check_shape(B, Hq, Hkv, N, d, scale, &empty, DIMS_64_128_256);
   if (st != FA2_OK || empty) return st;
   const uint64_t rq = (uint64_t)B * Hq * N, rkv = (uint64_t)B * Hkv * N;
   const Buf in[3] = {{q, rq * d * 2}, {k, rkv * d * 2}, {v, rkv * d * 2}};

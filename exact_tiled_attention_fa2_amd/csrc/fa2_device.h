@@ -109,20 +109,28 @@ __device__ __forceinline__ void pin_vgpr(f32x16& x) { asm volatile("" : "+v"(x))
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// LDS tiles of bf16 rows of D elements (D / 8 chunks of 16 bytes per row).
+// LDS tiles of bf16 rows of D elements (D / 8 chunks of 16 bytes per row). The 64 banks form
+// 16 groups of 16 bytes; a row of 256 or 512 bytes starts in group 0, a 128-byte row in group 0
+// or 8. SWZ_ROWS rows share one 256-byte bank row, SWZ_SPAN chunks can be permuted.
+template <int D>
+struct SwzCfg {
+  static constexpr int CH = D / 8;
+  static constexpr int SWZ_ROWS = CH >= 16 ? 1 : 16 / CH;
+  static constexpr int SWZ_SPAN = CH >= 16 ? 16 : CH;
+};
 // K tile: chunk c of row r is stored at chunk position c ^ swz_k(r). The 16 rows a
 // quarter-wave reads at one chunk then land in 16 different bank groups.
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
-  constexpr int CH = D / 8, RP = 16 / CH;
-  return (r / RP) & (CH - 1);
+  using S = SwzCfg<D>;
+  return (r / S::SWZ_ROWS) & (S::SWZ_SPAN - 1);
 }
 // V tile: chunk c of row r at c ^ swz_v(r). A transposing read touches 4 rows x 4 chunks
 // per half-wave; this XOR spreads them over all 16 bank groups.
 template <int D>
 __device__ __forceinline__ int swz_v(int r) {
-  constexpr int CH = D / 8, RP = 16 / CH;
-  return 4 * ((r / RP) & (CH / 4 - 1));
+  using S = SwzCfg<D>;
+  return 4 * ((r / S::SWZ_ROWS) & (S::SWZ_SPAN / 4 - 1));
 }
 
 }  // namespace fa2

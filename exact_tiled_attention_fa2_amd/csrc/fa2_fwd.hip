@@ -49,14 +49,16 @@ struct FwdParams {
 template <int D>
 struct FwdCfg {
   static constexpr int BN = 64;               // keys per tile
-  static constexpr int WAVES = 8;             // two waves per SIMD
+  // Two waves per SIMD up to d = 128. At d = 256 a 32-row block's O accumulators alone take
+  // 128 registers, so one wave per SIMD with them in AGPRs.
+  static constexpr int WAVES = D <= 128 ? 8 : 4;
+  static constexpr int WPE = D <= 128 ? 2 : 1;  // waves per SIMD
   static constexpr int QPW = 32;              // query rows per wave
   static constexpr int NQB = QPW / 32;        // 32-row MFMA blocks per wave
   static constexpr int BM = WAVES * QPW;      // query rows per workgroup
   static constexpr int KS = D / 16;           // k-steps of the Q.K contraction
   static constexpr int DB = D / 32;           // 32-wide blocks of the head dim
   static constexpr int CH = D / 8;            // 16-byte chunks per bf16 row
-  static constexpr int RP = 16 / CH;          // rows per 256 bytes of LDS
   static constexpr int ROWB = D * 2;          // bytes per bf16 row
   static constexpr int TILE = BN * ROWB;      // bytes of one K or V tile
   static constexpr int LPW = TILE / 1024 / WAVES;  // 1 KB direct-to-LDS loads per wave per tile
@@ -103,7 +105,8 @@ __device__ __forceinline__ void map_block(int bid, const FwdParams& p, int& bh, 
 constexpr float kRescaleSlack = 8.0f;
 
 template <int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(FwdCfg<D>::WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE)))
 void fa2_fwd_kernel(FwdParams p) {
   using C = FwdCfg<D>;
   // Two K and two V stages in separate arrays: a DMA into one array and LDS reads of another
@@ -117,6 +120,7 @@ void fa2_fwd_kernel(FwdParams p) {
   const int wave = threadIdx.x >> 6;
   const int hf = lane >> 5;
   const int l32 = lane & 31;
+  if constexpr (D == 256) agpr_accumulators_hint();  // O in AGPRs: one wave per SIMD
 
   int bh, qblk;
   map_block(blockIdx.x, p, bh, qblk);
@@ -451,15 +455,17 @@ hipError_t launch_forward(const void* q, const void* k, const void* v, float* o,
   p.causal = s.causal;
   p.c = fabsf(s.scale) * kLog2e;
   p.qneg = s.scale < 0.f ? 0x80008000u : 0u;
-  const int BM = FwdCfg<128>::BM;
+  const int BM = s.d == 256 ? FwdCfg<256>::BM : FwdCfg<128>::BM;
   p.nqb = (s.N + BM - 1) / BM;
   p.xcd_remap = ((s.B * s.Hq) % 8) == 0;
   p.window = s.window >= 0 ? s.window : kNoWindow;
-  const dim3 grid((unsigned)(s.B * s.Hq * p.nqb)), block(FwdCfg<128>::WAVES * 64);
+  const dim3 grid((unsigned)(s.B * s.Hq * p.nqb));
   if (s.d == 128)
-    hipLaunchKernelGGL(fa2_fwd_kernel<128>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL(fa2_fwd_kernel<128>, grid, dim3(FwdCfg<128>::WAVES * 64), 0, stream, p);
+  else if (s.d == 256)
+    hipLaunchKernelGGL(fa2_fwd_kernel<256>, grid, dim3(FwdCfg<256>::WAVES * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL(fa2_fwd_kernel<64>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL(fa2_fwd_kernel<64>, grid, dim3(FwdCfg<64>::WAVES * 64), 0, stream, p);
   return hipGetLastError();
 }
 

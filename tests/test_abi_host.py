@@ -70,7 +70,13 @@ def bwd(**kw):
 
 @pytest.mark.parametrize("call", [fwd, bwd])
 def test_validation_codes(lib, call):
-    assert call(d=96) == 3 and call(d=256) == 3 and call(d=32) == 3
+    assert call(d=96) == 3 and call(d=192) == 3 and call(d=32) == 3
+    # d = 256: supported by the forward (checked here only together with another invalid
+    # argument, so nothing is ever launched on these fake addresses), rejected by the backward.
+    if call is fwd:
+        assert call(d=256, scale=0.0) == 5 and call(d=256, q=P(0) + 8) == 6
+    else:
+        assert call(d=256) == 3
     assert call(Hq=3, Hkv=2) == 4 and call(Hkv=0) == 4 and call(Hq=0) == 4
     assert call(B=-1) == 2 and call(N=-5) == 2
     assert call(N=1 << 22, d=128) == 2           # N*d*4 bytes >= 2^31

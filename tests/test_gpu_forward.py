@@ -127,3 +127,16 @@ def test_rejected_call_writes_nothing():
     assert st == 5
     torch.cuda.synchronize()
     assert bool((o == 7.0).all()) and bool((lse == 7.0).all())
+
+
+# Head dim 256: its own configuration (4 waves x 32 rows, O in AGPRs, 32 KB K/V tiles).
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 128, 129, 300, 1000])
+def test_head_dim_256_ragged(N, causal):
+    check_forward(8000 + N, 1, 2, 1, N, 256, causal)
+
+
+def test_head_dim_256_gqa_and_long():
+    check_forward(8100, 2, 8, 2, 777, 256, True)
+    check_forward(8101, 1, 4, 4, 4096, 256, True, sample=256)
+    check_forward(8102, 1, 4, 2, 2048, 256, False, scale=-0.05)
