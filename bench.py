@@ -106,7 +106,8 @@ def extra_workloads(fa2, seedgen, dev, stream, steps):
     cases = [("window_W1024_B2_H32_N8192_d128", 2, 32, 32, 8192, 128, True, 1024, True, 0x5EED0006),
              ("fwd_B4_H16_N2048_d64", 4, 16, 16, 2048, 64, False, None, False, 0x5EED0002),
              ("fwd_B1_Hq32_Hkv8_N32768_d128_causal", 1, 32, 8, 32768, 128, True, None, False, 0x5EED0004),
-             ("fwdbwd_B4_H16_N4096_d128_causal", 4, 16, 16, 4096, 128, True, None, True, 0x5EED0005)]
+             ("fwdbwd_B4_H16_N4096_d128_causal", 4, 16, 16, 4096, 128, True, None, True, 0x5EED0005),
+             ("fwdbwd_B2_H16_N8192_d256_causal", 2, 16, 16, 8192, 256, True, None, True, 0x5EED0008)]
     for name, B, Hq, Hkv, N, d, causal, W, with_bwd, seed in cases:
         if with_bwd:
             q, k, v, dO = seedgen.attention_inputs(seed, B, Hq, Hkv, N, d, with_do=True)

@@ -158,7 +158,7 @@ int backward_impl(const void* q, const void* k, const void* v, const float* o, c
                   int d, int causal, int window, float scale, void* workspace,
                   size_t workspace_bytes, hipStream_t stream) {
   bool empty = false;
-  int st = check_shape(B, Hq, Hkv, N, d, scale, &empty);
+  int st = check_shape(B, Hq, Hkv, N, d, scale, &empty, DIMS_64_128_256);
   if (st != FA2_OK || empty) return st;
   const uint64_t rq = (uint64_t)B * Hq * N, rkv = (uint64_t)B * Hkv * N;
   const Buf in[6] = {{q, rq * d * 2}, {k, rkv * d * 2}, {v, rkv * d * 2},
@@ -241,7 +241,7 @@ int fa2_backward_preprocess(const float* o, const void* dO, const float* lse, vo
                             size_t workspace_bytes, int B, int Hq, int N, int d,
                             hipStream_t stream) {
   bool empty = false;
-  int st = check_shape(B, Hq, 1, N, d, 1.0f, &empty);
+  int st = check_shape(B, Hq, 1, N, d, 1.0f, &empty, DIMS_64_128_256);
   if (st != FA2_OK || empty) return st;
   const uint64_t rq = (uint64_t)B * Hq * N;
   const Buf in[3] = {{o, rq * d * 4}, {dO, rq * d * 2}, {lse, rq * 4}};
@@ -261,7 +261,7 @@ int fa2_backward_dkdv(const void* q, const void* k, const void* v, const void* d
                       int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                       hipStream_t stream) {
   bool empty = false;
-  int st = check_shape(B, Hq, Hkv, N, d, scale, &empty);
+  int st = check_shape(B, Hq, Hkv, N, d, scale, &empty, DIMS_64_128_256);
   if (st != FA2_OK || empty) return st;
   st = check_workspace(workspace, workspace_bytes, B, Hq, N);
   if (st != FA2_OK) return st;
@@ -279,7 +279,7 @@ int fa2_backward_dq(const void* q, const void* k, const void* v, const void* dO,
                     const void* workspace, size_t workspace_bytes, float* dq, int B, int Hq,
                     int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
   bool empty = false;
-  int st = check_shape(B, Hq, Hkv, N, d, scale, &empty);
+  int st = check_shape(B, Hq, Hkv, N, d, scale, &empty, DIMS_64_128_256);
   if (st != FA2_OK || empty) return st;
   st = check_workspace(workspace, workspace_bytes, B, Hq, N);
   if (st != FA2_OK) return st;

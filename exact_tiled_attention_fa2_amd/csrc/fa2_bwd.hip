@@ -49,22 +49,26 @@ struct BwdCfg {
   static constexpr int RPW = 32;            // rows (keys or queries) each wave owns
   static constexpr int BR = WAVES * RPW;    // rows per workgroup
   static constexpr int BT = 64;             // rows per streamed tile
-  static constexpr int KS = D / 16;
-  static constexpr int DB = D / 32;
-  static constexpr int CH = D / 8;
-  static constexpr int RP = 16 / CH;
+  static constexpr int KS = D / 16;         // k-steps of a contraction over the head dim
+  // dK/dV accumulate up to 128 head-dim columns per pass (32 fp32 registers per column block
+  // and wave); d = 256 takes two passes (NDH), each recomputing S and dP over the full d.
+  static constexpr int DB = (D <= 128 ? D : 128) / 32;
+  static constexpr int NDH = D / (DB * 32);
   static constexpr int ROWB = D * 2;
   static constexpr int TILE = BT * ROWB;
   static constexpr int LPW = TILE / 1024 / WAVES;
+  static constexpr int RO = KS < 8 ? KS : 8;  // distinct row-read offsets (chunks 16+ add 256 B)
 };
 
 // One swizzle for tiles read both as 16-byte rows (16 consecutive rows, one chunk) and by
 // transposing reads (4 consecutive rows x 4 consecutive chunks per half-wave): chunk c of
-// row r sits at c ^ swz(r); both access patterns then cover all 16 LDS bank groups.
+// row r sits at c ^ swz(r); both access patterns then cover all 16 LDS bank groups. It only
+// permutes the low four bits of the chunk index.
 template <int D>
 __device__ __forceinline__ int swz_dual(int r) {
-  constexpr int CH = D / 8, RP = 16 / CH, Q4 = CH / 4;
-  const int i = r / RP;
+  using S = SwzCfg<D>;
+  constexpr int Q4 = S::SWZ_SPAN / 4;
+  const int i = r / S::SWZ_ROWS;
   return ((i % Q4) << 2) | ((i / Q4) & 3);
 }
 
@@ -189,8 +193,10 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
   const int hf = lane >> 5, l32 = lane & 31;
   agpr_accumulators_hint();
   const int N = p.N;
-  int bg, kblk;  // causal: low key blocks see the most queries and go first
-  map_slice_block(blockIdx.x, p.B * p.Hkv, p.nblk, bg, kblk);
+  int bg, kblk, dh;  // causal: low key blocks see the most queries and go first
+  map_slice_block(blockIdx.x, p.B * p.Hkv, p.nblk * C::NDH, bg, kblk);
+  dh = kblk % C::NDH;  // which 128-column half of dK/dV this workgroup accumulates (d = 256)
+  kblk /= C::NDH;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int G = p.Hq / p.Hkv;
   const int k0 = kblk * C::BR;
@@ -247,14 +253,17 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
       vf[ks] = buffer_load16(rv, off);
     }
   }
-  int roff[C::KS], toff[C::DB], toff8[C::DB];
+  int roff[C::RO], toff[C::DB], toff8[C::DB];
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) roff[ks] = row_read_off<D>(lane, ks);
+  for (int ks = 0; ks < C::RO; ++ks) roff[ks] = row_read_off<D>(lane, ks);
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) {
-    toff[db] = tr_read_off<D>(lane, db, 0);
-    toff8[db] = tr_read_off<D>(lane, db, 1);
+    toff[db] = tr_read_off<D>(lane, dh * C::DB + db, 0);
+    toff8[db] = tr_read_off<D>(lane, dh * C::DB + db, 1);
   }
+  // Row-read offset of k-step ks: the swizzle leaves chunk bit 4 alone, so k-steps 8.. repeat
+  // those of 0.. shifted by 16 chunks.
+  auto rowoff = [&](int ks) { return roff[ks % C::RO] + (ks / C::RO) * 256; };
 
   f32x16 adk[C::DB], adv[C::DB];  // dK^T, dV^T: rows = head dim, columns = keys (lanes)
 #pragma unroll
@@ -284,9 +293,10 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
   constexpr int PF = 3;                // operand reads in flight ahead of the MFMA using them
   constexpr int DL = 2;                // steps between an accumulator's last MFMA and its use
   constexpr int EXP_RATE = 16 / KS;    // P elements per step
-  constexpr int DS_RATE = 8 / KS;      // dS element pairs per step
+  constexpr int DS_STEPS = KS < 8 ? KS : 8;  // steps per row block's dS
+  constexpr int DS_RATE = 8 / DS_STEPS;      // dS element pairs per step
   auto exp_start = [](int mb) { return KS + DL + KS * mb; };      // KS steps per row block
-  auto ds_start = [](int mb) { return 3 * KS + DL + KS * mb; };   // KS steps per row block
+  auto ds_start = [](int mb) { return 3 * KS + DL + KS * mb; };
   auto tile = [&](const DkdvStage<D>& st, int qrow0, bool fix) __attribute__((always_inline)) {
     f32x16 s[2], dp[2];
 #pragma unroll
@@ -344,8 +354,8 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
     };
     auto read_op = [&](auto J) __attribute__((always_inline)) -> u32x4 {
       constexpr int j = decltype(J)::value;
-      if constexpr (j < 2 * KS) return lds_read16(st.q + roff[j % KS] + (j / KS) * 32 * C::ROWB);
-      else if constexpr (j < 4 * KS) return lds_read16(st.dO + roff[j % KS] + ((j - 2 * KS) / KS) * 32 * C::ROWB);
+      if constexpr (j < 2 * KS) return lds_read16(st.q + rowoff(j % KS) + (j / KS) * 32 * C::ROWB);
+      else if constexpr (j < 4 * KS) return lds_read16(st.dO + rowoff(j % KS) + ((j - 2 * KS) / KS) * 32 * C::ROWB);
       else if constexpr (j < 4 * KS + 4 * DB) return trread(st.dO, j - 4 * KS);
       else return trread(st.q, j - 4 * KS - 4 * DB);
     };
@@ -381,7 +391,7 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
           }
         }
         constexpr int u = j - ds_start(mb);
-        if constexpr (u >= 0 && u < KS) ds_part(mb, u * DS_RATE, (u + 1) * DS_RATE);
+        if constexpr (u >= 0 && u < DS_STEPS) ds_part(mb, u * DS_RATE, (u + 1) * DS_RATE);
       });
     };
     u32x4 ring[PF + 1];
@@ -421,10 +431,10 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
   }
   if (it < iters) step(P0{}, it);
 
-  // ---- store dK = scale dK^T^T, dV: lane = key, registers = head dim ----
+  // ---- store dK = scale dK^T^T, dV: lane = key, registers = head dim (this pass's columns) ----
   if (key < N) {
-    float* dkrow = p.dk + kvoff + (size_t)key * D;
-    float* dvrow = p.dv + kvoff + (size_t)key * D;
+    float* dkrow = p.dk + kvoff + (size_t)key * D + dh * C::DB * 32;
+    float* dvrow = p.dv + kvoff + (size_t)key * D + dh * C::DB * 32;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -443,10 +453,17 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
 template <int D>
 struct DqCfg {
   static constexpr int WAVES = 4;           // one wave per SIMD
-  static constexpr int RPW = 64;            // query rows per wave: two 32-row blocks qb
+  // Query rows per wave: two 32-row blocks qb up to d = 128 (each K/V fragment read feeds two
+  // MFMAs); at d = 256 the Q and dO operands of one block already take 128 registers.
+  static constexpr int NQB = D <= 128 ? 2 : 1;
+  static constexpr int RPW = 32 * NQB;
   static constexpr int BR = WAVES * RPW;    // query rows per workgroup
   static constexpr int BT = 64;             // keys per streamed tile: two 32-key halves
   static constexpr int TILE = BT * D * 2;
+  static constexpr int DB = D / 32;         // dQ accumulator blocks (the whole head dim)
+  // K/V ring: three stages (one barrier per tile) when three fit in LDS, else two stages
+  // with a second barrier per tile before a stage is refilled.
+  static constexpr int STAGES = D <= 128 ? 3 : 2;
 };
 
 template <int D>
@@ -455,14 +472,15 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   using C = BwdCfg<D>;
   using Q = DqCfg<D>;
   static_assert(Q::WAVES == C::WAVES && Q::BT == C::BT, "tiles are loaded by load_tile_dual");
-  constexpr int KS = C::KS, DB = C::DB;
-  // Three stages of K and V, in separate arrays (a DMA into one never aliases reads of another).
+  constexpr int KS = C::KS, DB = Q::DB, NQB = Q::NQB;
+  // K and V stages in separate arrays (a DMA into one never aliases reads of another).
+  constexpr int TILE3 = Q::STAGES == 3 ? Q::TILE : 1024;
   __shared__ __attribute__((aligned(1024))) char k_st0[Q::TILE];
   __shared__ __attribute__((aligned(1024))) char k_st1[Q::TILE];
-  __shared__ __attribute__((aligned(1024))) char k_st2[Q::TILE];
+  __shared__ __attribute__((aligned(1024))) char k_st2[TILE3];
   __shared__ __attribute__((aligned(1024))) char v_st0[Q::TILE];
   __shared__ __attribute__((aligned(1024))) char v_st1[Q::TILE];
-  __shared__ __attribute__((aligned(1024))) char v_st2[Q::TILE];
+  __shared__ __attribute__((aligned(1024))) char v_st2[TILE3];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -515,14 +533,14 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   fetch(I0{}, 0);
   fetch(I1{}, 1);
 
-  // Q and dO of this wave's 64 queries as B operands (lane = query, k = head dim).
-  u32x4 qf[2][KS], df[2][KS];
-  float lse2v[2], dltv[2];
+  // Q and dO of this wave's queries as B operands (lane = query, k = head dim).
+  u32x4 qf[NQB][KS], df[NQB][KS];
+  float lse2v[NQB], dltv[NQB];
   {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + qoff, head_bytes);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dO + qoff, head_bytes);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
       const int qi = qw + 32 * qb + l32;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -535,18 +553,20 @@ void fa2_bwd_dq_kernel(BwdParams p) {
     }
   }
 
-  int roff[KS], toff[DB], toff8[DB];
+  int roff[C::RO], toff[DB], toff8[DB];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) roff[ks] = row_read_off<D>(lane, ks);
+  for (int ks = 0; ks < C::RO; ++ks) roff[ks] = row_read_off<D>(lane, ks);
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     toff[db] = tr_read_off<D>(lane, db, 0);
     toff8[db] = tr_read_off<D>(lane, db, 1);
   }
+  // Row-read offset of k-step ks (k-steps 8.. repeat 0.. shifted by 16 chunks).
+  auto rowoff = [&](int ks) { return roff[ks % C::RO] + (ks / C::RO) * 256; };
 
-  f32x16 adq[2][DB];  // dQ^T per row block: rows = head dim, columns = queries (lanes)
+  f32x16 adq[NQB][DB];  // dQ^T per row block: rows = head dim, columns = queries (lanes)
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
     for (int db = 0; db < DB; ++db) adq[qb][db] = f32x16{};
   const float c = p.c;
@@ -557,21 +577,24 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   // The work is software-pipelined across halves. Step u runs S(u+1) MFMAs beside dS(u),
   // then dQ(u) MFMAs beside P(u+1), then dP(u+1) MFMAs beside the rest of P(u+1).
   // Each step reads one A operand (shared by both row blocks) PF steps ahead.
-  f32x16 s[2], dp[2];
-  float pf[2][16];      // P^T of the half in flight, fp32
-  u32x4 pd[2][2];       // dS^T as B operands [qb][h]: 16 keys x 32 queries, packed bf16
+  f32x16 s[NQB], dp[NQB];
+  float pf[NQB][16];      // P^T of the half in flight, fp32
+  u32x4 pd[NQB][2];       // dS^T as B operands [qb][h]: 16 keys x 32 queries, packed bf16
   constexpr int NST = 2 * KS + 2 * DB;  // steps per half
   constexpr int PF = 3;
   constexpr int DL = 2;                 // steps between an accumulator's last MFMA and its use
+  constexpr int NEL = 16 * NQB;         // P elements per lane and half
   constexpr int EXP0 = KS + DL, EXPN = NST - EXP0;  // steps carrying P(u+1)
+  constexpr int DS_STEPS = KS < NEL / 2 ? KS : NEL / 2;  // steps carrying dS(u)
+  constexpr int DS_RATE = NEL / 2 / DS_STEPS;            // dS element pairs per step
 
   auto exp_el = [&](int e) __attribute__((always_inline)) {
     const int qb = e >> 4, rr = e & 15;
     pf[qb][rr] = fast_exp2(__builtin_fmaf(s[qb][rr], c, -lse2v[qb]));
   };
-  // dS elements in h-major order, so pd[.][0] is complete before pd[.][1].
-  auto ds_pair = [&](int e) __attribute__((always_inline)) {
-    const int h = e >> 4, qb = (e >> 3) & 1, rr = 8 * h + (e & 7);
+  // dS element pairs q in h-major order, so pd[.][0] is complete before pd[.][1].
+  auto ds_pair = [&](int q) __attribute__((always_inline)) {
+    const int h = q / (4 * NQB), qb = (q / 4) % NQB, rr = 8 * h + 2 * (q % 4);
     const float a = pf[qb][rr] * (dp[qb][rr] - dltv[qb]);
     const float bb = pf[qb][rr + 1] * (dp[qb][rr + 1] - dltv[qb]);
     pd[qb][h][(rr >> 1) & 3] = pack_bf16(a, bb);
@@ -580,7 +603,7 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   // crossing this wave's diagonal or its window's start.
   auto causal_fixup = [&](int ua) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
       const int lim = qw + 32 * qb + l32 - 32 * ua - 4 * hf;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
@@ -600,18 +623,18 @@ void fa2_bwd_dq_kernel(BwdParams p) {
     auto read_op = [&](auto J) __attribute__((always_inline)) -> u32x4 {
       constexpr int j = decltype(J)::value;
       if constexpr (j < KS) {
-        return lds_read16(kn + roff[j]);
+        return lds_read16(kn + rowoff(j));
       } else if constexpr (j < KS + 2 * DB) {
         constexpr int i = j - KS, db = i % DB, h = i / DB;
         return tr_pair(kc + toff[db] + 16 * h * C::ROWB, kc + toff8[db] + 16 * h * C::ROWB);
       } else {
-        return lds_read16(vn + roff[j - KS - 2 * DB]);
+        return lds_read16(vn + rowoff(j - KS - 2 * DB));
       }
     };
     auto mfma_step = [&](auto J, u32x4 a) __attribute__((always_inline)) {
       constexpr int j = decltype(J)::value;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < NQB; ++qb) {
         // S(u+1) and dP(u+1) start from zero; dP(u) stays live until dS(u) is done.
         if constexpr (j < KS) {
           s[qb] = mfma32x32x16(a, qf[qb][j], j == 0 ? f32x16{} : s[qb]);
@@ -629,13 +652,12 @@ void fa2_bwd_dq_kernel(BwdParams p) {
       if constexpr (j == 0) {
         if (fix) causal_fixup(ua);
       }
-      if constexpr (j >= DL && j < DL + KS) {
-        constexpr int per = 16 / KS;  // element pairs per step
+      if constexpr (j >= DL && j < DL + DS_STEPS) {
 #pragma unroll
-        for (int e = (j - DL) * per; e < (j - DL + 1) * per; ++e) ds_pair(2 * e);
+        for (int q = (j - DL) * DS_RATE; q < (j - DL + 1) * DS_RATE; ++q) ds_pair(q);
       }
       if constexpr (j >= EXP0) {
-        constexpr int e0 = (32 * (j - EXP0)) / EXPN, e1 = (32 * (j - EXP0 + 1)) / EXPN;
+        constexpr int e0 = (NEL * (j - EXP0)) / EXPN, e1 = (NEL * (j - EXP0 + 1)) / EXPN;
 #pragma unroll
         for (int e = e0; e < e1; ++e) exp_el(e);
       }
@@ -657,22 +679,22 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   // Prologue: S(0), dP(0) and P(0) from the first half of tile 0.
   if (my_last >= 0) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
       s[qb] = f32x16{};
       dp[qb] = f32x16{};
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const u32x4 ka = lds_read16((const lds_char*)k_st0 + roff[ks]);
-      const u32x4 va = lds_read16((const lds_char*)v_st0 + roff[ks]);
+      const u32x4 ka = lds_read16((const lds_char*)k_st0 + rowoff(ks));
+      const u32x4 va = lds_read16((const lds_char*)v_st0 + rowoff(ks));
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < NQB; ++qb) {
         s[qb] = mfma32x32x16(ka, qf[qb][ks], s[qb]);
         dp[qb] = mfma32x32x16(va, df[qb][ks], dp[qb]);
       }
     }
 #pragma unroll
-    for (int e = 0; e < 32; ++e) exp_el(e);
+    for (int e = 0; e < NEL; ++e) exp_el(e);
   }
 
   // Tile T: half 2T, then (all waves past their reads of tile T-1, tile T+1 landed) the DMA of
@@ -687,17 +709,37 @@ void fa2_bwd_dq_kernel(BwdParams p) {
     fetch(SN2{}, T + 2);
     if (2 * T + 1 <= my_last) half(S, I1{}, SN{}, I0{}, 2 * T + 1);
   };
+  // Two stages: tile T in stage T % 2 and T+1 in the other; half 2T+1 reads both, so the DMA
+  // of tile T+2 into T's stage waits for a barrier after it.
+  auto tile_iter2 = [&](auto S, int T) __attribute__((always_inline)) {
+    constexpr int st = decltype(S)::value;
+    using SN = std::integral_constant<int, st ^ 1>;
+    if (2 * T <= my_last) half(S, I0{}, S, I1{}, 2 * T);
+    wait_vmem_all();
+    __syncthreads();
+    if (2 * T + 1 <= my_last) half(S, I1{}, SN{}, I0{}, 2 * T + 1);
+    __syncthreads();
+    fetch(S, T + 2);
+  };
   int T = 0;
-  for (; T + 3 <= ntiles; T += 3) {
-    tile_iter(I0{}, T);
-    tile_iter(I1{}, T + 1);
-    tile_iter(I2{}, T + 2);
+  if constexpr (Q::STAGES == 3) {
+    for (; T + 3 <= ntiles; T += 3) {
+      tile_iter(I0{}, T);
+      tile_iter(I1{}, T + 1);
+      tile_iter(I2{}, T + 2);
+    }
+    if (T < ntiles) tile_iter(I0{}, T);
+    if (T + 1 < ntiles) tile_iter(I1{}, T + 1);
+  } else {
+    for (; T + 2 <= ntiles; T += 2) {
+      tile_iter2(I0{}, T);
+      tile_iter2(I1{}, T + 1);
+    }
+    if (T < ntiles) tile_iter2(I0{}, T);
   }
-  if (T < ntiles) tile_iter(I0{}, T);
-  if (T + 1 < ntiles) tile_iter(I1{}, T + 1);
 
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < NQB; ++qb) {
     const int qi = qw + 32 * qb + l32;
     if (qi < N) {
       float* dqrow = p.dq + qoff + (size_t)qi * D;
@@ -745,6 +787,8 @@ hipError_t launch_bwd_preprocess(const float* o, const void* dO, const float* ls
   float* lse2 = ws + rows;
   if (s.d == 128)
     hipLaunchKernelGGL(fa2_bwd_pre_kernel<128>, grid, block, 0, stream, o, (const uint16_t*)dO, lse, ws, lse2, rows);
+  else if (s.d == 256)
+    hipLaunchKernelGGL(fa2_bwd_pre_kernel<256>, grid, block, 0, stream, o, (const uint16_t*)dO, lse, ws, lse2, rows);
   else
     hipLaunchKernelGGL(fa2_bwd_pre_kernel<64>, grid, block, 0, stream, o, (const uint16_t*)dO, lse, ws, lse2, rows);
   return hipGetLastError();
@@ -757,9 +801,12 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
   p.dk = dk;
   p.dv = dv;
   p.nblk = (s.N + BwdCfg<128>::BR - 1) / BwdCfg<128>::BR;
-  const dim3 grid((unsigned)(s.B * s.Hkv * p.nblk)), block(BwdCfg<128>::WAVES * 64);
+  const int ndh = s.d == 256 ? BwdCfg<256>::NDH : 1;
+  const dim3 grid((unsigned)(s.B * s.Hkv * p.nblk * ndh)), block(BwdCfg<128>::WAVES * 64);
   if (s.d == 128)
     hipLaunchKernelGGL(fa2_bwd_dkdv_kernel<128>, grid, block, 0, stream, p);
+  else if (s.d == 256)
+    hipLaunchKernelGGL(fa2_bwd_dkdv_kernel<256>, grid, block, 0, stream, p);
   else
     hipLaunchKernelGGL(fa2_bwd_dkdv_kernel<64>, grid, block, 0, stream, p);
   return hipGetLastError();
@@ -769,10 +816,13 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
                          const float* ws, float* dq, const AttnShape& s, hipStream_t stream) {
   BwdParams p = make_params(q, k, v, dO, const_cast<float*>(ws), s);
   p.dq = dq;
-  p.nblk = (s.N + DqCfg<128>::BR - 1) / DqCfg<128>::BR;
+  const int BR = s.d == 256 ? DqCfg<256>::BR : DqCfg<128>::BR;
+  p.nblk = (s.N + BR - 1) / BR;
   const dim3 grid((unsigned)(s.B * s.Hq * p.nblk)), block(DqCfg<128>::WAVES * 64);
   if (s.d == 128)
     hipLaunchKernelGGL(fa2_bwd_dq_kernel<128>, grid, block, 0, stream, p);
+  else if (s.d == 256)
+    hipLaunchKernelGGL(fa2_bwd_dq_kernel<256>, grid, block, 0, stream, p);
   else
     hipLaunchKernelGGL(fa2_bwd_dq_kernel<64>, grid, block, 0, stream, p);
   return hipGetLastError();

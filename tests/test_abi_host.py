@@ -71,12 +71,9 @@ def bwd(**kw):
 @pytest.mark.parametrize("call", [fwd, bwd])
 def test_validation_codes(lib, call):
     assert call(d=96) == 3 and call(d=192) == 3 and call(d=32) == 3
-    # d = 256: supported by the forward (checked here only together with another invalid
-    # argument, so nothing is ever launched on these fake addresses), rejected by the backward.
-    if call is fwd:
-        assert call(d=256, scale=0.0) == 5 and call(d=256, q=P(0) + 8) == 6
-    else:
-        assert call(d=256) == 3
+    # d = 256 is supported; checked here only together with another invalid argument, so
+    # nothing is ever launched on these fake addresses.
+    assert call(d=256, scale=0.0) == 5 and call(d=256, q=P(0) + 8) == 6
     assert call(Hq=3, Hkv=2) == 4 and call(Hkv=0) == 4 and call(Hq=0) == 4
     assert call(B=-1) == 2 and call(N=-5) == 2
     assert call(N=1 << 22, d=128) == 2           # N*d*4 bytes >= 2^31
@@ -121,6 +118,9 @@ def test_phase_entry_points_validate(lib):
     assert fa2.fa2_backward_dq(*args, P(9), 1, 2, 1, 64, 64, 1, 0.1) == 7   # dq over the workspace
     assert fa2.fa2_backward_dq(*args, P(6) + 4, 1, 2, 1, 64, 64, 1, 0.1) == 6
     assert fa2.fa2_backward_dq(*args, P(6), 1, 2, 1, 64, 32, 1, 0.1) == 3
+    assert fa2.fa2_backward_dq(*args, P(6), 1, 2, 1, 64, 192, 1, 0.1) == 3
+    assert fa2.fa2_backward_dkdv(*args, P(7), P(8), 1, 2, 1, 64, 256, 1, 0.0) == 5   # d=256 accepted
+    assert pre(d=192) == 3
 
 
 def fwdw(**kw):
@@ -162,7 +162,7 @@ def dec(**kw):
 
 
 def test_decode_validation(lib):
-    assert dec(d=96) == 3 and dec(Hq=6, Hkv=4) == 4 and dec(scale=float("nan")) == 5
+    assert dec(d=256) == 3 and dec(d=96) == 3 and dec(Hq=6, Hkv=4) == 4 and dec(scale=float("nan")) == 5
     assert dec(Nk=0) == 2 and dec(Nq=8, Nk=7) == 2 and dec(Nq=-1) == 2
     assert dec(q=None) == 1 and dec(k=P(1) + 4) == 6 and dec(o=P(1)) == 7
     assert dec(Nq=0) == 0 and dec(B=0) == 0

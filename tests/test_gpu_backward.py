@@ -126,3 +126,17 @@ def test_phases_match_composed_backward():
     assert fa2.fa2_backward_dq(qd, kd, vd, dod, ws, W, dq2, B, Hq, Hkv, N, d, True, 0.09) == 0
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
+# Head dim 256: dK/dV in two passes over head-dim halves, dQ with one 32-row block per wave and
+# a two-stage K/V ring.
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 129, 257, 500])
+def test_head_dim_256_ragged(N, causal):
+    check_backward(9000 + N, 1, 2, 1, N, 256, causal)
+
+
+def test_head_dim_256_gqa_long_scale():
+    check_backward(9100, 2, 8, 2, 400, 256, True)
+    check_backward(9101, 1, 4, 4, 2048, 256, True, sample=256)
+    check_backward(9102, 1, 4, 2, 300, 256, False, scale=-0.06)

@@ -65,6 +65,11 @@ def test_window_ragged_lengths(N):
     check_window(6200 + N, 1, 2, 1, N, 64, 200)
 
 
+def test_window_head_dim_256():
+    check_window(6800, 1, 4, 2, 700, 256, 100)
+    check_window(6801, 1, 2, 1, 333, 256, 0)
+
+
 @pytest.mark.parametrize("Hkv", [1, 2, 8])
 def test_window_gqa(Hkv):
     check_window(6300 + Hkv, 2, 8, Hkv, 600, 128, 120)
