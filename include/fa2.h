@@ -21,10 +21,13 @@
  *     lse is the natural-log logsumexp of the scaled scores of each query row.
  *   - Grouped-query attention: query head hq reads key/value head hq / (Hq / Hkv).
  *   - causal != 0: query row i attends to key rows j <= i (square, top-left aligned).
- *   - d must be 64 or 128. Other head dims are rejected with FA2_ERR_UNSUPPORTED_HEAD_DIM
- *     (the pages treat an unsupported head dimension as a reported error, not a silent
- *     fallback: "Flash Attention 2: attivarla (llama.cpp, Ollama, vLLM)", qualellm.it,
- *     section "Risoluzione dei problemi", item "Errore unsupported head dimension").
+ *   - d must be 64, 128 or 256 (fa2_decode: 64 or 128); FlashAttention-2 handles head dims up
+ *     to 256 ("Flash Attention spiegata: una guida completa", section "Supporto per dimensioni di
+ *     testa maggiori").
+ *     Other head dims (96, 192, ...) are rejected with FA2_ERR_UNSUPPORTED_HEAD_DIM: the pages
+ *     treat an unsupported head dimension as a reported error, not a silent fallback ("Flash
+ *     Attention 2: attivarla (llama.cpp, Ollama, vLLM)", qualellm.it, section "Risoluzione dei
+ *     problemi", item "Errore unsupported head dimension").
  *   - scale must be finite and non-zero (negative values are accepted).
  *   - Every pointer must be 16-byte aligned; outputs must not overlap inputs or each other.
  *   - B == 0 or N == 0 is an empty problem: nothing is enqueued and FA2_OK is returned
@@ -52,7 +55,7 @@ typedef enum {
   FA2_OK = 0,
   FA2_ERR_NULL_POINTER = 1,         /* a required pointer is NULL (non-empty problem)      */
   FA2_ERR_BAD_SHAPE = 2,            /* negative size, or offsets overflow index arithmetic */
-  FA2_ERR_UNSUPPORTED_HEAD_DIM = 3, /* d not in {64, 128}                                  */
+  FA2_ERR_UNSUPPORTED_HEAD_DIM = 3, /* d not in {64, 128, 256} ({64, 128} for fa2_decode)   */
   FA2_ERR_BAD_GQA = 4,              /* Hq < 1, Hkv < 1 or Hq % Hkv != 0                    */
   FA2_ERR_BAD_SCALE = 5,            /* scale is NaN, infinite or zero                      */
   FA2_ERR_MISALIGNED = 6,           /* a pointer is not 16-byte aligned                    */
