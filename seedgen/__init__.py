@@ -49,6 +49,10 @@ def _load():
     lib.seedgen_normal_f64.argtypes = [u64, u64]
     lib.seedgen_normal_bf16.restype = ctypes.c_int
     lib.seedgen_normal_bf16.argtypes = [u64, u32, u64, u64, ctypes.c_void_p, ctypes.c_int]
+    lib.seedgen_f64_to_e4m3.restype = ctypes.c_uint8
+    lib.seedgen_f64_to_e4m3.argtypes = [ctypes.c_double]
+    lib.seedgen_normal_e4m3.restype = ctypes.c_int
+    lib.seedgen_normal_e4m3.argtypes = [u64, u32, u64, u64, ctypes.c_double, ctypes.c_void_p, ctypes.c_int]
     lib.seedgen_sample_rows.restype = ctypes.c_int
     lib.seedgen_sample_rows.argtypes = [u64, u64, i32, i32, ctypes.c_void_p]
     _lib = lib
@@ -102,6 +106,57 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def f64_to_e4m3(x: float) -> int:
+    """OCP FP8 E4M3FN code of x: round to nearest even, saturating to +-448 (seedgen.c)."""
+    return int(_load().seedgen_f64_to_e4m3(float(x)))
+
+
+def normal_e4m3(seed: int, tensor: str | int, shape, inv_scale: float, start: int = 0,
+                threads: int | None = None) -> np.ndarray:
+    """FP8 E4M3FN codes (uint8) of the seeded N(0,1) stream times ``inv_scale``; the values
+    they stand for are code_value * (1 / inv_scale)."""
+    t = TENSOR_IDS[tensor] if isinstance(tensor, str) else int(tensor)
+    shape = tuple(int(s) for s in shape)
+    count = int(np.prod(shape)) if shape else 1
+    out = np.empty(count, dtype=np.uint8)
+    if count:
+        _load().seedgen_normal_e4m3(seed & 0xFFFFFFFFFFFFFFFF, t, start, count, float(inv_scale),
+                                    out.ctypes.data, threads or host_threads())
+    return out.reshape(shape)
+
+
+def _e4m3_table() -> np.ndarray:
+    """Value of each of the 256 E4M3FN codes, from the format's definition (bias 7, subnormals
+    m/8 * 2^-6, 0x7F and 0xFF NaN)."""
+    t = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        sgn = -1.0 if code & 0x80 else 1.0
+        e, m = (code >> 3) & 15, code & 7
+        if e == 15 and m == 7:
+            t[code] = np.nan
+        elif e == 0:
+            t[code] = sgn * (m / 8.0) * 2.0 ** -6
+        else:
+            t[code] = sgn * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return t
+
+
+E4M3_VALUES = _e4m3_table()
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Exact fp64 values of FP8 E4M3FN codes."""
+    return E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]
+
+
+def fp8_attention_inputs(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int, scale: float = 1.0 / 32):
+    """Q [B,Hq,N,d], K/V [B,Hkv,N,d] as FP8 E4M3FN codes of the seeded N(0,1) streams divided by
+    ``scale`` (each tensor stands for codes * scale)."""
+    inv = 1.0 / scale
+    return (normal_e4m3(seed, "q", (B, Hq, N, d), inv), normal_e4m3(seed, "k", (B, Hkv, N, d), inv),
+            normal_e4m3(seed, "v", (B, Hkv, N, d), inv))
 
 
 def sample_rows(seed: int, slice_index: int, N: int, count: int) -> np.ndarray:

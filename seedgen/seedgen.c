@@ -84,6 +84,72 @@ int seedgen_normal_bf16(uint64_t seed, uint32_t tensor, uint64_t start, uint64_t
   return 0;
 }
 
+/*
+ * fp64 -> OCP FP8 E4M3FN bit pattern: sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * largest finite value 448, subnormals m/8 * 2^-6, no infinities (0x7F/0xFF are NaN). Round to
+ * nearest, ties to even, then saturate to +-448 (inputs are finite).
+ */
+uint8_t seedgen_f64_to_e4m3(double x) {
+  uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  double a = fabs(x);
+  if (a < 0.015625) { /* below 2^-6: subnormal step 2^-9; code 8 is the smallest normal */
+    double m = rint(a * 512.0);
+    return (uint8_t)(sign | (uint8_t)m);
+  }
+  int E;
+  double f = frexp(a, &E); /* a = f 2^E, f in [0.5, 1) */
+  int e = E - 1 + 7;       /* biased exponent of a = (2f) 2^(E-1) */
+  double m = rint((2.0 * f - 1.0) * 8.0);
+  if (m >= 8.0) {
+    m = 0.0;
+    e += 1;
+  }
+  int code = (e << 3) | (int)m;
+  if (code > 0x7E) code = 0x7E;
+  return (uint8_t)(sign | code);
+}
+
+typedef struct {
+  uint64_t key, start, count;
+  double inv_scale;
+  uint8_t* out;
+} fill8_job;
+
+static void* fill8_worker(void* p) {
+  fill8_job* j = (fill8_job*)p;
+  for (uint64_t i = 0; i < j->count; ++i)
+    j->out[i] = seedgen_f64_to_e4m3(seedgen_normal_f64(j->key, j->start + i) * j->inv_scale);
+  return NULL;
+}
+
+/* out[i] = e4m3(z_{start+i} * inv_scale): the same N(0,1) stream as seedgen_normal_bf16,
+   quantised to FP8 E4M3FN at scale 1 / inv_scale. */
+int seedgen_normal_e4m3(uint64_t seed, uint32_t tensor, uint64_t start, uint64_t count,
+                        double inv_scale, uint8_t* out, int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if (count < (uint64_t)nthreads * 65536) nthreads = 1;
+  uint64_t key = seedgen_stream_key(seed, tensor);
+  fill8_job jobs[256];
+  pthread_t th[256];
+  uint64_t per = count / (uint64_t)nthreads, rem = count % (uint64_t)nthreads, off = 0;
+  for (int t = 0; t < nthreads; ++t) {
+    uint64_t c = per + ((uint64_t)t < rem ? 1 : 0);
+    jobs[t].key = key; jobs[t].start = start + off; jobs[t].count = c;
+    jobs[t].inv_scale = inv_scale; jobs[t].out = out + off;
+    off += c;
+  }
+  if (nthreads == 1) { fill8_worker(&jobs[0]); return 0; }
+  int created[256];
+  for (int t = 0; t < nthreads; ++t) {
+    created[t] = pthread_create(&th[t], NULL, fill8_worker, &jobs[t]) == 0;
+    if (!created[t]) fill8_worker(&jobs[t]);
+  }
+  for (int t = 0; t < nthreads; ++t)
+    if (created[t]) pthread_join(th[t], NULL);
+  return 0;
+}
+
 static int cmp_i32(const void* a, const void* b) {
   int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
   return (x > y) - (x < y);

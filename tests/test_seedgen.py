@@ -87,3 +87,45 @@ def test_row_sample():
     assert np.array_equal(seedgen.sample_rows(1, 0, 100, 256), np.arange(100))
     allr = seedgen.sample_rows_all(1, 4, 300, 20)
     assert allr.shape == (4, 20)
+
+
+# ---------------------------------------------------------------- FP8 E4M3FN encoding
+
+def test_e4m3_decoder_anchor_values():
+    """Values fixed by the E4M3FN definition (bias 7, 3 mantissa bits, no infinities)."""
+    dec = seedgen.e4m3_to_f64
+    assert dec(np.array([0x38]))[0] == 1.0 and dec(np.array([0xB8]))[0] == -1.0
+    assert dec(np.array([0x7E]))[0] == 448.0 and dec(np.array([0x01]))[0] == 2.0 ** -9
+    assert dec(np.array([0x08]))[0] == 2.0 ** -6 and dec(np.array([0x07]))[0] == 7 * 2.0 ** -9
+    assert dec(np.array([0x3C]))[0] == 1.5 and dec(np.array([0x40]))[0] == 2.0
+    assert np.isnan(dec(np.array([0x7F]))[0]) and np.isnan(dec(np.array([0xFF]))[0])
+    finite = dec(np.arange(256, dtype=np.uint8))
+    pos = np.sort(finite[(finite > 0) & np.isfinite(finite)])
+    assert len(pos) == 126 and np.all(np.diff(pos) > 0)   # 126 distinct positive values
+
+
+def test_e4m3_encoder_round_trip_and_rne():
+    enc, vals = seedgen.f64_to_e4m3, seedgen.E4M3_VALUES
+    for code in range(256):
+        if code in (0x7F, 0xFF):
+            continue
+        assert enc(vals[code]) == code, hex(code)
+    pos = [(vals[c], c) for c in range(1, 0x7F)]
+    for (a, ca), (b, cb) in zip(pos, pos[1:]):
+        mid = (a + b) / 2
+        want = ca if ca % 2 == 0 else cb         # ties to the even code (even mantissa)
+        assert enc(mid) == want, (a, b)
+        assert enc(-mid) == want | 0x80
+        assert enc(mid * (1 - 1e-12)) == ca and enc(mid * (1 + 1e-12)) == cb
+    assert enc(1000.0) == 0x7E and enc(-1e30) == 0xFE and enc(449.0) == 0x7E   # saturation
+    assert enc(2.0 ** -10) == 0x00 and enc(2.0 ** -10 * 1.001) == 0x01          # below the smallest subnormal
+
+
+def test_e4m3_stream_matches_normals():
+    """The FP8 stream quantises the same N(0,1) values as the bf16 stream."""
+    codes = seedgen.normal_e4m3(11, "k", (4096,), 32.0)
+    bf = seedgen.bf16_bits_to_f64(seedgen.normal_bf16(11, "k", (4096,)))
+    vals = seedgen.e4m3_to_f64(codes) / 32.0
+    assert np.all(np.isfinite(vals))
+    # both are within their format's half-ulp of the same normal value
+    assert np.max(np.abs(vals - bf) / np.maximum(np.abs(bf), 2.0 ** -6 / 32)) < 2 ** -4 + 2 ** -8
