@@ -143,6 +143,25 @@ def extra_workloads(fa2, seedgen, dev, stream, steps):
         log("  extra %-38s %s" % (name, r))
         del q, k, v, dO, qd, kd, vd, dod, o, lse, dq, dk, dv, ws
         torch.cuda.empty_cache()
+    # FP8 forward at the headline shape (Q, K, V as E4M3FN codes, per-tensor scale 1/32).
+    B, Hq, Hkv, N, d = 2, 32, 32, 8192, 128
+    q8, k8, v8 = (torch.from_numpy(x).to(dev) for x in seedgen.fp8_attention_inputs(0x5EED0006, B, Hq, Hkv, N, d))
+    o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    wsb = fa2.fa2_forward_fp8_workspace_size(B, Hkv, N, d)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    sc = 1.0 / math.sqrt(d)
+    call = lambda: check(fa2.fa2_forward_fp8(q8, k8, v8, 1 / 32, 1 / 32, 1 / 32, o, lse, B, Hq, Hkv, N, d, True, sc,
+                                             ws, wsb, stream), "fa2_forward_fp8")
+    per, total = time_sequence([call], steps, 2, stream)
+    pairs = B * Hq * visible_pairs(N, True)
+    r = {"B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "causal": True, "fwd_ms": round(total, 4),
+         "fwd_tflops": round(pairs * 4 * d / (total * 1e-3) / 1e12, 1),
+         "note": "S = Q K^T on FP8 MFMA, P V in bf16 (V widened exactly); time includes the widening pass"}
+    out["fp8_fwd_B2_H32_N8192_d128_causal"] = r
+    log("  extra %-38s %s" % ("fp8_fwd_B2_H32_N8192_d128_causal", r))
+    del q8, k8, v8, o, lse, ws
+
     # Decode: one new token per sequence against a 32K-token cache (grouped-query heads). The
     # pass streams K and V once, so it is reported against HBM bandwidth.
     B, Hq, Hkv, Nq, Nk, d = 8, 32, 8, 1, 32768, 128

@@ -24,7 +24,8 @@ STATUS_NAMES = {
 }
 EXPORTED = ("fa2_forward", "fa2_backward", "fa2_backward_workspace_size", "fa2_backward_preprocess",
             "fa2_backward_dkdv", "fa2_backward_dq", "fa2_forward_window", "fa2_backward_window",
-            "fa2_decode_workspace_size", "fa2_decode", "fa2_status_string")
+            "fa2_decode_workspace_size", "fa2_decode", "fa2_forward_fp8_workspace_size", "fa2_forward_fp8",
+            "fa2_status_string")
 
 _lib = None
 
@@ -65,6 +66,10 @@ def load() -> ctypes.CDLL:
     lib.fa2_decode_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.fa2_decode.restype = i
     lib.fa2_decode.argtypes = [p, p, p, p, p, i, i, i, i, i, i, i, f, p, z, p]
+    lib.fa2_forward_fp8_workspace_size.restype = z
+    lib.fa2_forward_fp8_workspace_size.argtypes = [i, i, i, i]
+    lib.fa2_forward_fp8.restype = i
+    lib.fa2_forward_fp8.argtypes = [p, p, p, f, f, f, p, p, i, i, i, i, i, i, f, p, z, p]
     lib.fa2_status_string.restype = ctypes.c_char_p
     lib.fa2_status_string.argtypes = [i]
     _lib = lib
@@ -147,6 +152,17 @@ def fa2_decode(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, workspace,
                              _stream(stream))
 
 
+def fa2_forward_fp8_workspace_size(B, Hkv, N, d) -> int:
+    return int(load().fa2_forward_fp8_workspace_size(B, Hkv, N, d))
+
+
+def fa2_forward_fp8(q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, d, causal, scale,
+                    workspace, workspace_bytes, stream=None) -> int:
+    return load().fa2_forward_fp8(_ptr(q), _ptr(k), _ptr(v), float(q_scale), float(k_scale), float(v_scale),
+                                  _ptr(o), _ptr(lse), B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
+                                  _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
 def fa2_status_string(status: int) -> str:
     return load().fa2_status_string(int(status)).decode()
 
@@ -218,4 +234,22 @@ def decode(q, k, v, causal: bool, scale: float, stream=None, workspace=None):
     st = fa2_decode(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, workspace, wbytes, stream)
     if st != FA2_OK:
         raise Fa2Error(st, "fa2_decode")
+    return o, lse
+
+
+def forward_fp8(q8, k8, v8, scales, causal: bool, scale: float, stream=None, workspace=None):
+    """O, LSE (fp32) of attention over FP8 E4M3FN codes (uint8 device tensors q8 [B,Hq,N,d],
+    k8/v8 [B,Hkv,N,d]) standing for codes * (q_scale, k_scale, v_scale) = ``scales``."""
+    import torch
+    B, Hq, N, d = q8.shape
+    Hkv = k8.shape[1]
+    o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q8.device)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device)
+    need = fa2_forward_fp8_workspace_size(B, Hkv, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q8.device)
+    st = fa2_forward_fp8(q8, k8, v8, *scales, o, lse, B, Hq, Hkv, N, d, causal, scale, workspace,
+                         workspace.numel() * workspace.element_size(), stream)
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_forward_fp8")
     return o, lse

@@ -201,6 +201,40 @@ int fa2_backward_window(const void* q, const void* k, const void* v, const float
                        workspace, workspace_bytes, stream);
 }
 
+size_t fa2_forward_fp8_workspace_size(int B, int Hkv, int N, int d) {
+  if (B <= 0 || Hkv <= 0 || N <= 0 || d != 128) return 0;
+  fa2::AttnShape s{B, Hkv, Hkv, N, d, 0, 1.0f};
+  return fa2::forward_fp8_workspace_bytes(s);
+}
+
+int fa2_forward_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale,
+                    float v_scale, float* o, float* lse, int B, int Hq, int Hkv, int N, int d,
+                    int causal, float scale, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  if (B < 0 || N < 0 || Hq < 0 || Hkv < 0) return FA2_ERR_BAD_SHAPE;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return FA2_ERR_BAD_GQA;
+  if (d != 128) return FA2_ERR_UNSUPPORTED_HEAD_DIM;
+  if (!isfinite(scale) || scale == 0.0f) return FA2_ERR_BAD_SCALE;
+  for (float f : {q_scale, k_scale, v_scale})
+    if (!isfinite(f) || !(f > 0.0f)) return FA2_ERR_BAD_SCALE;
+  bool empty = false;
+  int st = check_shape(B, Hq, Hkv, N, d, scale, &empty);
+  if (st != FA2_OK || empty) return st;
+  const uint64_t rq = (uint64_t)B * Hq * N, rkv = (uint64_t)B * Hkv * N;
+  const Buf in[3] = {{q, rq * d}, {k, rkv * d}, {v, rkv * d}};
+  const Buf out[2] = {{o, rq * d * 4}, {lse, rq * 4}};
+  st = check_buffers(in, 3, out, 2);
+  if (st != FA2_OK) return st;
+  const size_t need = fa2_forward_fp8_workspace_size(B, Hkv, N, d);
+  if (!workspace || workspace_bytes < need) return FA2_ERR_WORKSPACE;
+  const Buf all[5] = {in[0], in[1], in[2], out[0], out[1]};
+  const Buf ws[1] = {{workspace, need}};
+  st = check_buffers(all, 5, ws, 1);
+  if (st != FA2_OK) return st;
+  fa2::AttnShape s{B, Hq, Hkv, N, d, causal != 0, scale};
+  return hip_status(fa2::launch_forward_fp8(q, k, v, q_scale, k_scale, v_scale, o, lse, s, workspace, stream));
+}
+
 size_t fa2_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || Hq % Hkv || (d != 64 && d != 128)) return 0;
   fa2::AttnShape s{B, Hq, Hkv, 0, d, 0, 1.0f};

@@ -36,6 +36,19 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef unsigned u32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// v_mfma_scale_f32_32x32x64_f8f6f4 with both operands FP8 E4M3FN (format code 0, the OCP
+// encoding: bias 7, largest finite 448) and unit block scales (E8M0 code 127 = 2^0). Lane l
+// supplies row (A) / column (B) l%32 and 32 bytes of k; as with the bf16 form, any ordering
+// of those bytes used identically by A and B gives the same product (checked on gfx950).
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8(u32x8 a, u32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, a),
+                                                         __builtin_bit_cast(i32x8, b), c, 0, 0, 0,
+                                                         127, 0, 127);
+}
+
 // Buffer resource over [base, base + bytes); loads past the end return zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,

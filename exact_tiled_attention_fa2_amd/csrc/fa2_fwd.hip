@@ -44,6 +44,7 @@ struct FwdParams {
   int nqb;        // query blocks per head
   int xcd_remap;  // B*Hq divisible by 8: keep each head's blocks on one XCD
   int window;     // causal window: query i sees keys i - window .. i (>= N: no window)
+  float vmul;     // factor on O: 1, or the FP8 value scale of V
 };
 
 template <int D>
@@ -104,15 +105,24 @@ __device__ __forceinline__ void map_block(int bid, const FwdParams& p, int& bh, 
 // 64 accumulator registers of a row block are rescaled only when a max really moves.
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D>
+// FP8: Q and K are FP8 E4M3FN rows of D bytes and S^T = K Q^T runs on the FP8 MFMA (64-deep
+// k-steps); V arrives as bf16 (widened exactly from FP8 by fa2_fp8_widen_kernel), so P V and
+// everything after S are the bf16 path's. The K tile is stored like a bf16 tile of D/2
+// elements (same bytes per row, same swizzle).
+template <int D, bool FP8>
 __global__ __launch_bounds__(FwdCfg<D>::WAVES * 64)
 __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE)))
 void fa2_fwd_kernel(FwdParams p) {
   using C = FwdCfg<D>;
+  static_assert(!FP8 || D == 128, "the FP8 forward is built for head dim 128");
+  constexpr int KROWB = FP8 ? D : 2 * D;      // bytes per Q / K row
+  constexpr int KSS = FP8 ? D / 64 : C::KS;   // k-steps of S^T = K Q^T
+  constexpr int KDE = FP8 ? D / 2 : D;        // K tile as a bf16 tile of KDE elements per row
+  using kop_t = std::conditional_t<FP8, u32x8, u32x4>;
   // Two K and two V stages in separate arrays: a DMA into one array and LDS reads of another
   // are then provably independent, so reads never wait on an unrelated in-flight DMA.
-  __shared__ __attribute__((aligned(1024))) char k_st0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char k_st1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char k_st0[C::BN * KROWB];
+  __shared__ __attribute__((aligned(1024))) char k_st1[C::BN * KROWB];
   __shared__ __attribute__((aligned(1024))) char v_st0[C::TILE];
   __shared__ __attribute__((aligned(1024))) char v_st1[C::TILE];
 
@@ -131,10 +141,11 @@ void fa2_fwd_kernel(FwdParams p) {
   const int qlo = q0 + wave * C::QPW;
 
   const uint32_t head_bytes = (uint32_t)N * C::ROWB;
+  const uint32_t qk_head_bytes = (uint32_t)N * KROWB;
   const size_t qoff = (size_t)bh * N * D;
   const size_t kvoff = ((size_t)b * p.Hkv + hkv) * (size_t)N * D;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + qoff, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + kvoff, head_bytes);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.q + qoff * (KROWB / D), qk_head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)p.k + kvoff * (KROWB / D), qk_head_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + kvoff, head_bytes);
 
   // Tiles are numbered from the workgroup's first visible tile tbase (a window hides the keys
@@ -156,29 +167,43 @@ void fa2_fwd_kernel(FwdParams p) {
   // Tile t goes to stage t % 2: K two tiles ahead of its use, V one tile ahead.
   auto fetch_k = [&](int t) {
     if (t < ntiles)
-      load_tile<D, false>(rk, (t & 1) ? (lds_char*)k_st1 : (lds_char*)k_st0, (tbase + t) * C::BN, wave, lane);
+      load_tile<KDE, false>(rk, (t & 1) ? (lds_char*)k_st1 : (lds_char*)k_st0, (tbase + t) * C::BN, wave, lane);
   };
   auto fetch_v = [&](int t) {
     if (t < ntiles)
       load_tile<D, true>(rv, (t & 1) ? (lds_char*)v_st1 : (lds_char*)v_st0, (tbase + t) * C::BN, wave, lane);
   };
 
-  // Q as the B operand of S^T = K Q^T: lane holds query l32, head-dim k = 16*ks + 8*hf + e.
-  u32x4 qf[C::NQB][C::KS];
+  // Q as the B operand of S^T = K Q^T: lane holds query l32 and, per k-step, the bytes of
+  // head dims [16 ks + 8 hf, +8) (bf16) or [64 ks + 32 hf, +32) (FP8).
+  kop_t qf[C::NQB][KSS];
 #pragma unroll
   for (int qb = 0; qb < C::NQB; ++qb) {
     const uint32_t row = (uint32_t)(qlo + qb * 32 + l32);
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      qf[qb][ks] = buffer_load16(rq, row * C::ROWB + (16 * ks + 8 * hf) * 2) ^ p.qneg;
+    for (int ks = 0; ks < KSS; ++ks) {
+      if constexpr (FP8) {
+        const u32x4 lo = buffer_load16(rq, row * KROWB + 64 * ks + 32 * hf) ^ p.qneg;
+        const u32x4 hi = buffer_load16(rq, row * KROWB + 64 * ks + 32 * hf + 16) ^ p.qneg;
+        qf[qb][ks] = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
+        qf[qb][ks] = buffer_load16(rq, row * C::ROWB + (16 * ks + 8 * hf) * 2) ^ p.qneg;
+      }
+    }
   }
   fetch_k(0);
   fetch_v(0);
   fetch_k(1);
 
-  int koff[C::KS];  // K A-operand: row l32 (+32 per key block), chunk 2*ks + hf
+  // K A-operand: row l32 (+32 per key block), 16-byte chunks 2*ks + hf (bf16) or
+  // 4*ks + 2*hf and the next one (FP8).
+  constexpr int NKO = FP8 ? 2 * KSS : KSS;
+  int koff[NKO];
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = l32 * C::ROWB + (((2 * ks + hf) ^ swz_k<D>(l32)) << 4);
+  for (int i = 0; i < NKO; ++i) {
+    const int chunk = FP8 ? 4 * (i >> 1) + 2 * hf + (i & 1) : 2 * i + hf;
+    koff[i] = l32 * KROWB + ((chunk ^ swz_k<KDE>(l32)) << 4);
+  }
   int voff[C::DB];  // V^T A-operand: transposing read base per 32-wide head-dim block
   {
     const int r = 4 * hf + ((lane & 15) >> 2);  // + 32*kb + 16*h (+8) leaves swz_v unchanged
@@ -209,11 +234,21 @@ void fa2_fwd_kernel(FwdParams p) {
   // place so the MFMAs read them without register copies.
   typedef u32x4 PTile[C::NQB][2][2];
   constexpr int NPV = 4 * C::DB;  // PV MFMA steps per tile (per query block)
-  constexpr int EXP_SLICE = 32 / C::KS;  // score elements exponentiated per S k-step
+  constexpr int EXP_SLICE = 32 / KSS;    // score elements exponentiated per S k-step
   constexpr int MAX_SLICE = 32 / NPV;    // score elements max-reduced per PV step
 
-  auto kread = [&](const lds_char* kt, int ks, int kb) {
-    return lds_read16(kt + koff[ks] + kb * 32 * C::ROWB);
+  auto kread = [&](const lds_char* kt, int ks, int kb) -> kop_t {
+    if constexpr (FP8) {
+      const u32x4 lo = lds_read16(kt + koff[2 * ks] + kb * 32 * KROWB);
+      const u32x4 hi = lds_read16(kt + koff[2 * ks + 1] + kb * 32 * KROWB);
+      return u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      return lds_read16(kt + koff[ks] + kb * 32 * C::ROWB);
+    }
+  };
+  auto mfma_s = [](kop_t a, kop_t b, f32x16 c) {
+    if constexpr (FP8) return mfma32x32x64_fp8(a, b, c);
+    else return mfma32x32x16(a, b, c);
   };
   // PV step i covers (kb, h, db) with db fastest, so consecutive MFMAs update different
   // accumulators.
@@ -264,12 +299,12 @@ void fa2_fwd_kernel(FwdParams p) {
     for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) sn[qb][kb] = f32x16{};
-    u32x4 kf[2][2];
+    kop_t kf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) kf[0][kb] = kread(kt, 0, kb);
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      if (ks + 1 < C::KS) {
+    for (int ks = 0; ks < KSS; ++ks) {
+      if (ks + 1 < KSS) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) kf[(ks + 1) & 1][kb] = kread(kt, ks + 1, kb);
       }
@@ -277,7 +312,7 @@ void fa2_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb) sn[qb][kb] = mfma32x32x16(kf[ks & 1][kb], qf[qb][ks], sn[qb][kb]);
+        for (int qb = 0; qb < C::NQB; ++qb) sn[qb][kb] = mfma_s(kf[ks & 1][kb], qf[qb][ks], sn[qb][kb]);
       also(ks);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -366,7 +401,7 @@ void fa2_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) sum[qb] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) exp_slice(sbuf[PAR], pf, sum, ks * EXP_SLICE);
+    for (int ks = 0; ks < KSS; ++ks) exp_slice(sbuf[PAR], pf, sum, ks * EXP_SLICE);
     pv_tile(v_cur, pf, [&](int) {});
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) l[qb] += sum[qb];
@@ -423,7 +458,7 @@ void fa2_fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int qb = 0; qb < C::NQB; ++qb) {
     const float lt = sum_halves(l[qb]);
-    const float inv = 1.0f / lt;
+    const float inv = p.vmul / lt;
     const int row = qlo + qb * 32 + l32;
     if (row < N) {
       float* orow = p.o + qoff + (size_t)row * D;
@@ -440,8 +475,8 @@ void fa2_fwd_kernel(FwdParams p) {
   }
 }
 
-hipError_t launch_forward(const void* q, const void* k, const void* v, float* o, float* lse,
-                          const AttnShape& s, hipStream_t stream) {
+static FwdParams forward_params(const void* q, const void* k, const void* v, float* o, float* lse,
+                                const AttnShape& s) {
   FwdParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -459,13 +494,61 @@ hipError_t launch_forward(const void* q, const void* k, const void* v, float* o,
   p.nqb = (s.N + BM - 1) / BM;
   p.xcd_remap = ((s.B * s.Hq) % 8) == 0;
   p.window = s.window >= 0 ? s.window : kNoWindow;
+  p.vmul = 1.0f;
+  return p;
+}
+
+hipError_t launch_forward(const void* q, const void* k, const void* v, float* o, float* lse,
+                          const AttnShape& s, hipStream_t stream) {
+  const FwdParams p = forward_params(q, k, v, o, lse, s);
   const dim3 grid((unsigned)(s.B * s.Hq * p.nqb));
   if (s.d == 128)
-    hipLaunchKernelGGL(fa2_fwd_kernel<128>, grid, dim3(FwdCfg<128>::WAVES * 64), 0, stream, p);
+    hipLaunchKernelGGL((fa2_fwd_kernel<128, false>), grid, dim3(FwdCfg<128>::WAVES * 64), 0, stream, p);
   else if (s.d == 256)
-    hipLaunchKernelGGL(fa2_fwd_kernel<256>, grid, dim3(FwdCfg<256>::WAVES * 64), 0, stream, p);
+    hipLaunchKernelGGL((fa2_fwd_kernel<256, false>), grid, dim3(FwdCfg<256>::WAVES * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL(fa2_fwd_kernel<64>, grid, dim3(FwdCfg<64>::WAVES * 64), 0, stream, p);
+    hipLaunchKernelGGL((fa2_fwd_kernel<64, false>), grid, dim3(FwdCfg<64>::WAVES * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+// FP8 E4M3FN codes -> bf16, exactly (every E4M3FN value is a bf16 value): 16 codes per thread.
+__global__ __launch_bounds__(256) void fa2_fp8_widen_kernel(const uint8_t* __restrict__ src,
+                                                            uint16_t* __restrict__ dst, long n16) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  const u32x4 w = *(const u32x4*)(src + i * 16);
+  u32x4 out[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], false);  // codes 0, 1 of the word
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], true);   // codes 2, 3
+    out[j >> 1][2 * (j & 1)] = pack_bf16(lo[0], lo[1]);
+    out[j >> 1][2 * (j & 1) + 1] = pack_bf16(hi[0], hi[1]);
+  }
+  *(u32x4*)(dst + i * 16) = out[0];
+  *(u32x4*)(dst + i * 16 + 8) = out[1];
+}
+
+size_t forward_fp8_workspace_bytes(const AttnShape& s) {
+  const size_t bytes = (size_t)s.B * s.Hkv * s.N * s.d * 2;
+  return (bytes + 255) & ~(size_t)255;
+}
+
+hipError_t launch_forward_fp8(const void* q8, const void* k8, const void* v8, float q_scale,
+                              float k_scale, float v_scale, float* o, float* lse,
+                              const AttnShape& s, void* ws, hipStream_t stream) {
+  const long n16 = (long)s.B * s.Hkv * s.N * s.d / 16;
+  hipLaunchKernelGGL(fa2_fp8_widen_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(v8), static_cast<uint16_t*>(ws), n16);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  FwdParams p = forward_params(q8, k8, ws, o, lse, s);
+  p.c = fabsf(s.scale) * q_scale * k_scale * kLog2e;
+  p.qneg = s.scale < 0.f ? 0x80808080u : 0u;
+  p.vmul = v_scale;
+  const dim3 grid((unsigned)(s.B * s.Hq * p.nqb));
+  hipLaunchKernelGGL((fa2_fwd_kernel<128, true>), grid, dim3(FwdCfg<128>::WAVES * 64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -20,6 +20,13 @@ constexpr int kNoWindow = 0x3fffffff;
 hipError_t launch_forward(const void* q, const void* k, const void* v, float* o, float* lse,
                           const AttnShape& s, hipStream_t stream);
 
+// FP8 forward (d = 128): q8, k8, v8 are FP8 E4M3FN codes standing for code * scale; the
+// workspace receives V widened to bf16 (forward_fp8_workspace_bytes).
+size_t forward_fp8_workspace_bytes(const AttnShape& s);
+hipError_t launch_forward_fp8(const void* q8, const void* k8, const void* v8, float q_scale,
+                              float k_scale, float v_scale, float* o, float* lse,
+                              const AttnShape& s, void* ws, hipStream_t stream);
+
 // Backward workspace: D at [0, R) and LSE*log2(e) at [R, 2R) floats, R = B*Hq*N.
 hipError_t launch_bwd_preprocess(const float* o, const void* dO, const float* lse, float* ws,
                                  const AttnShape& s, hipStream_t stream);

@@ -175,6 +175,28 @@ int fa2_decode(const void* q, const void* k, const void* v, float* o, float* lse
                int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * FP8 forward (FlashAttention-3 adds FP8 arithmetic: wiki article "FlashAttention-2 (IT)",
+ * section "FlashAttention-3"; "Flash Attention spiegata: una guida completa", section
+ * "Precisione FP8 nativa"). q, k, v hold OCP FP8 E4M3FN codes (1 byte: sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits; largest finite 448; 0x7F / 0xFF are NaN) in the layouts
+ * of fa2_forward, standing for
+ *     Q = code(q) * q_scale,  K = code(k) * k_scale,  V = code(v) * v_scale
+ * (per-tensor scales, finite and > 0; quantising is the caller's business). The result is exact
+ * attention over those values: o, lse as in fa2_forward. S = Q K^T runs on the FP8 matrix
+ * cores (each product of two E4M3 values is exact in fp32); V is widened exactly to bf16 into
+ * the workspace and P V runs as in the bf16 path. d must be 128.
+ * workspace: at least fa2_forward_fp8_workspace_size(B,Hkv,N,d) bytes (2 bytes per element of
+ * v), caller-owned, contents irrelevant, no overlap with other arguments. Other checks as
+ * fa2_forward; a non-positive or non-finite q/k/v scale is FA2_ERR_BAD_SCALE.
+ */
+size_t fa2_forward_fp8_workspace_size(int B, int Hkv, int N, int d);
+
+int fa2_forward_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale,
+                    float v_scale, float* o, float* lse, int B, int Hq, int Hkv, int N, int d,
+                    int causal, float scale, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
 /* Static, human-readable name of a status code ("FA2_OK", ...); "FA2_UNKNOWN" otherwise. */
 const char* fa2_status_string(int status);
 

@@ -179,3 +179,14 @@ def test_decode_workspace_size(lib):
     big = fa2.fa2_decode_workspace_size(1, 8, 2, 4, 1 << 16, 128)
     R = 4 * 4
     assert big >= 2 * R * 129 * 4 and big % 256 == 0
+
+
+def test_fp8_validation(lib):
+    W = fa2.fa2_forward_fp8_workspace_size(1, 1, 128, 128)
+    assert W == 128 * 128 * 2 and fa2.fa2_forward_fp8_workspace_size(1, 1, 128, 64) == 0
+    f = lambda **k: fa2.fa2_forward_fp8(k.get("q", P(0)), P(1), P(2), k.get("qs", 0.1), 0.1, k.get("vs", 0.1),
+                                        k.get("o", P(3)), P(4), 1, 2, 1, 128, k.get("d", 128), 1, k.get("sc", 0.1),
+                                        k.get("ws", P(9)), k.get("wsb", W))
+    assert f(d=64) == 3 and f(d=256) == 3 and f(qs=0.0) == 5 and f(vs=-1.0) == 5 and f(qs=float("inf")) == 5
+    assert f(sc=0.0) == 5 and f(q=None) == 1 and f(q=P(0) + 4) == 6 and f(o=P(1)) == 7
+    assert f(ws=None) == 8 and f(wsb=W - 1) == 8 and f(ws=P(3)) == 7
