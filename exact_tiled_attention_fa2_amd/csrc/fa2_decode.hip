@@ -17,7 +17,8 @@
 //    writes O and LSE directly.
 //  * Per 64-key tile a wave loads its K rows straight into MFMA A-operand registers and copies
 //    the V tile into its own LDS slot (buffer_load ... lds, swizzled for the transposing
-//    reads). Two waves per SIMD overlap one wave's loads with the other's MFMAs.
+//    reads), one tile ahead of the tile it computes (two register sets, two LDS slots), so
+//    each wave keeps about 32 KB of the cache in flight.
 #include "fa2_device.h"
 #include "fa2_launch.h"
 
@@ -54,10 +55,12 @@ struct DecCfg {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fa2_decode_kernel(DecParams p) {
   using C = DecCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char v_slot[C::WAVES][C::TILE];
+  // Two V slots per wave, in separate arrays, for the two tiles in flight.
+  __shared__ __attribute__((aligned(1024))) char v_slot_a[C::WAVES][C::TILE];
+  __shared__ __attribute__((aligned(1024))) char v_slot_b[C::WAVES][C::TILE];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -104,7 +107,8 @@ void fa2_decode_kernel(DecParams p) {
       voff[db] = rr * C::ROWB + (((dd >> 3) ^ swz_v<D>(rr)) << 4) + (dd & 7) * 2;
     }
   }
-  lds_char* vt = (lds_char*)v_slot[wave];
+  lds_char* va = (lds_char*)v_slot_a[wave];
+  lds_char* vb = (lds_char*)v_slot_b[wave];
 
   f32x16 acc[C::DB];
 #pragma unroll
@@ -113,24 +117,30 @@ void fa2_decode_kernel(DecParams p) {
   float l = 0.f;        // this lane's partial row sum
   const float c = p.c;
 
-  for (int t = 0; t < ntiles; ++t) {
+  // Software pipeline, two tiles deep: tile t+1's K rows (registers) and V tile (the other LDS
+  // array) are requested before tile t is computed; V(t) is waited for just before its reads.
+  // VMEM requests complete in order, so "V(t) landed" is "at most the requests of tile t+1 are
+  // still outstanding".
+  constexpr int KLOADS = 2 * C::KS;  // K loads per tile
+  constexpr int VLOADS = C::LPT;     // V copies per tile
+  auto issue = [&](int t, lds_char* vdst, u32x4 (&kdst)[2][C::KS]) __attribute__((always_inline)) {
     const int j0 = k0 + t * C::BN;
-    // V tile -> this wave's LDS slot (swizzled rows), K rows -> A-operand registers.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+        kdst[kb][ks] = buffer_load16(rk, (uint32_t)(j0 + 32 * kb + l32) * C::ROWB + (16 * ks + 8 * hf) * 2);
 #pragma unroll
     for (int blk = 0; blk < C::LPT; ++blk) {
       const int pos = blk * 1024 + lane * 16;
       const int row = pos / C::ROWB;
       const int cp = (pos % C::ROWB) / 16;
-      buffer_load16_lds(rv, vt + blk * 1024, (uint32_t)(j0 + row) * C::ROWB + ((cp ^ swz_v<D>(row)) << 4));
+      buffer_load16_lds(rv, vdst + blk * 1024, (uint32_t)(j0 + row) * C::ROWB + ((cp ^ swz_v<D>(row)) << 4));
     }
-    u32x4 kf[2][C::KS];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-        kf[kb][ks] = buffer_load16(rk, (uint32_t)(j0 + 32 * kb + l32) * C::ROWB + (16 * ks + 8 * hf) * 2);
-    wait_vmem_all();
-
+  };
+  auto compute = [&](int t, const lds_char* vt, const u32x4 (&kf)[2][C::KS], bool next_in_flight)
+      __attribute__((always_inline)) {
+    const int j0 = k0 + t * C::BN;
     // S^T = K Q^T: two 32-key blocks; register e of block kb holds key 8(e/4) + 4hf + e%4.
     f32x16 st[2];
 #pragma unroll
@@ -169,6 +179,13 @@ void fa2_decode_kernel(DecParams p) {
         l += p0 + p1;
         pf[kb][e >> 3][(e >> 1) & 3] = pack_bf16(p0, p1);
       }
+    // V(t) must have landed: only tile t+1's requests may still be outstanding.
+    if (next_in_flight) {
+      static_assert(KLOADS + VLOADS <= 63, "vmcnt range");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KLOADS + VLOADS) : "memory");
+    } else {
+      wait_vmem_all();
+    }
     // O^T += V^T P^T, V^T fragments by transposing LDS reads.
 #pragma unroll
     for (int i = 0; i < 4 * C::DB; ++i) {
@@ -178,7 +195,19 @@ void fa2_decode_kernel(DecParams p) {
       const u32x2 hi = lds_read8_tr(base + 8 * C::ROWB);
       acc[db] = mfma32x32x16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[kb][h], acc[db]);
     }
-    // The next tile's V overwrites this slot: every read above has been consumed by now.
+  };
+  // Tiles alternate between (va, kfa) and (vb, kfb). A slot is refilled only after the tile
+  // that used it is computed (its LDS reads are consumed by then).
+  u32x4 kfa[2][C::KS], kfb[2][C::KS];
+  if (ntiles > 0) issue(0, va, kfa);
+  for (int t = 0; t < ntiles; t += 2) {
+    const bool n1 = t + 1 < ntiles;
+    if (n1) issue(t + 1, vb, kfb);
+    compute(t, va, kfa, n1);
+    if (!n1) break;
+    const bool n2 = t + 2 < ntiles;
+    if (n2) issue(t + 2, va, kfa);
+    compute(t + 1, vb, kfb, n2);
   }
 
   // ---- epilogue: this chunk's O and LSE for row r (a row that met no visible key in the
@@ -207,43 +236,72 @@ void fa2_decode_kernel(DecParams p) {
   if (hf == 0) *lrow = lse_r;
 }
 
-// Merge of the chunks of each row: one thread per 4 consecutive head-dim values of a row.
+// Merge of the chunks of each row: one workgroup per row. The workgroup first finds the row's
+// largest chunk LSE M (finite: some chunk sees a key for every row); thread (slice sl, column
+// c4) then sums w_s = e^(LSE_s - M) and w_s O_s over chunks sl, sl + NSL, ... for 4
+// consecutive head-dim values (a chunk with LSE = -inf gets w = 0), and the slices are added
+// in LDS: LSE = M + ln sum_s w_s, O = sum_s w_s O_s / sum_s w_s.
 template <int D>
 __global__ __launch_bounds__(256) void fa2_decode_merge_kernel(DecParams p) {
-  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-  const long rows = (long)p.B * p.Hkv * p.R;
-  const long row = gid / (D / 4);
-  const int c4 = (int)(gid % (D / 4)) * 4;
-  if (row >= rows) return;
+  constexpr int NC = D / 4;       // column threads per row
+  constexpr int NSL = 256 / NC;   // chunk slices
+  __shared__ f32x4 so[NSL][NC];
+  __shared__ float ss[NSL];
+  __shared__ float smax[4];
+  const long row = blockIdx.x;    // (b * Hkv + g) * R + r
+  const int tid = threadIdx.x;
+  const int c = tid % NC, sl = tid / NC;
   const long vh = row / p.R;
   const int r = (int)(row % p.R);
   const float* pl = p.plse + (size_t)vh * p.nsplit * p.R + r;
+  const float* po = p.po + ((size_t)vh * p.nsplit * p.R + r) * D + 4 * c;
+  const size_t sstride = (size_t)p.R * D;
+
   float mx = -INFINITY;
-  for (int s = 0; s < p.nsplit; ++s) mx = fmaxf(mx, pl[(size_t)s * p.R]);
+  for (int s = tid; s < p.nsplit; s += 256) mx = fmaxf(mx, pl[(size_t)s * p.R]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((tid & 63) == 0) smax[tid >> 6] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+
   float sum = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < p.nsplit; ++s) {
-    const float ls = pl[(size_t)s * p.R];
-    const float w = ls == -INFINITY ? 0.f : __expf(ls - mx);  // mx is finite: some chunk sees a key
+#pragma unroll 8
+  for (int s = sl; s < p.nsplit; s += NSL) {
+    const float w = __expf(pl[(size_t)s * p.R] - M);  // e^-inf = 0
     sum += w;
-    o += w * *(const f32x4*)(p.po + (((size_t)vh * p.nsplit + s) * p.R + r) * D + c4);
+    o += w * *(const f32x4*)(po + s * sstride);
+  }
+  so[sl][c] = o;
+  if (c == 0) ss[sl] = sum;
+  __syncthreads();
+  if (sl != 0) return;
+#pragma unroll
+  for (int t = 1; t < NSL; ++t) {
+    o += so[t][c];
+    sum += ss[t];
   }
   const int b = (int)(vh / p.Hkv), g = (int)(vh % p.Hkv);
   const size_t orow = ((size_t)b * p.Hq + (size_t)g * (p.Hq / p.Hkv)) * p.Nq + r;
-  *(f32x4*)(p.o + orow * D + c4) = o * (1.0f / sum);
-  if (c4 == 0) p.lse[orow] = mx + __logf(sum);
+  *(f32x4*)(p.o + orow * D + 4 * c) = o * (1.0f / sum);  // sum >= 1 (the chunk holding M)
+  if (c == 0) p.lse[orow] = M + __logf(sum);
 }
 
-// Chunking: at least ~4096 waves in flight across the chip (two per SIMD, two rounds), chunks
-// of at least 256 keys, a multiple of the 64-key tile.
+// Chunking: about two rounds of resident waves (one wave per SIMD and workgroup-per-CU
+// residency give 1024 at a time), chunks a multiple of the 64-key tile and at least 256 keys;
+// chunks are lengthened to 1024 or 512 keys when that still leaves a full round of waves,
+// since a longer chunk spends less of its time filling the pipeline.
 static void decode_split(const AttnShape& s, int Nq, int Nk, int* nsplit, int* chunk) {
   const long groups = (long)s.B * s.Hkv * ((s.Hq / s.Hkv * Nq + 31) / 32);
-  long want = (4096 + groups - 1) / groups;
-  const long most = (Nk + 255) / 256;
-  if (want > most) want = most;
-  if (want < 1) want = 1;
+  const long want = (2048 + groups - 1) / groups;
   int ch = (int)((Nk + want - 1) / want);
   ch = (ch + 63) / 64 * 64;
+  for (int longer : {1024, 512, 256})
+    if (ch < longer && (longer == 256 || groups * ((Nk + longer - 1) / longer) >= 1024)) {
+      ch = longer;
+      break;
+    }
   *chunk = ch;
   *nsplit = (Nk + ch - 1) / ch;
 }
@@ -290,8 +348,7 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, float* o, 
     hipLaunchKernelGGL(fa2_decode_kernel<64>, grid, block, 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
-  const long threads = (long)s.B * s.Hkv * p.R * (s.d / 4);
-  const dim3 mgrid((unsigned)((threads + 255) / 256));
+  const dim3 mgrid((unsigned)((long)s.B * s.Hkv * p.R));
   if (s.d == 128)
     hipLaunchKernelGGL(fa2_decode_merge_kernel<128>, mgrid, block, 0, stream, p);
   else

@@ -58,6 +58,12 @@ def test_decode_long_cache(Nk):
     check_decode(7301, 1, 8, 1, 2, Nk, 128, True)
 
 
+def test_decode_more_chunks_than_merge_threads():
+    # one KV head over 131072 keys: 512 chunks per row, more than the merge has threads
+    check_decode(7302, 1, 8, 1, 1, 131072, 128, True)
+    check_decode(7303, 1, 4, 1, 1, 131072, 64, False)
+
+
 def test_decode_square_and_scales():
     check_decode(7400, 1, 4, 2, 300, 300, 128, True)           # Nq = Nk: ordinary causal attention
     check_decode(7401, 1, 4, 2, 7, 500, 128, True, scale=-0.09)
