@@ -111,15 +111,6 @@ __device__ __forceinline__ u32x4 tr_pair(const lds_char* lo_base, const lds_char
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
-// Calls f(std::integral_constant<int, I>) for I = B .. E-1, fully unrolled at compile time.
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
 // Block id -> (head slice, block within head). Workgroups are dealt round-robin to the 8 XCDs
 // (bid & 7 is the XCD); when the slice count divides by 8, each XCD gets a contiguous range of
 // slices and walks their blocks in order, so the blocks of one slice share that XCD's L2.

@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa2 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -144,6 +146,15 @@ template <int D>
 __device__ __forceinline__ int swz_v(int r) {
   using S = SwzCfg<D>;
   return 4 * ((r / S::SWZ_ROWS) & (S::SWZ_SPAN / 4 - 1));
+}
+
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1, fully unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 }  // namespace fa2

@@ -63,6 +63,7 @@ struct FwdCfg {
   static constexpr int ROWB = D * 2;          // bytes per bf16 row
   static constexpr int TILE = BN * ROWB;      // bytes of one K or V tile
   static constexpr int LPW = TILE / 1024 / WAVES;  // 1 KB direct-to-LDS loads per wave per tile
+  static constexpr int LA = 3;  // LDS operand reads run this many MFMA slots ahead
 };
 
 // Copy keys [j0, j0+64) of one head into a swizzled LDS tile. Rows past N read as zero.
@@ -234,8 +235,8 @@ void fa2_fwd_kernel(FwdParams p) {
   // place so the MFMAs read them without register copies.
   typedef u32x4 PTile[C::NQB][2][2];
   constexpr int NPV = 4 * C::DB;  // PV MFMA steps per tile (per query block)
-  constexpr int EXP_SLICE = 32 / KSS;    // score elements exponentiated per S k-step
   constexpr int MAX_SLICE = 32 / NPV;    // score elements max-reduced per PV step
+  constexpr int EXP_PAIRS = 16 / KSS;    // exponential pairs formed per S k-step
 
   auto kread = [&](const lds_char* kt, int ks, int kb) -> kop_t {
     if constexpr (FP8) {
@@ -250,7 +251,7 @@ void fa2_fwd_kernel(FwdParams p) {
     if constexpr (FP8) return mfma32x32x64_fp8(a, b, c);
     else return mfma32x32x16(a, b, c);
   };
-  // PV step i covers (kb, h, db) with db fastest, so consecutive MFMAs update different
+  // P V step i covers (kb, h, db) with db fastest, so consecutive MFMAs update different
   // accumulators.
   auto vread = [&](const lds_char* vt, int i) {
     const int db = i % C::DB, kb = i / (2 * C::DB), h = (i / C::DB) & 1;
@@ -259,15 +260,15 @@ void fa2_fwd_kernel(FwdParams p) {
     const u32x2 hi = lds_read8_tr(base + 8 * C::ROWB);
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
-  // Elements e = 16*kb + r of a lane's 32 scores per query block. A row that has not met a
-  // visible key yet (possible under a window) still has m = -inf; its masked scores then use
-  // reference 0 and give p = 0.
-  auto exp_slice = [&](STile& sc, PTile& pf, float (&sum)[C::NQB], int e0) {
+  // Pairs j0 .. j1-1: elements 2j, 2j+1 of a lane's 32 scores per query block (element
+  // e = 16*kb + r). A row that has not met a visible key yet (possible under a window) still
+  // has m = -inf; its masked scores then use reference 0 and give p = 0.
+  auto exp_pairs = [&](STile& sc, PTile& pf, float (&sum)[C::NQB], int j0, int j1) {
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
-      for (int e = e0; e < e0 + EXP_SLICE; e += 2) {
-        const int kb = e >> 4, r = e & 15;
+      for (int j = j0; j < j1; ++j) {
+        const int kb = j >> 3, r = (2 * j) & 15;
         const float mref = m[qb] == -INFINITY ? 0.f : m[qb];
         const float p0 = fast_exp2(__builtin_fmaf(sc[qb][kb][r], c, -mref));
         const float p1 = fast_exp2(__builtin_fmaf(sc[qb][kb][r + 1], c, -mref));
@@ -292,45 +293,49 @@ void fa2_fwd_kernel(FwdParams p) {
       }
     }
   };
-  // S^T(next) = K Q^T with K fragments read one k-step ahead; `also(ks)` is VALU work slotted
-  // between the MFMA groups. Scheduling fences keep this order.
-  auto s_tile = [&](const lds_char* kt, STile& sn, auto&& also) {
+  // One tile's MFMA stream: the S^T = K Q^T slots (k-step ks, key block kb; kb fastest) if
+  // HAS_S, then the O^T += V^T P^T slots if HAS_PV. Every LDS operand is read LA slots ahead
+  // of its MFMA from a ring of LA + 1 operands, so the reads of the P V phase start during the
+  // last S slots. also_s(ks) and also_pv(i) are VALU work slotted after the MFMAs of S k-step
+  // ks and P V step i; scheduling fences keep this order.
+  auto mfma_stream = [&](auto has_s, auto has_pv, const lds_char* kt, STile& sn, const lds_char* vt,
+                         PTile& pf, auto&& also_s, auto&& also_pv) __attribute__((always_inline)) {
+    constexpr bool HAS_S = decltype(has_s)::value, HAS_PV = decltype(has_pv)::value;
+    constexpr int LA = C::LA;
+    constexpr int NSS = HAS_S ? 2 * KSS : 0;
+    constexpr int NOP = NSS + (HAS_PV ? NPV : 0);
+    kop_t kring[LA + 1];
+    u32x4 vring[LA + 1];
+    auto load = [&](auto J) __attribute__((always_inline)) {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j < NSS) kring[j % (LA + 1)] = kread(kt, j >> 1, j & 1);
+      else vring[j % (LA + 1)] = vread(vt, j - NSS);
+    };
+    if constexpr (HAS_S) {
 #pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb)
+      for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) sn[qb][kb] = f32x16{};
-    kop_t kf[2][2];
+        for (int kb = 0; kb < 2; ++kb) sn[qb][kb] = f32x16{};
+    }
+    static_for<0, (LA < NOP ? LA : NOP)>(load);
+    static_for<0, NOP>([&](auto J) __attribute__((always_inline)) {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j + LA < NOP) load(std::integral_constant<int, j + LA>{});
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (j < NSS) {
+        constexpr int ks = j >> 1, kb = j & 1;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) kf[0][kb] = kread(kt, 0, kb);
+        for (int qb = 0; qb < C::NQB; ++qb) sn[qb][kb] = mfma_s(kring[j % (LA + 1)], qf[qb][ks], sn[qb][kb]);
+        if constexpr (kb == 1) also_s(ks);
+      } else {
+        constexpr int i = j - NSS;
+        constexpr int db = i % C::DB, kb = i / (2 * C::DB), h = (i / C::DB) & 1;
 #pragma unroll
-    for (int ks = 0; ks < KSS; ++ks) {
-      if (ks + 1 < KSS) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) kf[(ks + 1) & 1][kb] = kread(kt, ks + 1, kb);
+        for (int qb = 0; qb < C::NQB; ++qb) acc[qb][db] = mfma32x32x16(vring[j % (LA + 1)], pf[qb][kb][h], acc[qb][db]);
+        also_pv(i);
       }
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb) sn[qb][kb] = mfma_s(kf[ks & 1][kb], qf[qb][ks], sn[qb][kb]);
-      also(ks);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // O^T += V^T P^T with V^T fragments read one step ahead; `also(i)` slotted likewise.
-  auto pv_tile = [&](const lds_char* vt, PTile& pf, auto&& also) {
-    u32x4 vf[2];
-    vf[0] = vread(vt, 0);
-#pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      if (i + 1 < NPV) vf[(i + 1) & 1] = vread(vt, i + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      const int db = i % C::DB, kb = i / (2 * C::DB), h = (i / C::DB) & 1;
-#pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb) acc[qb][db] = mfma32x32x16(vf[i & 1], pf[qb][kb][h], acc[qb][db]);
-      also(i);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    });
   };
   auto rescale_if_needed = [&](const float (&mx)[C::NQB]) {
     float mt[C::NQB];
@@ -382,10 +387,9 @@ void fa2_fwd_kernel(FwdParams p) {
       sum[qb] = 0.f;
       mx[qb] = -INFINITY;
     }
-    s_tile(k_next, sbuf[PAR ^ 1], [&](int ks) { exp_slice(sbuf[PAR], pf, sum, ks * EXP_SLICE); });
-    pv_tile(v_cur, pf, [&](int i) {
-      max_slice(sbuf[PAR ^ 1], mx, i * MAX_SLICE, MASK_NEXT, (tbase + t + 1) * C::BN);
-    });
+    mfma_stream(std::true_type{}, std::true_type{}, k_next, sbuf[PAR ^ 1], v_cur, pf,
+                [&](int ks) { exp_pairs(sbuf[PAR], pf, sum, ks * EXP_PAIRS, (ks + 1) * EXP_PAIRS); },
+                [&](int i) { max_slice(sbuf[PAR ^ 1], mx, i * MAX_SLICE, MASK_NEXT, (tbase + t + 1) * C::BN); });
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) l[qb] += sum[qb];
     rescale_if_needed(mx);
@@ -400,9 +404,8 @@ void fa2_fwd_kernel(FwdParams p) {
     float sum[C::NQB];
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) sum[qb] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KSS; ++ks) exp_slice(sbuf[PAR], pf, sum, ks * EXP_SLICE);
-    pv_tile(v_cur, pf, [&](int) {});
+    exp_pairs(sbuf[PAR], pf, sum, 0, 16);
+    mfma_stream(std::false_type{}, std::true_type{}, nullptr, sbuf[PAR], v_cur, pf, [](int) {}, [](int) {});
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) l[qb] += sum[qb];
     sync_stage();
@@ -413,7 +416,9 @@ void fa2_fwd_kernel(FwdParams p) {
     float mx[C::NQB];
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) mx[qb] = -INFINITY;
-    s_tile((const lds_char*)k_st0, sbuf[0], [&](int) {});
+    PTile unused;
+    mfma_stream(std::true_type{}, std::false_type{}, (const lds_char*)k_st0, sbuf[0], nullptr, unused,
+                [](int) {}, [](int) {});
     for (int i = 0; i < NPV; ++i) max_slice(sbuf[0], mx, i * MAX_SLICE, nfree == 0 || nlead > 0, tbase * C::BN);
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) m[qb] = -INFINITY;
