@@ -88,10 +88,12 @@ def time_sequence(calls, steps, warmup, stream):
     return per, total
 
 
-def extra_workloads(fa2, seedgen, dev, stream, steps):
+def extra_workloads(fa2, seedgen, dev, stream, steps, only=None):
     """Non-headline measurements: the sliding-window path at the headline shape, and the other
     workload shapes (forward-only prefill shapes, a training shape). Values are TFLOP/s of the
-    counted FLOPs over the visible (query, key) pairs: 4d per pair forward, 10d fwd+bwd."""
+    counted FLOPs over the visible (query, key) pairs: 4d per pair forward, 10d fwd+bwd; forwards
+    also report GB/s of their compulsory HBM bytes (Q, K, V read once, O and LSE written once).
+    ``only``: names (substrings) of the workloads to run, or None for all."""
     import numpy as np
     import torch
 
@@ -102,13 +104,19 @@ def extra_workloads(fa2, seedgen, dev, stream, steps):
         if st != 0:
             raise fa2.Fa2Error(st, what)
 
+    def wanted(name):
+        return only is None or any(p in name for p in only)
+
     out = {}
     cases = [("window_W1024_B2_H32_N8192_d128", 2, 32, 32, 8192, 128, True, 1024, True, 0x5EED0006),
+             ("fwd_B1_H2_N256_d64", 1, 2, 2, 256, 64, False, None, False, 0x5EED0001),
              ("fwd_B4_H16_N2048_d64", 4, 16, 16, 2048, 64, False, None, False, 0x5EED0002),
              ("fwd_B1_Hq32_Hkv8_N32768_d128_causal", 1, 32, 8, 32768, 128, True, None, False, 0x5EED0004),
              ("fwdbwd_B4_H16_N4096_d128_causal", 4, 16, 16, 4096, 128, True, None, True, 0x5EED0005),
              ("fwdbwd_B2_H16_N8192_d256_causal", 2, 16, 16, 8192, 256, True, None, True, 0x5EED0008)]
     for name, B, Hq, Hkv, N, d, causal, W, with_bwd, seed in cases:
+        if not wanted(name):
+            continue
         if with_bwd:
             q, k, v, dO = seedgen.attention_inputs(seed, B, Hq, Hkv, N, d, with_do=True)
         else:
@@ -134,8 +142,10 @@ def extra_workloads(fa2, seedgen, dev, stream, steps):
         calls = [fcall, bcall] if with_bwd else [fcall]
         per, total = time_sequence(calls, steps, 2, stream)
         pairs = B * Hq * visible_pairs(N, causal, W)
+        fwd_bytes = (B * Hq + 2 * B * Hkv) * N * d * 2 + B * Hq * N * (d + 1) * 4
         r = {"B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "causal": causal, "window": W,
-             "fwd_ms": round(per[0], 4), "fwd_tflops": round(pairs * 4 * d / (per[0] * 1e-3) / 1e12, 1)}
+             "fwd_ms": round(per[0], 4), "fwd_tflops": round(pairs * 4 * d / (per[0] * 1e-3) / 1e12, 1),
+             "fwd_algorithmic_bytes": fwd_bytes, "fwd_GBps": round(fwd_bytes / (per[0] * 1e-3) / 1e9, 1)}
         if with_bwd:
             r["bwd_ms"] = round(per[1], 4)
             r["fwd_bwd_tflops"] = round(pairs * 10 * d / (total * 1e-3) / 1e12, 1)
@@ -143,7 +153,21 @@ def extra_workloads(fa2, seedgen, dev, stream, steps):
         log("  extra %-38s %s" % (name, r))
         del q, k, v, dO, qd, kd, vd, dod, o, lse, dq, dk, dv, ws
         torch.cuda.empty_cache()
-    # FP8 forward at the headline shape (Q, K, V as E4M3FN codes, per-tensor scale 1/32).
+    if wanted("fp8_fwd_B2_H32_N8192_d128_causal"):
+        fp8_forward(fa2, seedgen, dev, stream, steps, out)
+    if wanted("decode_B8_Hq32_Hkv8_Nq1_Nk32768_d128"):
+        decode(fa2, seedgen, dev, stream, steps, out)
+    return out
+
+
+def fp8_forward(fa2, seedgen, dev, stream, steps, out):
+    """FP8 forward at the headline shape (Q, K, V as E4M3FN codes, per-tensor scale 1/32)."""
+    import torch
+
+    def check(st, what):
+        if st != 0:
+            raise fa2.Fa2Error(st, what)
+
     B, Hq, Hkv, N, d = 2, 32, 32, 8192, 128
     q8, k8, v8 = (torch.from_numpy(x).to(dev) for x in seedgen.fp8_attention_inputs(0x5EED0006, B, Hq, Hkv, N, d))
     o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
@@ -162,8 +186,20 @@ def extra_workloads(fa2, seedgen, dev, stream, steps):
     log("  extra %-38s %s" % ("fp8_fwd_B2_H32_N8192_d128_causal", r))
     del q8, k8, v8, o, lse, ws
 
-    # Decode: one new token per sequence against a 32K-token cache (grouped-query heads). The
-    # pass streams K and V once, so it is reported against HBM bandwidth.
+
+def decode(fa2, seedgen, dev, stream, steps, out):
+    """Decode: one new token per sequence against a 32K-token cache (grouped-query heads). The
+    pass streams K and V once, so it is reported against HBM bandwidth."""
+    import numpy as np
+    import torch
+
+    def up(x):
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def check(st, what):
+        if st != 0:
+            raise fa2.Fa2Error(st, what)
+
     B, Hq, Hkv, Nq, Nk, d = 8, 32, 8, 1, 32768, 128
     q = seedgen.normal_bf16(0x5EED0007, seedgen.TENSOR_IDS["q"], (B, Hq, Nq, d))
     kc = seedgen.normal_bf16(0x5EED0007, seedgen.TENSOR_IDS["k"], (B, Hkv, Nk, d))
@@ -183,7 +219,6 @@ def extra_workloads(fa2, seedgen, dev, stream, steps):
          "hbm_frac": round(nbytes / (total * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     out["decode_B8_Hq32_Hkv8_Nq1_Nk32768_d128"] = r
     log("  extra %-38s %s" % ("decode_B8_Hq32_Hkv8_Nq1_Nk32768_d128", r))
-    return out
 
 
 def cpu_baseline(q, k, v, dO, w, budget_s):
@@ -227,6 +262,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the non-headline workloads")
+    ap.add_argument("--only-extras", default=None, metavar="NAMES",
+                    help="run only the non-headline workloads whose names contain one of these "
+                         "comma-separated strings (no headline step); prints them as one JSON line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (5 times), for scaling "
@@ -259,6 +297,11 @@ def main():
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
     dev = torch.device("cuda:0")
+    if args.only_extras:
+        only = [p for p in args.only_extras.split(",") if p]
+        extras = extra_workloads(fa2, seedgen, dev, torch.cuda.current_stream(), max(5, args.steps), only)
+        print(json.dumps({"extras": extras, "steps": max(5, args.steps)}), flush=True)
+        return
     w = WORKLOAD
     B, Hq, Hkv, N, d, causal = w["B"], w["Hq"], w["Hkv"], w["N"], w["d"], w["causal"]
     scale = 1.0 / math.sqrt(d)
