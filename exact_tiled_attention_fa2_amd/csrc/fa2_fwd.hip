@@ -7,9 +7,10 @@
 // row sum l, with the output accumulator rescaled whenever m grows -- so the N x N matrix is
 // never stored. Only O and LSE = m + ln l reach HBM.
 //
-// gfx950 mapping (one workgroup per (batch, query head, 256-row query block)):
-//  * 8 waves, two per SIMD; each wave owns 32 query rows for the whole pass, so the
-//    online-softmax state and all row reductions stay in that wave's registers.
+// gfx950 mapping (one workgroup per (batch, query head, query block of 256 or 128 rows)):
+//  * 8 waves (or 4 on small grids, two workgroups per CU), two per SIMD; each wave owns 32
+//    query rows for the whole pass, so the online-softmax state and all row reductions stay in
+//    that wave's registers.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: each lane then
 //    holds one query row and 16 keys, the row max/sum are in-register reductions plus one
 //    v_permlane32_swap, and S^T's accumulator is directly the B operand of O^T += V^T P^T.
@@ -47,12 +48,13 @@ struct FwdParams {
   float vmul;     // factor on O: 1, or the FP8 value scale of V
 };
 
-template <int D>
+// NW waves per workgroup (8 or 4; 4 at d = 256).
+template <int D, int NW>
 struct FwdCfg {
   static constexpr int BN = 64;               // keys per tile
   // Two waves per SIMD up to d = 128. At d = 256 a 32-row block's O accumulators alone take
   // 128 registers, so one wave per SIMD with them in AGPRs.
-  static constexpr int WAVES = D <= 128 ? 8 : 4;
+  static constexpr int WAVES = NW;
   static constexpr int WPE = D <= 128 ? 2 : 1;  // waves per SIMD
   static constexpr int QPW = 32;              // query rows per wave
   static constexpr int NQB = QPW / 32;        // 32-row MFMA blocks per wave
@@ -64,13 +66,14 @@ struct FwdCfg {
   static constexpr int TILE = BN * ROWB;      // bytes of one K or V tile
   static constexpr int LPW = TILE / 1024 / WAVES;  // 1 KB direct-to-LDS loads per wave per tile
   static constexpr int LA = 3;  // LDS operand reads run this many MFMA slots ahead
+  static_assert(TILE % (1024 * WAVES) == 0, "a tile splits evenly into the waves' copies");
 };
 
 // Copy keys [j0, j0+64) of one head into a swizzled LDS tile. Rows past N read as zero.
-template <int D, bool IS_V>
+template <int D, int NW, bool IS_V>
 __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, lds_char* tile, int j0,
                                           int wave, int lane) {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, NW>;
 #pragma unroll
   for (int t = 0; t < C::LPW; ++t) {
     const int blk = wave * C::LPW + t;
@@ -110,11 +113,11 @@ constexpr float kRescaleSlack = 8.0f;
 // k-steps); V arrives as bf16 (widened exactly from FP8 by fa2_fp8_widen_kernel), so P V and
 // everything after S are the bf16 path's. The K tile is stored like a bf16 tile of D/2
 // elements (same bytes per row, same swizzle).
-template <int D, bool FP8>
-__global__ __launch_bounds__(FwdCfg<D>::WAVES * 64)
-__attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE)))
+template <int D, int NW, bool FP8>
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(FwdCfg<D, NW>::WPE, FwdCfg<D, NW>::WPE)))
 void fa2_fwd_kernel(FwdParams p) {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, NW>;
   static_assert(!FP8 || D == 128, "the FP8 forward is built for head dim 128");
   constexpr int KROWB = FP8 ? D : 2 * D;      // bytes per Q / K row
   constexpr int KSS = FP8 ? D / 64 : C::KS;   // k-steps of S^T = K Q^T
@@ -168,11 +171,11 @@ void fa2_fwd_kernel(FwdParams p) {
   // Tile t goes to stage t % 2: K two tiles ahead of its use, V one tile ahead.
   auto fetch_k = [&](int t) {
     if (t < ntiles)
-      load_tile<KDE, false>(rk, (t & 1) ? (lds_char*)k_st1 : (lds_char*)k_st0, (tbase + t) * C::BN, wave, lane);
+      load_tile<KDE, NW, false>(rk, (t & 1) ? (lds_char*)k_st1 : (lds_char*)k_st0, (tbase + t) * C::BN, wave, lane);
   };
   auto fetch_v = [&](int t) {
     if (t < ntiles)
-      load_tile<D, true>(rv, (t & 1) ? (lds_char*)v_st1 : (lds_char*)v_st0, (tbase + t) * C::BN, wave, lane);
+      load_tile<D, NW, true>(rv, (t & 1) ? (lds_char*)v_st1 : (lds_char*)v_st0, (tbase + t) * C::BN, wave, lane);
   };
 
   // Q as the B operand of S^T = K Q^T: lane holds query l32 and, per k-step, the bytes of
@@ -480,8 +483,18 @@ void fa2_fwd_kernel(FwdParams p) {
   }
 }
 
+// Waves per workgroup: 8 (256 query rows) normally; 4 (128 rows) when the 8-wave grid would give
+// fewer than six workgroups per CU, so that two workgroups share a CU and one's start-up (Q and the
+// first K/V tiles) and O stores overlap the other's tiles. Head dim 256: always 4.
+constexpr int kComputeUnits = 256;
+static int forward_waves(const AttnShape& s) {
+  if (s.d == 256) return 4;
+  const long wg8 = (long)s.B * s.Hq * ((s.N + 255) / 256);
+  return wg8 < 6L * kComputeUnits ? 4 : 8;
+}
+
 static FwdParams forward_params(const void* q, const void* k, const void* v, float* o, float* lse,
-                                const AttnShape& s) {
+                                const AttnShape& s, int nw) {
   FwdParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -495,7 +508,7 @@ static FwdParams forward_params(const void* q, const void* k, const void* v, flo
   p.causal = s.causal;
   p.c = fabsf(s.scale) * kLog2e;
   p.qneg = s.scale < 0.f ? 0x80008000u : 0u;
-  const int BM = s.d == 256 ? FwdCfg<256>::BM : FwdCfg<128>::BM;
+  const int BM = 32 * nw;  // FwdCfg<D, nw>::BM
   p.nqb = (s.N + BM - 1) / BM;
   p.xcd_remap = ((s.B * s.Hq) % 8) == 0;
   p.window = s.window >= 0 ? s.window : kNoWindow;
@@ -503,16 +516,23 @@ static FwdParams forward_params(const void* q, const void* k, const void* v, flo
   return p;
 }
 
+template <int D, int NW, bool FP8>
+static void launch_fwd_kernel(const FwdParams& p, const AttnShape& s, hipStream_t stream) {
+  static_assert(32 * NW == FwdCfg<D, NW>::BM, "rows per workgroup");
+  const dim3 grid((unsigned)(s.B * s.Hq * p.nqb));
+  hipLaunchKernelGGL((fa2_fwd_kernel<D, NW, FP8>), grid, dim3(NW * 64), 0, stream, p);
+}
+
 hipError_t launch_forward(const void* q, const void* k, const void* v, float* o, float* lse,
                           const AttnShape& s, hipStream_t stream) {
-  const FwdParams p = forward_params(q, k, v, o, lse, s);
-  const dim3 grid((unsigned)(s.B * s.Hq * p.nqb));
-  if (s.d == 128)
-    hipLaunchKernelGGL((fa2_fwd_kernel<128, false>), grid, dim3(FwdCfg<128>::WAVES * 64), 0, stream, p);
-  else if (s.d == 256)
-    hipLaunchKernelGGL((fa2_fwd_kernel<256, false>), grid, dim3(FwdCfg<256>::WAVES * 64), 0, stream, p);
+  const int nw = forward_waves(s);
+  const FwdParams p = forward_params(q, k, v, o, lse, s, nw);
+  if (s.d == 256)
+    launch_fwd_kernel<256, 4, false>(p, s, stream);
+  else if (s.d == 128)
+    nw == 8 ? launch_fwd_kernel<128, 8, false>(p, s, stream) : launch_fwd_kernel<128, 4, false>(p, s, stream);
   else
-    hipLaunchKernelGGL((fa2_fwd_kernel<64, false>), grid, dim3(FwdCfg<64>::WAVES * 64), 0, stream, p);
+    nw == 8 ? launch_fwd_kernel<64, 8, false>(p, s, stream) : launch_fwd_kernel<64, 4, false>(p, s, stream);
   return hipGetLastError();
 }
 
@@ -548,12 +568,12 @@ hipError_t launch_forward_fp8(const void* q8, const void* k8, const void* v8, fl
                      static_cast<const uint8_t*>(v8), static_cast<uint16_t*>(ws), n16);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  FwdParams p = forward_params(q8, k8, ws, o, lse, s);
+  const int nw = forward_waves(s);
+  FwdParams p = forward_params(q8, k8, ws, o, lse, s, nw);
   p.c = fabsf(s.scale) * q_scale * k_scale * kLog2e;
   p.qneg = s.scale < 0.f ? 0x80808080u : 0u;
   p.vmul = v_scale;
-  const dim3 grid((unsigned)(s.B * s.Hq * p.nqb));
-  hipLaunchKernelGGL((fa2_fwd_kernel<128, true>), grid, dim3(FwdCfg<128>::WAVES * 64), 0, stream, p);
+  nw == 8 ? launch_fwd_kernel<128, 8, true>(p, s, stream) : launch_fwd_kernel<128, 4, true>(p, s, stream);
   return hipGetLastError();
 }
 

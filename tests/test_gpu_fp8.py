@@ -60,6 +60,11 @@ def test_fp8_gqa_scales_and_sign():
     check_fp8(9602, 1, 32, 8, 4096, 128, True, sample=128)
 
 
+def test_fp8_eight_wave_blocks_sampled():
+    # B*Hq*ceil(N/256) >= 1536: 8-wave workgroups, ragged end, grouped heads
+    check_fp8(9700, 2, 192, 48, 1000, 128, True, sample=48)
+
+
 def test_fp8_rejects_without_launch():
     import torch
     q8 = to_dev_u8(seedgen.normal_e4m3(9700, "q", (1, 2, 64, 128), 32.0))
