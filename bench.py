@@ -153,11 +153,73 @@ def extra_workloads(fa2, seedgen, dev, stream, steps, only=None):
         log("  extra %-38s %s" % (name, r))
         del q, k, v, dO, qd, kd, vd, dod, o, lse, dq, dk, dv, ws
         torch.cuda.empty_cache()
+    if wanted("hbm_sweep_d64_noncausal"):
+        hbm_sweep(fa2, seedgen, dev, stream, steps, out)
     if wanted("fp8_fwd_B2_H32_N8192_d128_causal"):
         fp8_forward(fa2, seedgen, dev, stream, steps, out)
     if wanted("decode_B8_Hq32_Hkv8_Nq1_Nk32768_d128"):
         decode(fa2, seedgen, dev, stream, steps, out)
     return out
+
+
+def hbm_sweep(fa2, seedgen, dev, stream, steps, out):
+    """Forward on short sequences with many heads (d=64, non-causal). Per (b, h) the pass does
+    4*N^2*d FLOP over N*(3*2d + 4d + 4) compulsory bytes, about 0.4*N FLOP per byte: below the
+    chip's ridge point (~315) for N <= 512, so these shapes are bound by HBM and are reported in
+    GB/s of the compulsory bytes (Q, K, V read once; O and LSE written once)."""
+    import numpy as np
+    import torch
+
+    def up(x):
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    d, res = 64, {}
+    for N in (128, 256, 512):
+        for B, H in ((4, 256), (16, 256)):
+            q, k, v = seedgen.attention_inputs(0x5EED0010 + N, B, H, H, N, d)
+            qd, kd, vd = up(q), up(k), up(v)
+            o = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+            def call():
+                st = fa2.fa2_forward(qd, kd, vd, o, lse, B, H, H, N, d, False, 0.125, stream)
+                if st != 0:
+                    raise fa2.Fa2Error(st, "fa2_forward")
+
+            per, total = time_sequence([call], max(20, steps), 3, stream)
+            nbytes = 3 * B * H * N * d * 2 + B * H * N * (d + 1) * 4
+            flops = 4.0 * B * H * N * N * d
+            res["BH%d_N%d" % (B * H, N)] = {
+                "B": B, "H": H, "N": N, "d": d, "ms": round(total, 4), "algorithmic_bytes": nbytes,
+                "GBps": round(nbytes / (total * 1e-3) / 1e9, 1),
+                "hbm_frac": round(nbytes / (total * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "flop_per_byte": round(flops / nbytes, 1), "tflops": round(flops / (total * 1e-3) / 1e12, 1)}
+            del q, k, v, qd, kd, vd, o, lse
+    out["hbm_sweep_d64_noncausal"] = res
+    log("  extra %-38s %s" % ("hbm_sweep_d64_noncausal", {k: v["GBps"] for k, v in res.items()}))
+    torch.cuda.empty_cache()
+
+
+def peak_from_device(props):
+    """Dense bf16 MFMA peak recomputed from the device: CUs x 4096 FLOP/clk x peak clock, with the
+    clock read by hipDeviceGetAttribute(hipDeviceAttributeClockRate) from the HIP runtime this
+    process has loaded. None if that runtime cannot be found."""
+    import ctypes
+    path = None
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64.so" in line:
+                path = line.split()[-1]
+                break
+    if path is None:
+        return None
+    hip = ctypes.CDLL(path)
+    khz = ctypes.c_int(0)
+    hip_device_attribute_clock_rate = 5  # peak clock in kHz
+    if hip.hipDeviceGetAttribute(ctypes.byref(khz), hip_device_attribute_clock_rate, 0) != 0:
+        return None
+    return {"cus": props.multi_processor_count, "clock_mhz": khz.value / 1e3,
+            "bf16_tflops": round(props.multi_processor_count * 4096 * khz.value * 1e3 / 1e12, 1)}
 
 
 def fp8_forward(fa2, seedgen, dev, stream, steps, out):
@@ -393,6 +455,10 @@ def main():
         cpu = cpu_baseline(q, k, v, dO, w, args.cpu_seconds)
 
     props = torch.cuda.get_device_properties(0)
+    peak_dev = peak_from_device(props)
+    if peak_dev is not None:
+        log("peak recomputed from the device: %d CUs x 4096 FLOP/clk x %.0f MHz = %.1f TFLOP/s bf16"
+            % (peak_dev["cus"], peak_dev["clock_mhz"], peak_dev["bf16_tflops"]))
     log("device %s, %d CUs; step %.3f ms (wall %.3f ms); fwd %.3f ms = %.1f TFLOP/s (%.1f%% peak); "
         "bwd %.3f ms; fwd+bwd %.1f TFLOP/s (%.1f%%)" % (props.name, props.multi_processor_count, ms_step, wall_ms,
                                                      avg["fwd"], fwd_tflops, 100 * fwd_tflops / PEAK_BF16_TFLOPS,
@@ -425,6 +491,7 @@ def main():
         "cpu_baseline": cpu,
         "extras": extras,
         "peak_tflops": PEAK_BF16_TFLOPS,
+        "peak_from_device": peak_dev,
         "device": props.name,
     }
     print(json.dumps(out), flush=True)

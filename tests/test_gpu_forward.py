@@ -73,13 +73,13 @@ def test_gqa_ratios(Hkv, d):
     check_forward(77 + Hkv, 2, 8, Hkv, 333, d, True)
 
 
-# Workgroups hold 8 waves (256 query rows) when the grid of such blocks reaches six per CU
-# (B*Hq*ceil(N/256) >= 1536) and 4 waves (128 rows) below that; the small shapes above run the
-# 4-wave blocks, these the 8-wave ones, with ragged ends, grouped heads and both mask modes.
-@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal", [(2, 192, 48, 1000, 128, True), (3, 128, 128, 777, 64, False),
-                                                 (6, 64, 8, 1025, 128, False), (4, 96, 96, 1000, 64, True)])
+# Workgroups hold 8 waves (256 query rows) for N > 4096 when the grid of such blocks reaches six
+# per CU (B*Hq*ceil(N/256) >= 1536), else 4 waves (128 rows); the shapes above mostly run 4-wave
+# blocks, these 8-wave ones, with ragged ends, grouped heads and both mask modes.
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal", [(1, 192, 48, 4200, 128, True), (1, 96, 96, 4500, 64, False),
+                                                 (2, 64, 8, 4353, 128, False), (1, 128, 128, 5000, 64, True)])
 def test_eight_wave_blocks_sampled(B, Hq, Hkv, N, d, causal):
-    assert B * Hq * ((N + 255) // 256) >= 1536
+    assert N > 4096 and B * Hq * ((N + 255) // 256) >= 1536
     check_forward(0x8A0 + N + Hq, B, Hq, Hkv, N, d, causal, sample=48)
 
 

@@ -61,8 +61,8 @@ def test_fp8_gqa_scales_and_sign():
 
 
 def test_fp8_eight_wave_blocks_sampled():
-    # B*Hq*ceil(N/256) >= 1536: 8-wave workgroups, ragged end, grouped heads
-    check_fp8(9700, 2, 192, 48, 1000, 128, True, sample=48)
+    # N > 4096 and B*Hq*ceil(N/256) >= 1536: 8-wave workgroups, ragged end, grouped heads
+    check_fp8(9700, 1, 192, 48, 4200, 128, True, sample=48)
 
 
 def test_fp8_rejects_without_launch():
