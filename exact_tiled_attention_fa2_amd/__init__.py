@@ -81,7 +81,17 @@ def _ptr(x):
         return None
     if isinstance(x, int):
         return x
-    return x.data_ptr()  # torch tensor
+    # torch tensor: the library reads plain row-major buffers, so a strided view would be
+    # read with the wrong layout
+    if not x.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous (row-major [B, H, N, d]); got strides %s"
+                         % (tuple(x.stride()),))
+    return x.data_ptr()
+
+
+def _expect(name, x, dtype):
+    if x.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, x.dtype))
 
 
 def _stream(s):
@@ -180,6 +190,8 @@ def forward(q, k, v, causal: bool, scale: float, stream=None, window: int | None
 
     ``window`` (with ``causal``): query i sees keys i - window .. i (fa2_forward_window)."""
     import torch
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _expect(name, x, torch.bfloat16)
     B, Hq, Hkv, N, d = _dims(q, k)
     o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
@@ -198,6 +210,10 @@ def backward(q, k, v, o, lse, dO, causal: bool, scale: float, stream=None, works
              window: int | None = None):
     """dQ, dK, dV (fp32) of sum(O * dO) for the outputs of :func:`forward` (same ``window``)."""
     import torch
+    for name, x in (("q", q), ("k", k), ("v", v), ("dO", dO)):
+        _expect(name, x, torch.bfloat16)
+    _expect("o", o, torch.float32)
+    _expect("lse", lse, torch.float32)
     B, Hq, Hkv, N, d = _dims(q, k)
     dq = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
     dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device)
@@ -223,6 +239,8 @@ def decode(q, k, v, causal: bool, scale: float, stream=None, workspace=None):
     """O (fp32) and LSE (fp32) of q [B,Hq,Nq,d] against the cache k, v [B,Hkv,Nk,d] (bf16);
     causal rows are the newest tokens (row i sees keys j <= Nk - Nq + i)."""
     import torch
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _expect(name, x, torch.bfloat16)
     B, Hq, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
     o = torch.empty((B, Hq, Nq, d), dtype=torch.float32, device=q.device)
@@ -241,6 +259,8 @@ def forward_fp8(q8, k8, v8, scales, causal: bool, scale: float, stream=None, wor
     """O, LSE (fp32) of attention over FP8 E4M3FN codes (uint8 device tensors q8 [B,Hq,N,d],
     k8/v8 [B,Hkv,N,d]) standing for codes * (q_scale, k_scale, v_scale) = ``scales``."""
     import torch
+    for name, x in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _expect(name, x, torch.uint8)
     B, Hq, N, d = q8.shape
     Hkv = k8.shape[1]
     o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q8.device)

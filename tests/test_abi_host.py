@@ -190,3 +190,21 @@ def test_fp8_validation(lib):
     assert f(d=64) == 3 and f(d=256) == 3 and f(qs=0.0) == 5 and f(vs=-1.0) == 5 and f(qs=float("inf")) == 5
     assert f(sc=0.0) == 5 and f(q=None) == 1 and f(q=P(0) + 4) == 6 and f(o=P(1)) == 7
     assert f(ws=None) == 8 and f(wsb=W - 1) == 8 and f(ws=P(3)) == 7
+
+
+def test_binding_rejects_strided_views_and_wrong_dtypes(lib):
+    # The library reads plain row-major buffers: the binding refuses a strided view (and the
+    # conveniences a wrong dtype) before anything reaches it. CPU tensors are fine for this:
+    # nothing is launched.
+    import torch
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    view = q[:, :, ::2]
+    assert not view.is_contiguous()
+    o = torch.zeros(1, 2, 4, 64)
+    lse = torch.zeros(1, 2, 4)
+    with pytest.raises(ValueError, match="contiguous"):
+        fa2.fa2_forward(view, view, view, o, lse, 1, 2, 2, 4, 64, True, 0.125)
+    with pytest.raises(TypeError, match="bfloat16"):
+        fa2.forward(q.float(), q, q, True, 0.125)
+    with pytest.raises(TypeError, match="uint8"):
+        fa2.forward_fp8(q, q, q, (1.0, 1.0, 1.0), True, 0.125)
