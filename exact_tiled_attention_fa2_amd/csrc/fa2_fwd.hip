@@ -52,10 +52,11 @@ struct FwdParams {
 template <int D, int NW>
 struct FwdCfg {
   static constexpr int BN = 64;               // keys per tile
-  // Two waves per SIMD up to d = 128. At d = 256 a 32-row block's O accumulators alone take
-  // 128 registers, so one wave per SIMD with them in AGPRs.
+  // Waves per SIMD: three for 4-wave workgroups at d = 64 (the kernel fits 168 registers; three
+  // workgroups share a CU), two otherwise up to d = 128. At d = 256 a 32-row block's O
+  // accumulators alone take 128 registers, so one wave per SIMD with them in AGPRs.
   static constexpr int WAVES = NW;
-  static constexpr int WPE = D <= 128 ? 2 : 1;  // waves per SIMD
+  static constexpr int WPE = D <= 64 && NW == 4 ? 3 : D <= 128 ? 2 : 1;
   static constexpr int QPW = 32;              // query rows per wave
   static constexpr int NQB = QPW / 32;        // 32-row MFMA blocks per wave
   static constexpr int BM = WAVES * QPW;      // query rows per workgroup
