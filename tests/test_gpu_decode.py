@@ -58,6 +58,12 @@ def test_decode_long_cache(Nk):
     check_decode(7301, 1, 8, 1, 2, Nk, 128, True)
 
 
+def test_decode_largest_cache():
+    # Nk = 2^22 - 1, the longest cache accepted at d = 128: 32-bit in-head offsets at the top of
+    # their range, and 2048 chunks merged per row
+    check_decode(7310, 1, 8, 1, 1, (1 << 22) - 1, 128, True)
+
+
 def test_decode_more_chunks_than_merge_threads():
     # one KV head over 131072 keys: 512 chunks per row, more than the merge has threads
     check_decode(7302, 1, 8, 1, 1, 131072, 128, True)

@@ -73,6 +73,12 @@ def test_gqa_ratios(Hkv, d):
     check_forward(77 + Hkv, 2, 8, Hkv, 333, d, True)
 
 
+def test_largest_sequence_accepted():
+    # N = 2^22 - 1 is the longest sequence accepted at d = 128 (fp32 rows of one head stay under
+    # 2^31 bytes); every buffer's 32-bit in-head offsets reach the top of their range here.
+    check_forward(0x5EED0A00, 1, 1, 1, (1 << 22) - 1, 128, True, sample=24)
+
+
 # Workgroups hold 8 waves (256 query rows) for N > 4096 when the grid of such blocks reaches six
 # per CU (B*Hq*ceil(N/256) >= 1536), else 4 waves (128 rows); the shapes above mostly run 4-wave
 # blocks, these 8-wave ones, with ragged ends, grouped heads and both mask modes.
