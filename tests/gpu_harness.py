@@ -60,3 +60,21 @@ def rel_l2(a, b):
 
 def sample_rows(seed, nslices, N, count=256):
     return seedgen.sample_rows_all(seed, nslices, N, count)
+
+
+def causal_row_stats(q64, k64, v64, dO64, scale, stat_rows):
+    """The oracle's backward row statistics (m, l, D), [B,Hq,N] each, filled only at the per-slice
+    rows ``stat_rows`` [B*Hq, R] of a causal problem: m = LSE and l = 1 from the oracle's own
+    forward of those rows, D = dO . O. Other entries are left at m = 0, l = 1, D = 0 and must not
+    be read (causal dK/dV of the last keys and dQ of a row read only their own rows)."""
+    B, Hq, N = q64.shape[:3]
+    ro, rl = oracle.forward(q64, k64, v64, True, scale, rows=stat_rows)
+    m = np.zeros((B, Hq, N))
+    l = np.ones((B, Hq, N))
+    D = np.zeros((B, Hq, N))
+    for s in range(B * Hq):
+        b, h = divmod(s, Hq)
+        m[b, h, stat_rows[s]] = rl[b, h]
+        D[b, h, stat_rows[s]] = np.einsum("rc,rc->r", dO64[b, h, stat_rows[s]], ro[b, h])
+    return m, l, D
+

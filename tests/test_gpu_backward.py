@@ -42,6 +42,37 @@ def check_backward(seed, B, Hq, Hkv, N, d, causal, scale=None, sample=None):
     return dq, dk, dv, dO
 
 
+def check_backward_long_causal(seed, B, Hq, Hkv, N, d, nq=32, nk=64):
+    """Causal backward at a long sequence, checked exactly where that is cheap: dQ at sampled
+    query rows (each needs only its own row of the softmax) and dK/dV at the last nk keys (only
+    the last nk queries see them). The oracle's row statistics for those rows come from its own
+    forward: m = LSE, l = 1, D = dO . O (the identity the CPU pins tie to sum_j P dP)."""
+    scale = 1.0 / math.sqrt(d)
+    q, k, v, dO = H.make_inputs(seed, B, Hq, Hkv, N, d, with_do=True)
+    o, lse, dq, dk, dv = run_fwd_bwd(q, k, v, dO, True, scale)
+    qrows = H.sample_rows(seed, B * Hq, N, nq)
+    tail = np.arange(N - nk, N, dtype=np.int32)
+    stat_rows = np.concatenate([qrows, np.tile(tail, (B * Hq, 1))], axis=1)
+    q64, k64, v64, dO64 = H.f64(q), H.f64(k), H.f64(v), H.f64(dO)
+    m, l, D = H.causal_row_stats(q64, k64, v64, dO64, scale, stat_rows)
+    krows = np.tile(tail, (B * Hkv, 1))
+    rdq, rdk, rdv, _ = oracle.backward(q64, k64, v64, dO64, True, scale, qrows=qrows, krows=krows,
+                                       stats=(m, l, D))
+    gdq, gdk, gdv = H.gather_rows(dq, qrows), H.gather_rows(dk, krows), H.gather_rows(dv, krows)
+    eq, ek, ev = H.rel_l2(gdq, rdq), H.rel_l2(gdk, rdk), H.rel_l2(gdv, rdv)
+    print("bwd long B=%d Hq=%d Hkv=%d N=%d d=%d: dQ %.3e dK %.3e dV %.3e" % (B, Hq, Hkv, N, d, eq, ek, ev))
+    assert eq <= H.TOL_GRAD and ek <= H.TOL_GRAD and ev <= H.TOL_GRAD
+
+
+def test_prefill_shape_backward_long_rows():
+    # the benchmark's workload: B=2, H=32, N=8192, d=128, causal
+    check_backward_long_causal(0x5EED0006, 2, 32, 32, 8192, 128)
+
+
+def test_gqa_long_backward_long_rows():
+    check_backward_long_causal(0x5EED0B00, 1, 32, 8, 32768, 128, nq=16)
+
+
 def test_training_step_causal_sampled():
     check_backward(0x5EED0005, 4, 16, 16, 4096, 128, True, sample=256)
 

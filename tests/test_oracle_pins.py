@@ -38,3 +38,25 @@ def test_rejects_bad_shapes(orc):
         orc.forward(q, k, k, False, 1.0)
     with pytest.raises(RuntimeError):
         orc.forward(np.zeros((1, 2, 4, 2)), k, k, False, 1.0, rows=[0, 9])
+
+
+def test_causal_row_stats_shortcut_matches_full_statistics(orc):
+    # The long-sequence GPU backward check feeds the oracle row statistics for only the rows it
+    # needs (sampled queries and the last keys' queries); on a small causal problem that must
+    # give what the oracle's own full statistics give.
+    import math
+    import numpy as np
+    import seedgen
+    from tests import gpu_harness as H
+    B, Hq, Hkv, N, d = 1, 4, 2, 300, 64
+    q, k, v, dO = (H.f64(x) for x in seedgen.attention_inputs(5, B, Hq, Hkv, N, d, with_do=True))
+    scale = 1 / math.sqrt(d)
+    qrows = seedgen.sample_rows_all(5, B * Hq, N, 8)
+    tail = np.arange(N - 16, N, dtype=np.int32)
+    stat_rows = np.concatenate([qrows, np.tile(tail, (B * Hq, 1))], axis=1)
+    stats = H.causal_row_stats(q, k, v, dO, scale, stat_rows)
+    krows = np.tile(tail, (B * Hkv, 1))
+    short = orc.backward(q, k, v, dO, True, scale, qrows=qrows, krows=krows, stats=stats)[:3]
+    full = orc.backward(q, k, v, dO, True, scale, qrows=qrows, krows=krows)[:3]
+    for a, b in zip(short, full):
+        assert np.abs(a - b).max() <= 1e-12 * max(1.0, np.abs(b).max())
