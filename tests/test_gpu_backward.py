@@ -73,6 +73,11 @@ def test_gqa_long_backward_long_rows():
     check_backward_long_causal(0x5EED0B00, 1, 32, 8, 32768, 128, nq=16)
 
 
+def test_head_dim_256_backward_long_rows():
+    # the d = 256 benchmark extra's shape, B=2, H=16, N=8192 (two dK/dV passes, two-stage dQ ring)
+    check_backward_long_causal(0x5EED0008, 2, 16, 16, 8192, 256)
+
+
 def test_training_step_causal_sampled():
     check_backward(0x5EED0005, 4, 16, 16, 4096, 128, True, sample=256)
 
