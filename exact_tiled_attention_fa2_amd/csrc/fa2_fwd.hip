@@ -8,23 +8,27 @@
 // never stored. Only O and LSE = m + ln l reach HBM.
 //
 // gfx950 mapping (one workgroup per (batch, query head, query block of 256 or 128 rows)):
-//  * 8 waves (or 4 on small grids, two workgroups per CU), two per SIMD; each wave owns 32
-//    query rows for the whole pass, so the online-softmax state and all row reductions stay in
-//    that wave's registers.
+//  * 8 waves for long sequences on large grids, else 4 (several workgroups per CU); two waves
+//    per SIMD (three at d = 64 with 4-wave workgroups, one at d = 256). Each wave owns 32 query
+//    rows for the whole pass, so the online-softmax state and all row reductions stay in that
+//    wave's registers.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: each lane then
 //    holds one query row and 16 keys, the row max/sum are in-register reductions plus one
 //    v_permlane32_swap, and S^T's accumulator is directly the B operand of O^T += V^T P^T.
 //  * K and V tiles (64 keys) arrive by buffer_load ... lds (no staging registers), double
 //    buffered. K is read as 16-byte A-operand rows; V^T is read with ds_read_b64_tr_b16.
-//    Both tiles are XOR-swizzled so these reads hit distinct LDS banks.
+//    Both tiles are XOR-swizzled so these reads hit distinct LDS banks. Each tile is one
+//    unrolled MFMA stream (S slots, then P V slots) whose LDS operands are read a few slots
+//    ahead; the exponentials of one tile run between the S MFMAs of the next.
 //  * Causal: K/V tiles above a wave's last row are skipped; only tiles that straddle the
 //    diagonal (or the ragged end of the sequence) are masked. Query blocks are scheduled
 //    heaviest first, and blocks of one head stay on one XCD so their K/V reads share an L2.
 //  * Sliding window (causal, keys i - W .. i): the workgroup starts at its first visible tile,
 //    and the leading tiles that cross the window's lower edge are masked too.
 //  * Scale folded into the exponent: p = 2^(s*c - m) with c = |scale|*log2(e); a negative
-//    scale flips the sign of the Q operand instead. The accumulator rescale is skipped when
-//    no row max in the wave changed.
+//    scale flips the sign of the Q operand instead. The reference m is raised -- and O and l
+//    rescaled -- only when some row's tile max exceeds it by more than 8 (log2 units), so p
+//    stays below 2^8.
 #include <type_traits>
 
 #include "fa2_device.h"
