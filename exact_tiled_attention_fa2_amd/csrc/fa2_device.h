@@ -99,6 +99,14 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(unsigned, v);
 }
 
+// acc + lo + hi of a packed bf16 pair, in fp32 (v_dot2c_f32_bf16 against (1, 1)): sums exactly
+// the bf16 values an MFMA consumed.
+__device__ __forceinline__ float add_bf16_pair(unsigned pk, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
+                                         __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // An empty asm statement with an AGPR operand. Its presence tells the compiler that the kernel

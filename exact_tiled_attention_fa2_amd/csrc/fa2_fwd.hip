@@ -228,11 +228,16 @@ void fa2_fwd_kernel(FwdParams p) {
   for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) acc[qb][db] = f32x16{};
+  // Row sums relative to m, this lane's part: [0] of the fp32 p (for LSE), [1] of the bf16 P
+  // that P V consumed (for normalising O). Normalising by the sum of the very weights applied
+  // keeps O a convex combination of V rows: with the lazy reference the dominant p can be up
+  // to 2^8, and its bf16 rounding would otherwise shift a nearly one-hot row by up to 2^-9 |O|.
+  typedef float Sums[C::NQB][2];
   float m[C::NQB];        // reference (log2 domain) per query row, -inf before tile 0
-  float l[C::NQB];        // this lane's partial row sum relative to m
+  Sums l;
 #pragma unroll
   for (int qb = 0; qb < C::NQB; ++qb) {
-    l[qb] = 0.f;
+    l[qb][0] = l[qb][1] = 0.f;
     m[qb] = -INFINITY;
   }
   const float c = p.c;
@@ -271,7 +276,7 @@ void fa2_fwd_kernel(FwdParams p) {
   // Pairs j0 .. j1-1: elements 2j, 2j+1 of a lane's 32 scores per query block (element
   // e = 16*kb + r). A row that has not met a visible key yet (possible under a window) still
   // has m = -inf; its masked scores then use reference 0 and give p = 0.
-  auto exp_pairs = [&](STile& sc, PTile& pf, float (&sum)[C::NQB], int j0, int j1) {
+  auto exp_pairs = [&](STile& sc, PTile& pf, Sums& sum, int j0, int j1) {
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
@@ -280,8 +285,10 @@ void fa2_fwd_kernel(FwdParams p) {
         const float mref = m[qb] == -INFINITY ? 0.f : m[qb];
         const float p0 = fast_exp2(__builtin_fmaf(sc[qb][kb][r], c, -mref));
         const float p1 = fast_exp2(__builtin_fmaf(sc[qb][kb][r + 1], c, -mref));
-        sum[qb] += p0 + p1;
-        pf[qb][kb][r >> 3][(r >> 1) & 3] = pack_bf16(p0, p1);
+        const unsigned pk = pack_bf16(p0, p1);
+        sum[qb][0] += p0 + p1;
+        sum[qb][1] = add_bf16_pair(pk, sum[qb][1]);
+        pf[qb][kb][r >> 3][(r >> 1) & 3] = pk;
       }
   };
   auto max_slice = [&](STile& sn, float (&mx)[C::NQB], int e0, bool mask, int j0) {
@@ -362,7 +369,8 @@ void fa2_fwd_kernel(FwdParams p) {
         // the wave brought into this branch.
         const float alpha = m[qb] == mnew ? 1.f : fast_exp2(m[qb] - mnew);
         m[qb] = mnew;
-        l[qb] *= alpha;
+        l[qb][0] *= alpha;
+        l[qb][1] *= alpha;
         // Scaled through a zero-operand MFMA: every definition of an accumulator is then an
         // MFMA result, and the allocator keeps one register home for it around this branch.
 #pragma unroll
@@ -389,17 +397,21 @@ void fa2_fwd_kernel(FwdParams p) {
     fetch_k(t + 2);
     fetch_v(t + 1);
     PTile pf;
-    float sum[C::NQB], mx[C::NQB];
+    Sums sum;
+    float mx[C::NQB];
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) {
-      sum[qb] = 0.f;
+      sum[qb][0] = sum[qb][1] = 0.f;
       mx[qb] = -INFINITY;
     }
     mfma_stream(std::true_type{}, std::true_type{}, k_next, sbuf[PAR ^ 1], v_cur, pf,
                 [&](int ks) { exp_pairs(sbuf[PAR], pf, sum, ks * EXP_PAIRS, (ks + 1) * EXP_PAIRS); },
                 [&](int i) { max_slice(sbuf[PAR ^ 1], mx, i * MAX_SLICE, MASK_NEXT, (tbase + t + 1) * C::BN); });
 #pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) l[qb] += sum[qb];
+    for (int qb = 0; qb < C::NQB; ++qb) {
+      l[qb][0] += sum[qb][0];
+      l[qb][1] += sum[qb][1];
+    }
     rescale_if_needed(mx);
     sync_stage();
   };
@@ -409,13 +421,16 @@ void fa2_fwd_kernel(FwdParams p) {
     fetch_k(t + 2);
     fetch_v(t + 1);
     PTile pf;
-    float sum[C::NQB];
+    Sums sum;
 #pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) sum[qb] = 0.f;
+    for (int qb = 0; qb < C::NQB; ++qb) sum[qb][0] = sum[qb][1] = 0.f;
     exp_pairs(sbuf[PAR], pf, sum, 0, 16);
     mfma_stream(std::false_type{}, std::true_type{}, nullptr, sbuf[PAR], v_cur, pf, [](int) {}, [](int) {});
 #pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) l[qb] += sum[qb];
+    for (int qb = 0; qb < C::NQB; ++qb) {
+      l[qb][0] += sum[qb][0];
+      l[qb][1] += sum[qb][1];
+    }
     sync_stage();
   };
 
@@ -467,11 +482,11 @@ void fa2_fwd_kernel(FwdParams p) {
     sync_stage();
   }
 
-  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
+  // ---- epilogue: O = acc / (sum of the bf16 P), LSE = (m + log2 l) ln 2 ----
 #pragma unroll
   for (int qb = 0; qb < C::NQB; ++qb) {
-    const float lt = sum_halves(l[qb]);
-    const float inv = p.vmul / lt;
+    const float lt = sum_halves(l[qb][0]);
+    const float inv = p.vmul / sum_halves(l[qb][1]);
     const int row = qlo + qb * 32 + l32;
     if (row < N) {
       float* orow = p.o + qoff + (size_t)row * D;

@@ -78,3 +78,16 @@ def causal_row_stats(q64, k64, v64, dO64, scale, stat_rows):
         D[b, h, stat_rows[s]] = np.einsum("rc,rc->r", dO64[b, h, stat_rows[s]], ro[b, h])
     return m, l, D
 
+
+def to_bf16_bits(x):
+    """Round finite values to bf16 (round to nearest, ties to even) and return the bit patterns:
+    builds test inputs from transformed seeded values (both sides then read the same bytes)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((u + (((u >> 16) & 1) + 0x7FFF)) >> 16).astype(np.uint16)
+
+
+def scale_rows(bits, factors):
+    """bf16 tensor [B,H,N,d] with row n multiplied by factors[n], re-rounded to bf16."""
+    x = seedgen.bf16_bits_to_f64(bits) * np.asarray(factors, dtype=np.float64)[None, None, :, None]
+    return to_bf16_bits(x)
+

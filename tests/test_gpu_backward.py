@@ -21,8 +21,14 @@ def run_fwd_bwd(q, k, v, dO, causal, scale, stream=None):
 
 
 def check_backward(seed, B, Hq, Hkv, N, d, causal, scale=None, sample=None):
-    scale = 1.0 / math.sqrt(d) if scale is None else scale
     q, k, v, dO = H.make_inputs(seed, B, Hq, Hkv, N, d, with_do=True)
+    return check_backward_on(q, k, v, dO, causal, scale, seed=seed, sample=sample)
+
+
+def check_backward_on(q, k, v, dO, causal, scale=None, seed=0, sample=None):
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
     o, lse, dq, dk, dv = run_fwd_bwd(q, k, v, dO, causal, scale)
     if sample is None:
         qrows = np.tile(np.arange(N, dtype=np.int32), (B * Hq, 1))
@@ -80,6 +86,23 @@ def test_head_dim_256_backward_long_rows():
 
 def test_training_step_causal_sampled():
     check_backward(0x5EED0005, 4, 16, 16, 4096, 128, True, sample=256)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("profile", ["growing", "shrinking"])
+def test_score_range_stress(profile, causal):
+    # keys scaled along the sequence: large reference jumps between tiles, or tiles that
+    # contribute nothing (the backward recomputes P from the forward's LSE)
+    N = 700
+    q, k, v, dO = H.make_inputs(0x57E7, 1, 4, 2, N, 128, with_do=True)
+    j = np.arange(N, dtype=np.float64)
+    factors = 1.0 + (j if profile == "growing" else N - 1 - j) / 8.0
+    check_backward_on(q, H.scale_rows(k, factors), v, dO, causal, seed=0x57E7)
+
+
+def test_near_one_hot_backward():
+    q, k, v, dO = H.make_inputs(0x57E8, 1, 4, 2, 500, 128, with_do=True)
+    check_backward_on(q, k, v, dO, True, scale=8.0, seed=0x57E8)
 
 
 def test_small_full():

@@ -76,6 +76,12 @@ def test_decode_square_and_scales():
     check_decode(7402, 2, 16, 4, 2, 3000, 64, False, scale=0.3)
 
 
+def test_decode_near_one_hot_rows():
+    # scale 8 on N(0,1) inputs: each row is dominated by one or two keys, spread over the chunks
+    check_decode(7403, 2, 8, 2, 3, 5000, 128, True, scale=8.0)
+    check_decode(7404, 1, 8, 8, 1, 20000, 64, False, scale=8.0)
+
+
 def test_decode_deterministic():
     import torch
     q, k, v = (H.to_dev(x) for x in decode_inputs(7500, 4, 32, 8, 2, 20000, 128))

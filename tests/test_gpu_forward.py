@@ -20,8 +20,14 @@ def run_forward(q, k, v, causal, scale, stream=None):
 
 
 def check_forward(seed, B, Hq, Hkv, N, d, causal, scale=None, sample=None):
-    scale = 1.0 / math.sqrt(d) if scale is None else scale
     q, k, v = H.make_inputs(seed, B, Hq, Hkv, N, d)
+    return check_forward_on(q, k, v, causal, scale, seed=seed, sample=sample)
+
+
+def check_forward_on(q, k, v, causal, scale=None, seed=0, sample=None):
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
     o, lse = run_forward(q, k, v, causal, scale)
     if sample is None:
         rows = np.tile(np.arange(N, dtype=np.int32), (B * Hq, 1))
@@ -71,6 +77,28 @@ def test_ragged_lengths(N, d, causal):
 @pytest.mark.parametrize("d", [64, 128])
 def test_gqa_ratios(Hkv, d):
     check_forward(77 + Hkv, 2, 8, Hkv, 333, d, True)
+
+
+# Online-softmax stress: the reference is raised only when a row's tile max passes it by more than
+# 8 (log2 units). Keys scaled up along the sequence make almost every tile raise it by a large
+# jump; scaled down, later tiles contribute nothing; a huge scale makes each row nearly one-hot.
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("profile", ["growing", "shrinking", "steps"])
+def test_score_range_stress(profile, causal, d):
+    N = 1000
+    q, k, v = H.make_inputs(0x57E5 + d, 1, 4, 2, N, d)
+    j = np.arange(N, dtype=np.float64)
+    factors = {"growing": 1.0 + j / 8.0,                       # score spread x126 by the end
+               "shrinking": 1.0 + (N - 1 - j) / 8.0,
+               "steps": 2.0 ** np.floor(j / 64.0) / 64.0}[profile]  # doubles every tile
+    check_forward_on(q, H.scale_rows(k, factors), v, causal, seed=0x57E5)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_near_one_hot_rows(causal):
+    q, k, v = H.make_inputs(0x57E6, 1, 4, 4, 700, 128)
+    check_forward_on(q, k, v, causal, scale=8.0, seed=0x57E6)
 
 
 def test_largest_sequence_accepted():
