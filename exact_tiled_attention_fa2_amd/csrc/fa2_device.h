@@ -76,12 +76,6 @@ __device__ __forceinline__ u32x2 lds_read8_tr(const lds_char* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-__device__ __forceinline__ float partner_half(float x) {
-  // value held by lane (l ^ 32)
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return (__lane_id() < 32) ? __uint_as_float(r[1]) : __uint_as_float(r[0]);
-}
-
 __device__ __forceinline__ float max_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -113,22 +107,6 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // uses AGPRs, which makes it select the AGPR-accumulator form of MFMA: the O accumulators then
 // stay in AGPRs across the loop instead of being copied out and back every iteration.
 __device__ __forceinline__ void agpr_accumulators_hint() { asm volatile("" ::"a"(0.0f)); }
-
-// Hides a value's origin from the optimiser (no instruction is emitted), so address
-// arithmetic on it is not re-associated and hoisted into many loop-invariant registers.
-template <typename T>
-__device__ __forceinline__ T opaque(T x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
-// Marks an accumulator as redefined here, in AGPRs (no instruction is emitted): copies of it
-// into VGPRs cannot be scheduled above this point.
-__device__ __forceinline__ void pin_agpr(f32x16& x) { asm volatile("" : "+a"(x)); }
-
-// The VGPR counterpart: score accumulators are consumed by VALU code, so keeping them in
-// VGPRs avoids a copy out of AGPRs per register.
-__device__ __forceinline__ void pin_vgpr(f32x16& x) { asm volatile("" : "+v"(x)); }
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
