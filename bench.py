@@ -67,9 +67,10 @@ def visible_pairs(N, causal, window=None):
     return W * (W + 1) // 2 + (N - W) * (W + 1)
 
 
-def time_sequence(calls, steps, warmup, stream):
+def time_sequence(calls, steps, warmup, stream, spread=None):
     """Median (over steps) of each call's duration and of the whole sequence, in ms, from HIP
-    events recorded on ``stream`` between the calls."""
+    events recorded on ``stream`` between the calls. ``spread``, if a dict, receives the min and
+    max of each call's duration ("min", "max": lists like the medians)."""
     import numpy as np
     import torch
     for _ in range(warmup):
@@ -83,7 +84,11 @@ def time_sequence(calls, steps, warmup, stream):
             c()
         ev[s][len(calls)].record(stream)
     torch.cuda.synchronize()
-    per = [float(np.median([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)])) for i in range(len(calls))]
+    durs = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)] for i in range(len(calls))]
+    per = [float(np.median(d)) for d in durs]
+    if spread is not None:
+        spread["min"] = [float(np.min(d)) for d in durs]
+        spread["max"] = [float(np.max(d)) for d in durs]
     total = float(np.median([ev[s][0].elapsed_time(ev[s][len(calls)]) for s in range(steps)]))
     return per, total
 
@@ -140,11 +145,17 @@ def extra_workloads(fa2, seedgen, dev, stream, steps, only=None):
             bcall = lambda: check(fa2.fa2_backward_window(qd, kd, vd, o, lse, dod, dq, dk, dv, B, Hq, Hkv, N, d, W,
                                                           scale, ws, wsb, stream), name)
         calls = [fcall, bcall] if with_bwd else [fcall]
-        per, total = time_sequence(calls, steps, 2, stream)
+        spread, runs = {}, steps
+        per, total = time_sequence(calls, runs, 2, stream, spread)
+        if per[0] < 0.5:  # short launches: many more samples (at least 200)
+            runs = max(200, steps)
+            per, total = time_sequence(calls, runs, 5, stream, spread)
         pairs = B * Hq * visible_pairs(N, causal, W)
         fwd_bytes = (B * Hq + 2 * B * Hkv) * N * d * 2 + B * Hq * N * (d + 1) * 4
         r = {"B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "causal": causal, "window": W,
-             "fwd_ms": round(per[0], 4), "fwd_tflops": round(pairs * 4 * d / (per[0] * 1e-3) / 1e12, 1),
+             "fwd_ms": round(per[0], 4), "fwd_ms_min": round(spread["min"][0], 4),
+             "fwd_ms_max": round(spread["max"][0], 4), "timed_runs": runs,
+             "fwd_tflops": round(pairs * 4 * d / (per[0] * 1e-3) / 1e12, 1),
              "fwd_algorithmic_bytes": fwd_bytes, "fwd_GBps": round(fwd_bytes / (per[0] * 1e-3) / 1e9, 1)}
         if with_bwd:
             r["bwd_ms"] = round(per[1], 4)
@@ -438,8 +449,10 @@ def main():
     for n in names:
         bound, work, unit, peak = algo[n]
         ach = work / (avg[n] * 1e-3)
-        kernels[n] = {"avg_ms": round(avg[n], 4), "achieved": round(ach, 1), "unit": unit,
-                      "frac": round(ach / peak, 4)}
+        kernels[n] = {"avg_ms": round(avg[n], 4), "median_ms": round(float(np.median(per_kernel[n])), 4),
+                      "min_ms": round(float(np.min(per_kernel[n])), 4),
+                      "max_ms": round(float(np.max(per_kernel[n])), 4),
+                      "achieved": round(ach, 1), "unit": unit, "frac": round(ach / peak, 4)}
     dom = max(names, key=lambda n: avg[n])
     bound, work, unit, peak = algo[dom]
     achieved = work / (avg[dom] * 1e-3)
