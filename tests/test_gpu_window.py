@@ -84,6 +84,12 @@ def test_window_long_sampled():
     check_window(6500, 1, 8, 2, 8192, 128, 1024, sample=256)
 
 
+def test_window_eight_wave_blocks_sampled():
+    # windows of more than 4096 keys on long sequences and large grids run 8-wave workgroups
+    # (shorter windows run 4-wave ones, like the shapes above)
+    check_window(6600, 1, 192, 48, 4500, 128, 4200, sample=32, backward=False)
+
+
 def test_wide_window_is_causal():
     """A window of N - 1 or more gives exactly fa2_forward / fa2_backward with causal = 1."""
     import torch
