@@ -503,14 +503,15 @@ void fa2_fwd_kernel(FwdParams p) {
   }
 }
 
-// Waves per workgroup: 4 (128 query rows, two workgroups per CU, so that one's start-up -- Q and
-// the first K/V tiles -- and O stores overlap the other's tiles), or 8 (256 rows, fewer K/V tile
-// copies per row) for long sequences (N > 4096, and no window of 4096 keys or fewer, which
-// makes each row's work as short as a short sequence's) on grids of at least six 8-wave
-// workgroups per CU, the only case where 8 measured faster. Head dim 256: always 4.
+// Waves per workgroup: 4 (128 query rows, several workgroups per CU, so that one's start-up --
+// Q and the first K/V tiles -- and O stores overlap the others' tiles), or, at d = 128 only, 8
+// (256 rows, fewer K/V tile copies per row) for long sequences (N > 4096, and no window of 4096
+// keys or fewer, which makes each row's work as short as a short sequence's) on grids of at
+// least six 8-wave workgroups per CU: the only case where 8 measured faster. d = 64 runs three
+// 4-wave workgroups per CU and d = 256 one.
 constexpr int kComputeUnits = 256;
 static int forward_waves(const AttnShape& s) {
-  if (s.d == 256 || s.N <= 4096 || (s.window >= 0 && s.window <= 4096)) return 4;
+  if (s.d != 128 || s.N <= 4096 || (s.window >= 0 && s.window <= 4096)) return 4;
   const long wg8 = (long)s.B * s.Hq * ((s.N + 255) / 256);
   return wg8 < 6L * kComputeUnits ? 4 : 8;
 }
@@ -554,7 +555,7 @@ hipError_t launch_forward(const void* q, const void* k, const void* v, float* o,
   else if (s.d == 128)
     nw == 8 ? launch_fwd_kernel<128, 8, false>(p, s, stream) : launch_fwd_kernel<128, 4, false>(p, s, stream);
   else
-    nw == 8 ? launch_fwd_kernel<64, 8, false>(p, s, stream) : launch_fwd_kernel<64, 4, false>(p, s, stream);
+    launch_fwd_kernel<64, 4, false>(p, s, stream);
   return hipGetLastError();
 }
 

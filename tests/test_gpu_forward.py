@@ -107,13 +107,13 @@ def test_largest_sequence_accepted():
     check_forward(0x5EED0A00, 1, 1, 1, (1 << 22) - 1, 128, True, sample=24)
 
 
-# Workgroups hold 8 waves (256 query rows) for N > 4096 when the grid of such blocks reaches six
-# per CU (B*Hq*ceil(N/256) >= 1536), else 4 waves (128 rows); the shapes above mostly run 4-wave
-# blocks, these 8-wave ones, with ragged ends, grouped heads and both mask modes.
-@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal", [(1, 192, 48, 4200, 128, True), (1, 96, 96, 4500, 64, False),
-                                                 (2, 64, 8, 4353, 128, False), (1, 128, 128, 5000, 64, True)])
+# At d = 128, workgroups hold 8 waves (256 query rows) for N > 4096 when the grid of such blocks
+# reaches six per CU (B*Hq*ceil(N/256) >= 1536), else 4 waves (128 rows); the shapes above mostly
+# run 4-wave blocks, these 8-wave ones, with ragged ends, grouped heads and both mask modes.
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal", [(1, 192, 48, 4200, 128, True), (1, 96, 96, 4500, 128, False),
+                                                 (2, 64, 8, 4353, 128, False), (1, 128, 128, 5000, 128, True)])
 def test_eight_wave_blocks_sampled(B, Hq, Hkv, N, d, causal):
-    assert N > 4096 and B * Hq * ((N + 255) // 256) >= 1536
+    assert d == 128 and N > 4096 and B * Hq * ((N + 255) // 256) >= 1536
     check_forward(0x8A0 + N + Hq, B, Hq, Hkv, N, d, causal, sample=48)
 
 
