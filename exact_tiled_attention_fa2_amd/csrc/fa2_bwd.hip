@@ -9,13 +9,16 @@
 // Three kernels run in stream order, none with atomics (the result is deterministic, as
 // the wiki article "FlashAttention-2" stresses in its performance section):
 //   1. preprocess   D_i = sum_c dO_ic O_ic                   (one value per query row)
-//   2. dK/dV        one workgroup per (batch, KV head, 128-key block); each wave keeps its
-//                   32 keys' K, V (MFMA B operands) and fp32 dK^T, dV^T in registers and
-//                   walks every query tile of every query head sharing the KV head.
-//   3. dQ           one workgroup per (batch, query head, 128-query block); each wave keeps
-//                   its 32 queries' Q, dO and fp32 dQ^T in registers and walks the key tiles.
-// Q/dO (dK/dV kernel) and K/V (dQ kernel) tiles stream into LDS by buffer_load ... lds,
-// double buffered, in a layout that serves both 16-byte row reads and the transposing
+//   2. dK/dV        one workgroup per (batch, KV head, 128-key block), walking every query
+//                   tile of every query head sharing the KV head. Head dims 64 and 128: four
+//                   pairs of waves, one pair per 32 keys; the first keeps K and makes P and
+//                   dV, the second keeps V and makes dS and dK from the P its partner leaves
+//                   in LDS. Head dim 256: four waves, each with its 32 keys' K, V and dK, dV.
+//   3. dQ           one workgroup per (batch, query head, query block); each wave keeps its
+//                   queries' Q, dO and fp32 dQ^T in registers (64 queries, 32 at head dim
+//                   256) and walks the key tiles.
+// Q/dO (dK/dV kernels) and K/V (dQ kernel) tiles stream into LDS by buffer_load ... lds, in
+// two or three stages, in a layout that serves both 16-byte row reads and the transposing
 // ds_read_b64_tr_b16 reads without bank conflicts.
 #include <type_traits>
 
@@ -56,7 +59,6 @@ struct BwdCfg {
   static constexpr int NDH = D / (DB * 32);
   static constexpr int ROWB = D * 2;
   static constexpr int TILE = BT * ROWB;
-  static constexpr int LPW = TILE / 1024 / WAVES;
   static constexpr int RO = KS < 8 ? KS : 8;  // distinct row-read offsets (chunks 16+ add 256 B)
 };
 
@@ -72,13 +74,15 @@ __device__ __forceinline__ int swz_dual(int r) {
   return ((i % Q4) << 2) | ((i / Q4) & 3);
 }
 
-template <int D>
+template <int D, int NW = BwdCfg<D>::WAVES>
 __device__ __forceinline__ void load_tile_dual(__amdgpu_buffer_rsrc_t rs, lds_char* tile, int row0,
                                                int wave, int lane) {
   using C = BwdCfg<D>;
+  constexpr int LPW = C::TILE / 1024 / NW;  // 1 KB loads per wave
+  static_assert(LPW * NW * 1024 == C::TILE, "tile not divisible among the waves");
 #pragma unroll
-  for (int t = 0; t < C::LPW; ++t) {
-    const int blk = wave * C::LPW + t;
+  for (int t = 0; t < LPW; ++t) {
+    const int blk = wave * LPW + t;
     const int pos = blk * 1024 + lane * 16;
     const int r = pos / C::ROWB;
     const int cp = (pos % C::ROWB) / 16;
@@ -439,6 +443,355 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
+// ------------------------------------------------------------------ 2b. dK / dV, paired waves
+
+// Head dims up to 128: eight waves, two per SIMD, in four pairs that each own 32 keys. Wave w
+// (w < 4) keeps the keys' K and computes S = Q K^T, P = 2^(S c - lse2) and dV^T += dO^T P; it
+// leaves P in LDS as packed bf16, in the MFMA operand layout. Its partner w + 4, on the same
+// SIMD, keeps V and works one query tile behind: dP = dO V^T, dS = P (dP - D) from the P it
+// reads back, dK^T += Q^T dS. The two halves are one MFMA sequence on one register set (K or
+// V, dV^T or dK^T, S or dP, P or dS) with the row-read and transposed-read tiles swapped, so
+// a wave holds half the state of the single-wave kernel: everything stays in VGPRs, and a
+// SIMD runs the MFMAs of one wave beside the exponentials or dS arithmetic of the other.
+// P enters dS rounded to bf16, the value the dV product consumed.
+template <int D>
+struct PairCfg {
+  static constexpr int WAVES = 8;
+  static constexpr int PAIRS = 4;
+  static constexpr int RPW = 32;             // keys per pair
+  static constexpr int BR = PAIRS * RPW;     // keys per workgroup
+  static constexpr int PBUF = PAIRS * 4096;  // one tile's P: [pair][row block][half][lane] x 16 B
+  static_assert(BR == BwdCfg<D>::BR, "both dK/dV kernels use the same key blocks");
+};
+
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
+  using C = BwdCfg<D>;
+  using PC = PairCfg<D>;
+  // Three stages (the P waves read tile s while their partners read tile s - 1 and tile s + 1
+  // lands), each in separate arrays, and two P buffers. The compiler lays the 16 KB arrays out
+  // as q0 q1 q2 do0 do1 do2 pbuf0 pbuf1, then the statistics: an LDS read reaches the tiles
+  // below 64 KB through its immediate offset; the others get lane offsets raised by 64 KB
+  // once per tile (tile below), the statistics a base lowered by 128 KB.
+  __shared__ __attribute__((aligned(1024))) char t0_do0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char t1_do1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char t2_do2[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char t3_q0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char t4_q1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char t5_q2[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char t6_pbuf0[PC::PBUF];
+  __shared__ __attribute__((aligned(1024))) char t7_pbuf1[PC::PBUF];
+  __shared__ __attribute__((aligned(1024))) char stat_st0[2048];
+  __shared__ __attribute__((aligned(1024))) char stat_st1[2048];
+  __shared__ __attribute__((aligned(1024))) char stat_st2[2048];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pair = wave & 3;
+  const bool pwave = wave < 4;  // keeps K and produces P (else keeps V and produces dS)
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int N = p.N;
+  int bg, kblk;
+  map_slice_block(blockIdx.x, p.B * p.Hkv, p.nblk, bg, kblk);
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const int G = p.Hq / p.Hkv;
+  const int k0 = kblk * PC::BR;
+  const int kw = k0 + pair * PC::RPW;  // the pair's first key
+
+  const uint32_t head_bytes = (uint32_t)N * C::ROWB;
+  const size_t kvoff = ((size_t)b * p.Hkv + g) * (size_t)N * D;
+
+  // Query tiles as in the single-wave kernel: every query head of the group, from the top
+  // tile that sees a key of the block down to the one holding key k0.
+  const int W = p.window;
+  const int nqt_all = (N + C::BT - 1) / C::BT;
+  const int qt0 = p.causal ? k0 / C::BT : 0;
+  const int qt_top = min(nqt_all - 1, (k0 + PC::BR - 1 + W) / C::BT);
+  const int nqt = qt_top - qt0 + 1;
+  const int iters = G * nqt;
+
+  auto q_st = [&](auto S) __attribute__((always_inline)) {
+    constexpr int s = decltype(S)::value;
+    return (lds_char*)(s == 0 ? t3_q0 : s == 1 ? t4_q1 : t5_q2);
+  };
+  auto do_st = [&](auto S) __attribute__((always_inline)) {
+    constexpr int s = decltype(S)::value;
+    return (lds_char*)(s == 0 ? t0_do0 : s == 1 ? t1_do1 : t2_do2);
+  };
+  auto stat_st = [&](auto S) __attribute__((always_inline)) {
+    constexpr int s = decltype(S)::value;
+    return (lds_char*)(s == 0 ? stat_st0 : s == 1 ? stat_st1 : stat_st2);
+  };
+  // Tiles are numbered it = h nqt + u (query head g G + h, tile row (qt_top - u) 64); the
+  // loops below step a (head, tile) cursor instead of dividing.
+  struct Cursor {
+    int h, u;
+  };
+  auto advance = [&](Cursor& c) __attribute__((always_inline)) {
+    if (++c.u == nqt) {
+      c.u = 0;
+      ++c.h;
+    }
+  };
+  // Lane part of the DMA offsets (row within the tile, swizzled chunk), fixed for the kernel.
+  constexpr int LPW = C::TILE / 1024 / PC::WAVES;
+  uint32_t dma_off[LPW];
+#pragma unroll
+  for (int t = 0; t < LPW; ++t) {
+    const int pos = (wave * LPW + t) * 1024 + lane * 16;
+    const int r = pos / C::ROWB;
+    dma_off[t] = (uint32_t)(r * C::ROWB + ((((pos % C::ROWB) / 16) ^ swz_dual<D>(r)) << 4));
+  }
+  auto fetch = [&](auto S, int it, const Cursor& cur) __attribute__((always_inline)) {
+    if (it >= iters) return;
+    const int hq = g * G + cur.h;
+    const int qrow0 = (qt_top - cur.u) * C::BT;
+    const size_t qoff = ((size_t)b * p.Hq + hq) * (size_t)N * D;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + qoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dO + qoff, head_bytes);
+#pragma unroll
+    for (int t = 0; t < LPW; ++t) {
+      const uint32_t off = (uint32_t)qrow0 * C::ROWB + dma_off[t];
+      buffer_load16_lds(rq, q_st(S) + (wave * LPW + t) * 1024, off);
+      buffer_load16_lds(rd, do_st(S) + (wave * LPW + t) * 1024, off);
+    }
+    if (wave == 0) {
+      // D and lse2 of the tile's 64 rows; lanes past 15 read past the end (zeros).
+      const size_t roff = ((size_t)b * p.Hq + hq) * (size_t)N;
+      const uint32_t off = lane < 16 ? (uint32_t)(qrow0 + 4 * lane) * 4 : (uint32_t)N * 4;
+      buffer_load16_lds(make_rsrc(p.delta + roff, (uint32_t)N * 4), stat_st(S), off);
+      buffer_load16_lds(make_rsrc(p.lse2 + roff, (uint32_t)N * 4), stat_st(S) + 1024, off);
+    }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  fetch(I0{}, 0, Cursor{0, 0});
+
+  constexpr int KS = C::KS, DB = C::DB;
+  int roff[C::RO], toff[DB], toff8[DB];
+#pragma unroll
+  for (int ks = 0; ks < C::RO; ++ks) roff[ks] = row_read_off<D>(lane, ks);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    toff[db] = tr_read_off<D>(lane, db, 0);
+    toff8[db] = tr_read_off<D>(lane, db, 1);
+  }
+
+  const float c = p.c;
+  const int key = kw + l32;
+
+  // One query tile: NS MFMA steps, S or dP of row blocks 0 and 1 (KS steps each), then
+  // dV^T or dK^T over (row block, half, head-dim block). Operand reads run PF steps ahead.
+  // The P or dS values of row block mb become readable DL steps after its last S or dP step
+  // (ready) and are consumed from step use(mb, h) on: the first half's eight values are made
+  // in [ready, use(mb, 0)), the second half's in [use(mb, 0), use(mb, 1)).
+  constexpr int NS = 2 * KS + 4 * DB;
+  constexpr int PF = 3;
+  constexpr int DL = 2;
+  auto ready = [](int mb) { return KS * (mb + 1) + DL; };
+  auto use = [](int mb, int h) { return 2 * KS + (2 * mb + h) * DB; };
+  static_assert(ready(0) < use(0, 0) && ready(1) < use(1, 0), "row block consumed before ready");
+  // RH / TH: the row-read / transposed-read tile lies above the reach of a read's immediate
+  // offset; its reads then use lane offsets raised by 64 KB once per tile (an opaque add, so
+  // the compiler does not fold it back into one add per read).
+  auto tile = [&](auto PW, auto RH, auto TH, const u32x4 (&kv)[KS], f32x16 (&acc)[DB],
+                  const lds_char* rsrc, const lds_char* tsrc, const lds_char* stat, lds_char* pb,
+                  int qrow0, bool fix) __attribute__((always_inline)) {
+    constexpr bool PWAVE = decltype(PW)::value;
+    constexpr int RB = decltype(RH)::value ? 65536 : 0, TB = decltype(TH)::value ? 65536 : 0;
+    int ro[C::RO], to[DB], to8[DB];
+#pragma unroll
+    for (int k = 0; k < C::RO; ++k) ro[k] = RB ? opaque_add<RB>(roff[k]) : roff[k];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      to[db] = TB ? opaque_add<TB>(toff[db]) : toff[db];
+      to8[db] = TB ? opaque_add<TB>(toff8[db]) : toff8[db];
+    }
+    const lds_char* rlo = rsrc - RB;
+    const lds_char* tlo = tsrc - TB;
+    f32x16 sd[2] = {f32x16{}, f32x16{}};  // S (P waves) or dP
+    u32x4 op[2][2];                        // [mb][h]: P or dS, 16 queries x 32 keys, packed bf16
+    float pf[2][16];                       // P in fp32 until packed (P waves)
+    f32x4 st4[2][4];                       // lse2 (P waves) or D of the lane's rows
+    const FA2_LDS float* sbase = (const FA2_LDS float*)(stat - 131072 + opaque_add<131072>(16 * hf));
+    auto load_stats = [&](int mb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) st4[mb][rq] = *(const FA2_LDS f32x4*)(sbase + 32 * mb + 8 * rq);
+    };
+    lds_char* pfrag = pb + pair * 4096 + lane * 16;  // + (2 mb + h) KB
+    // Zero P outside key <= query <= key + window for the eight rows of half h (see the
+    // single-wave kernel for the register-to-row map).
+    auto causal_fixup = [&](int mb, int h) __attribute__((always_inline)) {
+      const int lo = key - qrow0 - 4 * hf;
+      const int hi = lo + W;
+#pragma unroll
+      for (int r = 8 * h; r < 8 * h + 8; r += 2) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int x = 32 * mb + 8 * ((r + u) >> 2) + ((r + u) & 3);
+          pf[mb][r + u] = (x >= lo && x <= hi) ? pf[mb][r + u] : 0.f;
+        }
+        op[mb][h][(r >> 1) & 3] = pack_bf16(pf[mb][r], pf[mb][r + 1]);
+      }
+    };
+    auto values = [&](int mb, int h, int e0, int e1) __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = e0; e < e1; e += 2) {
+        const int r = 8 * h + e;
+        if constexpr (PWAVE) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            pf[mb][r + u] = fast_exp2(__builtin_fmaf(sd[mb][r + u], c, -st4[mb][(r + u) >> 2][(r + u) & 3]));
+          op[mb][h][(r >> 1) & 3] = pack_bf16(pf[mb][r], pf[mb][r + 1]);
+        } else {
+          const unsigned w = op[mb][h][(r >> 1) & 3];
+          const float p0 = __uint_as_float(w << 16), p1 = __uint_as_float(w & 0xffff0000u);
+          op[mb][h][(r >> 1) & 3] = pack_bf16(p0 * (sd[mb][r] - st4[mb][r >> 2][r & 3]),
+                                              p1 * (sd[mb][r + 1] - st4[mb][(r + 1) >> 2][(r + 1) & 3]));
+        }
+      }
+    };
+    auto read_op = [&](auto J) __attribute__((always_inline)) -> u32x4 {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j < 2 * KS) {
+        constexpr int ks = j % KS;
+        return lds_read16(rlo + ro[ks % C::RO] + (ks / C::RO) * 256 + (j / KS) * 32 * C::ROWB);
+      } else {
+        constexpr int i = j - 2 * KS, db = i % DB, mb = i / (2 * DB), h = (i / DB) & 1;
+        const int rowsel = (32 * mb + 16 * h) * C::ROWB;
+        return tr_pair(tlo + to[db] + rowsel, tlo + to8[db] + rowsel);
+      }
+    };
+    auto mfma_step = [&](auto J, u32x4 a) __attribute__((always_inline)) {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j < 2 * KS) {
+        sd[j / KS] = mfma32x32x16(a, kv[j % KS], sd[j / KS]);
+      } else {
+        constexpr int i = j - 2 * KS, db = i % DB, mb = i / (2 * DB), h = (i / DB) & 1;
+        acc[db] = mfma32x32x16(a, op[mb][h], acc[db]);
+      }
+    };
+    auto valu_step = [&](auto J) __attribute__((always_inline)) {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j == 0) {
+        load_stats(0);
+        if constexpr (!PWAVE) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) op[mb][h] = lds_read16(pfrag + (2 * mb + h) * 1024);
+        }
+      }
+      if constexpr (j == KS) load_stats(1);
+      static_for<0, 4>([&](auto MH) __attribute__((always_inline)) {
+        constexpr int mb = decltype(MH)::value / 2, h = decltype(MH)::value % 2;
+        constexpr int lo = h == 0 ? ready(mb) : use(mb, 0), hi = use(mb, h), n = hi - lo;
+        if constexpr (j >= lo && j < hi) {
+          constexpr int e0 = 2 * ((4 * (j - lo)) / n), e1 = 2 * ((4 * (j - lo + 1)) / n);
+          values(mb, h, e0, e1);
+          if constexpr (PWAVE && j == hi - 1) {
+            if (fix) causal_fixup(mb, h);
+            *(FA2_LDS u32x4*)(pfrag + (2 * mb + h) * 1024) = op[mb][h];
+          }
+        }
+      });
+    };
+    u32x4 ring[PF + 1];
+    static_for<0, PF>([&](auto J) __attribute__((always_inline)) { ring[decltype(J)::value] = read_op(J); });
+    static_for<0, NS>([&](auto J) __attribute__((always_inline)) {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j + PF < NS) ring[(j + PF) % (PF + 1)] = read_op(std::integral_constant<int, j + PF>{});
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(J, ring[j % (PF + 1)]);
+      valu_step(J);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // Each role runs its own copy of the loop (the barriers match one to one: both run
+  // iters + 1 steps), so the two register sets never meet at a branch merge.
+  auto run = [&](auto PW) __attribute__((always_inline)) {
+    constexpr bool PWAVE = decltype(PW)::value;
+    // K (sign-flipped when scale < 0) or V of the pair's 32 keys as B operands.
+    u32x4 kv[KS];
+    {
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc((PWAVE ? p.k : p.v) + kvoff, head_bytes);
+      const unsigned flip = PWAVE ? p.kneg : 0u;
+      const uint32_t row = (uint32_t)(kw + l32);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kv[ks] = buffer_load16(rs, row * C::ROWB + (16 * ks + 8 * hf) * 2) ^ flip;
+    }
+    f32x16 acc[DB];  // dV^T or dK^T: rows = head dim, columns = keys (lanes)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+    // Step s: the P waves take tile s, their partners tile s - 1; tile s + 1 is fetched into
+    // the third stage. The barrier at the end orders P(s) before its reads and frees stage
+    // s - 1 for the next fetch.
+    Cursor fc{0, 0}, tc{0, 0};  // the tile fetched next (s + 1) and the one this wave takes
+    advance(fc);
+    auto step = [&](auto S, int s) __attribute__((always_inline)) {
+      constexpr int st = decltype(S)::value;
+      using SN = std::integral_constant<int, (st + 1) % 3>;
+      using SP = std::integral_constant<int, (st + 2) % 3>;
+      fetch(SN{}, s + 1, fc);
+      advance(fc);
+      const int t = PWAVE ? s : s - 1;
+      if (t >= 0 && t < iters) {
+        const int qrow0 = (qt_top - tc.u) * C::BT;
+        advance(tc);
+        // Causal: skip tiles wholly above the pair's keys or past their window.
+        const bool skip = (p.causal && qrow0 + C::BT - 1 < kw) || qrow0 > kw + PC::RPW - 1 + W;
+        lds_char* pb = (lds_char*)((t & 1) ? t7_pbuf1 : t6_pbuf0);
+        if (!skip) {
+          // dO stages 1 and 2 lie at 64 KB and above.
+          if constexpr (PWAVE) {
+            const bool fix = (p.causal && qrow0 < kw + PC::RPW - 1) || qrow0 + C::BT - 1 > kw + W;
+            tile(PW, std::false_type{}, std::bool_constant<D == 128 && st != 0>{}, kv, acc, q_st(S),
+                 do_st(S), stat_st(S) + 1024, pb, qrow0, fix);
+          } else {
+            tile(PW, std::bool_constant<D == 128 && SP::value != 0>{}, std::false_type{}, kv, acc,
+                 do_st(SP{}), q_st(SP{}), stat_st(SP{}), pb, qrow0, false);
+          }
+        }
+      }
+      wait_vmem_all();
+      __syncthreads();
+    };
+
+    int s = 0;
+    for (; s + 3 <= iters + 1; s += 3) {
+      step(I0{}, s);
+      step(I1{}, s + 1);
+      step(I2{}, s + 2);
+    }
+    if (s <= iters) step(I0{}, s);
+    if (s + 1 <= iters) step(I1{}, s + 1);
+
+    // Store dV, or dK = scale dK^T^T: lane = key, registers = head dim.
+    if (key < N) {
+      float* row = (PWAVE ? p.dv : p.dk) + kvoff + (size_t)key * D;
+      const float f = PWAVE ? 1.f : p.scale;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq)
+          *(f32x4*)(row + 32 * db + 8 * rq + 4 * hf) =
+              f32x4{acc[db][4 * rq], acc[db][4 * rq + 1], acc[db][4 * rq + 2], acc[db][4 * rq + 3]} * f;
+    }
+  };
+
+  wait_vmem_all();
+  __syncthreads();
+  if (pwave)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
+}
+
 // ------------------------------------------------------------------ 3. dQ
 
 template <int D>
@@ -793,13 +1146,13 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
   p.dv = dv;
   p.nblk = (s.N + BwdCfg<128>::BR - 1) / BwdCfg<128>::BR;
   const int ndh = s.d == 256 ? BwdCfg<256>::NDH : 1;
-  const dim3 grid((unsigned)(s.B * s.Hkv * p.nblk * ndh)), block(BwdCfg<128>::WAVES * 64);
+  const dim3 grid((unsigned)(s.B * s.Hkv * p.nblk * ndh));
   if (s.d == 128)
-    hipLaunchKernelGGL(fa2_bwd_dkdv_kernel<128>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL(fa2_bwd_dkdv_pair_kernel<128>, grid, dim3(PairCfg<128>::WAVES * 64), 0, stream, p);
   else if (s.d == 256)
-    hipLaunchKernelGGL(fa2_bwd_dkdv_kernel<256>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL(fa2_bwd_dkdv_kernel<256>, grid, dim3(BwdCfg<256>::WAVES * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL(fa2_bwd_dkdv_kernel<64>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL(fa2_bwd_dkdv_pair_kernel<64>, grid, dim3(PairCfg<64>::WAVES * 64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -108,6 +108,15 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // stay in AGPRs across the loop instead of being copied out and back every iteration.
 __device__ __forceinline__ void agpr_accumulators_hint() { asm volatile("" ::"a"(0.0f)); }
 
+// x + C through an add the optimiser cannot see into (it stays one add, not folded into the
+// address arithmetic of every later use).
+template <int C>
+__device__ __forceinline__ int opaque_add(int x) {
+  int r;
+  asm("v_add_u32 %0, %1, %2" : "=v"(r) : "i"(C), "v"(x));
+  return r;
+}
+
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // LDS tiles of bf16 rows of D elements (D / 8 chunks of 16 bytes per row). The 64 banks form

@@ -154,6 +154,50 @@ def test_backward_deterministic_and_stream():
         assert torch.equal(x, y)
 
 
+def test_concurrent_calls_on_two_streams():
+    """Two host threads drive forward + backward on their own streams at the same time; the
+    library keeps no state between calls, so each result equals the one computed alone."""
+    import threading
+    import torch
+    cases = [(H.make_inputs(4250, 2, 8, 2, 1500, 128, with_do=True), True, 0.09),
+             (H.make_inputs(4251, 1, 4, 4, 700, 64, with_do=True), False, 0.125)]
+    dev = [tuple(H.to_dev(x) for x in arrs) for arrs, _, _ in cases]
+    torch.cuda.synchronize()
+
+    def fwd_bwd(i, stream):
+        (qd, kd, vd, dod), (_, causal, scale) = dev[i], cases[i]
+        o, lse = fa2.forward(qd, kd, vd, causal, scale, stream=stream)
+        return (o, lse) + fa2.backward(qd, kd, vd, o, lse, dod, causal, scale, stream=stream)
+
+    alone = [fwd_bwd(i, None) for i in range(2)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    results = [[], []]
+    errors = []
+
+    def worker(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                for _ in range(4):
+                    results[i].append(fwd_bwd(i, streams[i]))
+        except Exception as e:  # reported below, on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for st in streams:
+        st.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        assert len(results[i]) == 4
+        for res in results[i]:
+            for x, y in zip(res, alone[i]):
+                assert torch.equal(x, y)
+
+
 def test_backward_rejects_small_workspace():
     import torch
     q, k, v, dO = H.make_inputs(4300, 1, 2, 2, 64, 64, with_do=True)
