@@ -15,8 +15,8 @@
 //                   dV, the second keeps V and makes dS and dK from the P its partner leaves
 //                   in LDS. Head dim 256: four waves, each with its 32 keys' K, V and dK, dV.
 //   3. dQ           one workgroup per (batch, query head, query block); each wave keeps its
-//                   queries' Q, dO and fp32 dQ^T in registers (64 queries, 32 at head dim
-//                   256) and walks the key tiles.
+//                   32 queries' Q, dO and fp32 dQ^T in registers and walks the key tiles
+//                   (eight waves, two per SIMD; four at head dim 256).
 // Q/dO (dK/dV kernels) and K/V (dQ kernel) tiles stream into LDS by buffer_load ... lds, in
 // two or three stages, in a layout that serves both 16-byte row reads and the transposing
 // ds_read_b64_tr_b16 reads without bank conflicts.
@@ -794,12 +794,15 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------ 3. dQ
 
-template <int D>
+template <int D, int NW = 4>
 struct DqCfg {
-  static constexpr int WAVES = 4;           // one wave per SIMD
-  // Query rows per wave: two 32-row blocks qb up to d = 128 (each K/V fragment read feeds two
-  // MFMAs); at d = 256 the Q and dO operands of one block already take 128 registers.
-  static constexpr int NQB = D <= 128 ? 2 : 1;
+  static constexpr int WAVES = NW;          // one (4) or two (8) waves per SIMD
+  static constexpr int WPE = NW / 4;
+  // Query rows per wave. Two waves per SIMD (head dims 64, 128): one 32-row block each, every
+  // accumulator in VGPRs, and one wave's exponentials run beside the other's MFMAs. One wave
+  // per SIMD: two blocks up to d = 128 (each K/V fragment read feeds two MFMAs); at d = 256
+  // the Q and dO operands of one block already take 128 registers.
+  static constexpr int NQB = D <= 128 && NW == 4 ? 2 : 1;
   static constexpr int RPW = 32 * NQB;
   static constexpr int BR = WAVES * RPW;    // query rows per workgroup
   static constexpr int BT = 64;             // keys per streamed tile: two 32-key halves
@@ -810,12 +813,12 @@ struct DqCfg {
   static constexpr int STAGES = D <= 128 ? 3 : 2;
 };
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DqCfg<D, NW>::WPE, DqCfg<D, NW>::WPE)))
 void fa2_bwd_dq_kernel(BwdParams p) {
   using C = BwdCfg<D>;
-  using Q = DqCfg<D>;
-  static_assert(Q::WAVES == C::WAVES && Q::BT == C::BT, "tiles are loaded by load_tile_dual");
+  using Q = DqCfg<D, NW>;
+  static_assert(Q::BT == C::BT, "tiles are loaded by load_tile_dual");
   constexpr int KS = C::KS, DB = Q::DB, NQB = Q::NQB;
   // K and V stages in separate arrays (a DMA into one never aliases reads of another).
   constexpr int TILE3 = Q::STAGES == 3 ? Q::TILE : 1024;
@@ -829,7 +832,7 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
-  agpr_accumulators_hint();
+  if constexpr (NW == 4) agpr_accumulators_hint();
   const int N = p.N;
   int bh, r;
   map_slice_block(blockIdx.x, p.B * p.Hq, p.nblk, bh, r);
@@ -868,8 +871,8 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   // the end read as zero).
   auto fetch = [&](auto S, int t) __attribute__((always_inline)) {
     if (t > ntiles) return;
-    load_tile_dual<D>(rk, kst(S), (tbase + t) * Q::BT, wave, lane);
-    load_tile_dual<D>(rv, vst(S), (tbase + t) * Q::BT, wave, lane);
+    load_tile_dual<D, NW>(rk, kst(S), (tbase + t) * Q::BT, wave, lane);
+    load_tile_dual<D, NW>(rv, vst(S), (tbase + t) * Q::BT, wave, lane);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -1160,15 +1163,16 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
                          const float* ws, float* dq, const AttnShape& s, hipStream_t stream) {
   BwdParams p = make_params(q, k, v, dO, const_cast<float*>(ws), s);
   p.dq = dq;
-  const int BR = s.d == 256 ? DqCfg<256>::BR : DqCfg<128>::BR;
+  constexpr int NW = 8;  // head dims 64 and 128: two waves per SIMD (measured 5-20 % faster)
+  const int BR = s.d == 256 ? DqCfg<256>::BR : DqCfg<128, NW>::BR;
   p.nblk = (s.N + BR - 1) / BR;
-  const dim3 grid((unsigned)(s.B * s.Hq * p.nblk)), block(DqCfg<128>::WAVES * 64);
+  const dim3 grid((unsigned)(s.B * s.Hq * p.nblk));
   if (s.d == 128)
-    hipLaunchKernelGGL(fa2_bwd_dq_kernel<128>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL((fa2_bwd_dq_kernel<128, NW>), grid, dim3(NW * 64), 0, stream, p);
   else if (s.d == 256)
-    hipLaunchKernelGGL(fa2_bwd_dq_kernel<256>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL((fa2_bwd_dq_kernel<256, 4>), grid, dim3(4 * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL(fa2_bwd_dq_kernel<64>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL((fa2_bwd_dq_kernel<64, NW>), grid, dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
