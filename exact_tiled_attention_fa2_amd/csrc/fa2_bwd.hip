@@ -35,7 +35,7 @@ struct BwdParams {
   float* dq;
   float* dk;
   float* dv;
-  float* delta;  // D, [B,Hq,N]
+  float* delta;  // -D, [B,Hq,N]
   float* lse2;   // LSE * log2(e), [B,Hq,N]
   int B, Hq, Hkv, N;
   int causal;
@@ -131,8 +131,9 @@ __device__ __forceinline__ void map_slice_block(int bid, int nslices, int nblk, 
 
 // ------------------------------------------------------------------ 1. preprocess
 
-// delta[i] = D_i = sum_c dO_ic O_ic, and lse2[i] = LSE_i * log2(e) (so the kernels below form
-// P = 2^(s c - lse2) with one FMA and one exp2 per score).
+// delta[i] = -D_i = -sum_c dO_ic O_ic, and lse2[i] = LSE_i * log2(e): the kernels below form
+// P = 2^(s c - lse2) with one FMA and one exp2 per score, and start the dP accumulators from
+// -D, so that an MFMA chain ends at dP - D.
 template <int D>
 __global__ __launch_bounds__(256) void fa2_bwd_pre_kernel(const float* __restrict__ o,
                                                           const uint16_t* __restrict__ dO,
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(256) void fa2_bwd_pre_kernel(const float* __restric
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
   if (row < rows && part == 0) {
-    delta[row] = acc;
+    delta[row] = -acc;
     lse2[row] = lse[row] * kLog2e;
   }
 }
@@ -338,7 +339,7 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
         const int r = 2 * q;
         float dv2[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) dv2[u] = pf[mb][r + u] * (dp[mb][r + u] - d4[mb][(r + u) >> 2][(r + u) & 3]);
+        for (int u = 0; u < 2; ++u) dv2[u] = pf[mb][r + u] * (dp[mb][r + u] + d4[mb][(r + u) >> 2][(r + u) & 3]);
         pd[mb][r >> 3][(r >> 1) & 3] = pack_bf16(dv2[0], dv2[1]);
       }
     };
@@ -615,7 +616,7 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
     f32x16 sd[2] = {f32x16{}, f32x16{}};  // S (P waves) or dP
     u32x4 op[2][2];                        // [mb][h]: P or dS, 16 queries x 32 keys, packed bf16
     float pf[2][16];                       // P in fp32 until packed (P waves)
-    f32x4 st4[2][4];                       // lse2 (P waves) or D of the lane's rows
+    f32x4 st4[2][4];                       // lse2 (P waves) or -D of the lane's rows
     const FA2_LDS float* sbase = (const FA2_LDS float*)(stat - 131072 + opaque_add<131072>(16 * hf));
     auto load_stats = [&](int mb) __attribute__((always_inline)) {
 #pragma unroll
@@ -647,10 +648,10 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
             pf[mb][r + u] = fast_exp2(__builtin_fmaf(sd[mb][r + u], c, -st4[mb][(r + u) >> 2][(r + u) & 3]));
           op[mb][h][(r >> 1) & 3] = pack_bf16(pf[mb][r], pf[mb][r + 1]);
         } else {
+          // sd holds dP - D (its chain started from -D).
           const unsigned w = op[mb][h][(r >> 1) & 3];
           const float p0 = __uint_as_float(w << 16), p1 = __uint_as_float(w & 0xffff0000u);
-          op[mb][h][(r >> 1) & 3] = pack_bf16(p0 * (sd[mb][r] - st4[mb][r >> 2][r & 3]),
-                                              p1 * (sd[mb][r + 1] - st4[mb][(r + 1) >> 2][(r + 1) & 3]));
+          op[mb][h][(r >> 1) & 3] = pack_bf16(p0 * sd[mb][r], p1 * sd[mb][r + 1]);
         }
       }
     };
@@ -668,7 +669,17 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
     auto mfma_step = [&](auto J, u32x4 a) __attribute__((always_inline)) {
       constexpr int j = decltype(J)::value;
       if constexpr (j < 2 * KS) {
-        sd[j / KS] = mfma32x32x16(a, kv[j % KS], sd[j / KS]);
+        constexpr int mb = j / KS;
+        if constexpr (!PWAVE && j % KS == 0) {
+          // dP chain of row block mb starts from -D (register r holds row 8 (r/4) + 4 hf + r%4).
+          const f32x16 init = {st4[mb][0][0], st4[mb][0][1], st4[mb][0][2], st4[mb][0][3],
+                               st4[mb][1][0], st4[mb][1][1], st4[mb][1][2], st4[mb][1][3],
+                               st4[mb][2][0], st4[mb][2][1], st4[mb][2][2], st4[mb][2][3],
+                               st4[mb][3][0], st4[mb][3][1], st4[mb][3][2], st4[mb][3][3]};
+          sd[mb] = mfma32x32x16(a, kv[0], init);
+        } else {
+          sd[mb] = mfma32x32x16(a, kv[j % KS], sd[mb]);
+        }
       } else {
         constexpr int i = j - 2 * KS, db = i % DB, mb = i / (2 * DB), h = (i / DB) & 1;
         acc[db] = mfma32x32x16(a, op[mb][h], acc[db]);
@@ -677,15 +688,16 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
     auto valu_step = [&](auto J) __attribute__((always_inline)) {
       constexpr int j = decltype(J)::value;
       if constexpr (j == 0) {
-        load_stats(0);
-        if constexpr (!PWAVE) {
+        if constexpr (PWAVE) {
+          load_stats(0);
+        } else {
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int h = 0; h < 2; ++h) op[mb][h] = lds_read16(pfrag + (2 * mb + h) * 1024);
         }
       }
-      if constexpr (j == KS) load_stats(1);
+      if constexpr (PWAVE && j == KS) load_stats(1);
       static_for<0, 4>([&](auto MH) __attribute__((always_inline)) {
         constexpr int mb = decltype(MH)::value / 2, h = decltype(MH)::value % 2;
         constexpr int lo = h == 0 ? ready(mb) : use(mb, 0), hi = use(mb, h), n = hi - lo;
@@ -699,6 +711,10 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
         }
       });
     };
+    if constexpr (!PWAVE) {
+      load_stats(0);  // -D initialises the dP chains
+      load_stats(1);
+    }
     u32x4 ring[PF + 1];
     static_for<0, PF>([&](auto J) __attribute__((always_inline)) { ring[decltype(J)::value] = read_op(J); });
     static_for<0, NS>([&](auto J) __attribute__((always_inline)) {
@@ -882,7 +898,8 @@ void fa2_bwd_dq_kernel(BwdParams p) {
 
   // Q and dO of this wave's queries as B operands (lane = query, k = head dim).
   u32x4 qf[NQB][KS], df[NQB][KS];
-  float lse2v[NQB], dltv[NQB];
+  float lse2v[NQB];
+  f32x16 negd[NQB];  // -D of the lane's query in every register: the start of each dP chain
   {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + qoff, head_bytes);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dO + qoff, head_bytes);
@@ -896,7 +913,9 @@ void fa2_bwd_dq_kernel(BwdParams p) {
         df[qb][ks] = buffer_load16(rd, off);
       }
       lse2v[qb] = qi < N ? p.lse2[(size_t)bh * N + qi] : 0.f;
-      dltv[qb] = qi < N ? p.delta[(size_t)bh * N + qi] : 0.f;
+      const float nd = qi < N ? p.delta[(size_t)bh * N + qi] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) negd[qb][r] = nd;
     }
   }
 
@@ -942,8 +961,8 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   // dS element pairs q in h-major order, so pd[.][0] is complete before pd[.][1].
   auto ds_pair = [&](int q) __attribute__((always_inline)) {
     const int h = q / (4 * NQB), qb = (q / 4) % NQB, rr = 8 * h + 2 * (q % 4);
-    const float a = pf[qb][rr] * (dp[qb][rr] - dltv[qb]);
-    const float bb = pf[qb][rr + 1] * (dp[qb][rr + 1] - dltv[qb]);
+    const float a = pf[qb][rr] * dp[qb][rr];  // dp holds dP - D
+    const float bb = pf[qb][rr + 1] * dp[qb][rr + 1];
     pd[qb][h][(rr >> 1) & 3] = pack_bf16(a, bb);
   };
   // Causal: zero P^T outside query - window <= key <= query, for a half (first key 32 ua)
@@ -982,7 +1001,7 @@ void fa2_bwd_dq_kernel(BwdParams p) {
       constexpr int j = decltype(J)::value;
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        // S(u+1) and dP(u+1) start from zero; dP(u) stays live until dS(u) is done.
+        // S(u+1) starts from zero and dP(u+1) from -D; dP(u) stays live until dS(u) is done.
         if constexpr (j < KS) {
           s[qb] = mfma32x32x16(a, qf[qb][j], j == 0 ? f32x16{} : s[qb]);
         } else if constexpr (j < KS + 2 * DB) {
@@ -990,7 +1009,7 @@ void fa2_bwd_dq_kernel(BwdParams p) {
           adq[qb][db] = mfma32x32x16(a, pd[qb][h], adq[qb][db]);
         } else {
           constexpr int ks = j - KS - 2 * DB;
-          dp[qb] = mfma32x32x16(a, df[qb][ks], ks == 0 ? f32x16{} : dp[qb]);
+          dp[qb] = mfma32x32x16(a, df[qb][ks], ks == 0 ? negd[qb] : dp[qb]);
         }
       }
     };
@@ -1028,7 +1047,7 @@ void fa2_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       s[qb] = f32x16{};
-      dp[qb] = f32x16{};
+      dp[qb] = negd[qb];
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {

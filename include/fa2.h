@@ -79,9 +79,10 @@ int fa2_forward(const void* q, const void* k, const void* v, float* o, float* ls
                 int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                 hipStream_t stream);
 
-/* Bytes of device workspace fa2_backward needs: two floats per query row (D = rowsum(dO*O)
-   and LSE*log2(e)), rounded up to 256 bytes. 0 for an empty problem or negative sizes.
-   Layout, with R = B*Hq*N: D at floats [0, R), LSE*log2(e) at floats [R, 2R). */
+/* Bytes of device workspace fa2_backward needs: two floats per query row (-D, with
+   D = rowsum(dO*O), and LSE*log2(e)), rounded up to 256 bytes. 0 for an empty problem or
+   negative sizes. Layout, with R = B*Hq*N: -D at floats [0, R), LSE*log2(e) at floats [R, 2R)
+   (the kernels start their dP accumulators from -D). */
 size_t fa2_backward_workspace_size(int B, int Hq, int N);
 
 /*
@@ -110,7 +111,7 @@ int fa2_backward(const void* q, const void* k, const void* v, const float* o, co
  * fa2_backward; `workspace` must be at least fa2_backward_workspace_size(B,Hq,N) bytes.
  *
  * fa2_backward_preprocess: fills the workspace from o f32 [B,Hq,N,d], dO bf16 [B,Hq,N,d] and
- *   lse f32 [B,Hq,N] (all read only): D_i = sum_c dO_ic o_ic and LSE_i * log2(e).
+ *   lse f32 [B,Hq,N] (all read only): -D_i = -sum_c dO_ic o_ic and LSE_i * log2(e).
  */
 int fa2_backward_preprocess(const float* o, const void* dO, const float* lse, void* workspace,
                             size_t workspace_bytes, int B, int Hq, int N, int d,

@@ -231,6 +231,31 @@ def test_phases_match_composed_backward():
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_preprocess_workspace_layout(d):
+    """fa2_backward_preprocess leaves -D (D_i = sum_c dO_ic O_ic) at floats [0, R) and
+    LSE * log2(e) at [R, 2R), R = B*Hq*N, as the header documents."""
+    import torch
+    B, Hq, Hkv, N = 2, 3, 3, 100
+    q, k, v, dO = H.make_inputs(4500 + d, B, Hq, Hkv, N, d, with_do=True)
+    qd, kd, vd, dod = H.to_dev(q), H.to_dev(k), H.to_dev(v), H.to_dev(dO)
+    o, lse = fa2.forward(qd, kd, vd, True, 0.1)
+    W = fa2.fa2_backward_workspace_size(B, Hq, N)
+    ws = torch.full((W // 4,), float("nan"), dtype=torch.float32, device=qd.device)
+    assert fa2.fa2_backward_preprocess(o, dod, lse, ws, W, B, Hq, N, d) == 0
+    torch.cuda.synchronize()
+    R = B * Hq * N
+    got = ws.cpu().numpy().astype(np.float64)
+    o64 = o.cpu().numpy().astype(np.float64)
+    want_negd = -np.einsum("bhnc,bhnc->bhn", H.f64(dO), o64).reshape(-1)
+    want_lse2 = lse.cpu().numpy().astype(np.float64).reshape(-1) * np.log2(np.e)
+    assert np.abs(got[:R] - want_negd).max() <= 1e-5 * (1 + np.abs(want_negd).max())
+    assert np.abs(got[R:2 * R] - want_lse2).max() <= 1e-5 * (1 + np.abs(want_lse2).max())
+    # -D against the oracle's D = sum_j P_ij dP_ij (a different route to the same value).
+    _, _, D = oracle.row_stats(H.f64(q), H.f64(k), H.f64(v), H.f64(dO), True, 0.1)
+    assert np.abs(-got[:R] - D.reshape(-1)).max() <= 2e-2 * (1 + np.abs(D).max())
+
+
 # Head dim 256: dK/dV in two passes over head-dim halves, dQ with one 32-row block per wave and
 # a two-stage K/V ring.
 @pytest.mark.parametrize("causal", [False, True])
