@@ -164,12 +164,12 @@ __global__ __launch_bounds__(256) void fa2_bwd_pre_kernel(const float* __restric
 
 // ------------------------------------------------------------------ 2. dK / dV
 
-// Q and dO tiles: stage s holds 64 query rows of Q, of dO, and [D | lse2] of those rows.
+// Q and dO tiles: stage s holds 64 query rows of Q, of dO, and [-D | lse2] of those rows.
 template <int D>
 struct DkdvStage {
   lds_char* q;
   lds_char* dO;
-  lds_char* stat;  // D at +0 (64 floats), lse2 at +1024 bytes
+  lds_char* stat;  // -D at +0 (64 floats), lse2 at +1024 bytes
 };
 
 template <int D>
@@ -226,7 +226,7 @@ void fa2_bwd_dkdv_kernel(BwdParams p) {
     load_tile_dual<D>(make_rsrc(p.q + qoff, head_bytes), st.q, qrow0, wave, lane);
     load_tile_dual<D>(make_rsrc(p.dO + qoff, head_bytes), st.dO, qrow0, wave, lane);
     if (wave == 0) {
-      // D and lse2 of the tile's 64 rows; lanes past 15 read past the end (zeros).
+      // -D and lse2 of the tile's 64 rows; lanes past 15 read past the end (zeros).
       const size_t roff = ((size_t)b * p.Hq + hq) * (size_t)N;
       const uint32_t off = lane < 16 ? (uint32_t)(qrow0 + 4 * lane) * 4 : (uint32_t)N * 4;
       buffer_load16_lds(make_rsrc(p.delta + roff, (uint32_t)N * 4), st.stat, off);
@@ -558,7 +558,7 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
       buffer_load16_lds(rd, do_st(S) + (wave * LPW + t) * 1024, off);
     }
     if (wave == 0) {
-      // D and lse2 of the tile's 64 rows; lanes past 15 read past the end (zeros).
+      // -D and lse2 of the tile's 64 rows; lanes past 15 read past the end (zeros).
       const size_t roff = ((size_t)b * p.Hq + hq) * (size_t)N;
       const uint32_t off = lane < 16 ? (uint32_t)(qrow0 + 4 * lane) * 4 : (uint32_t)N * 4;
       buffer_load16_lds(make_rsrc(p.delta + roff, (uint32_t)N * 4), stat_st(S), off);
