@@ -311,8 +311,10 @@ void fa2_fwd_kernel(FwdParams p) {
   // One tile's MFMA stream: the S^T = K Q^T slots (k-step ks, key block kb; kb fastest) if
   // HAS_S, then the O^T += V^T P^T slots if HAS_PV. Every LDS operand is read LA slots ahead
   // of its MFMA from a ring of LA + 1 operands, so the reads of the P V phase start during the
-  // last S slots. also_s(ks) and also_pv(i) are VALU work slotted after the MFMAs of S k-step
-  // ks and P V step i; scheduling fences keep this order.
+  // last S slots. also_s(ks) and also_pv(i) are VALU work placed after the MFMAs of S k-step
+  // ks and P V step i. Up to d = 128 the compiler's scheduler interleaves them (fences around
+  // each slot measured 1-2 % slower); at d = 256 (one wave per SIMD) fences keep the slot
+  // order, which measured 9 % faster there.
   auto mfma_stream = [&](auto has_s, auto has_pv, const lds_char* kt, STile& sn, const lds_char* vt,
                          PTile& pf, auto&& also_s, auto&& also_pv) __attribute__((always_inline)) {
     constexpr bool HAS_S = decltype(has_s)::value, HAS_PV = decltype(has_pv)::value;
@@ -336,7 +338,7 @@ void fa2_fwd_kernel(FwdParams p) {
     static_for<0, NOP>([&](auto J) __attribute__((always_inline)) {
       constexpr int j = decltype(J)::value;
       if constexpr (j + LA < NOP) load(std::integral_constant<int, j + LA>{});
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (D == 256) __builtin_amdgcn_sched_barrier(0);
       if constexpr (j < NSS) {
         constexpr int ks = j >> 1, kb = j & 1;
 #pragma unroll
@@ -349,7 +351,7 @@ void fa2_fwd_kernel(FwdParams p) {
         for (int qb = 0; qb < C::NQB; ++qb) acc[qb][db] = mfma32x32x16(vring[j % (LA + 1)], pf[qb][kb][h], acc[qb][db]);
         also_pv(i);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (D == 256) __builtin_amdgcn_sched_barrier(0);
     });
   };
   auto rescale_if_needed = [&](const float (&mx)[C::NQB]) {
