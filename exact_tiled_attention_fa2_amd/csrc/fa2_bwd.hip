@@ -10,10 +10,10 @@
 // the wiki article "FlashAttention-2" stresses in its performance section):
 //   1. preprocess   D_i = sum_c dO_ic O_ic                   (one value per query row)
 //   2. dK/dV        one workgroup per (batch, KV head, 128-key block), walking every query
-//                   tile of every query head sharing the KV head. Head dims 64 and 128: four
-//                   pairs of waves, one pair per 32 keys; the first keeps K and makes P and
-//                   dV, the second keeps V and makes dS and dK from the P its partner leaves
-//                   in LDS. Head dim 256: four waves, each with its 32 keys' K, V and dK, dV.
+//                   tile of every query head sharing the KV head: four pairs of waves, one
+//                   pair per 32 keys; the first keeps K and makes P and dV, the second keeps
+//                   V and makes dS and dK from the P its partner leaves in LDS (head dim 256:
+//                   32-row tiles and two passes over head-dim halves).
 //   3. dQ           one workgroup per (batch, query head, query block); each wave keeps its
 //                   32 queries' Q, dO and fp32 dQ^T in registers and walks the key tiles
 //                   (eight waves, two per SIMD; four at head dim 256).
@@ -46,17 +46,14 @@ struct BwdParams {
   int window;     // causal window: query i sees keys i - window .. i (>= N: no window)
 };
 
+// Shared by the dK/dV and dQ kernels: 64-row tiles of bf16 rows, read as 16-byte rows and by
+// transposing reads.
 template <int D>
 struct BwdCfg {
-  static constexpr int WAVES = 4;
-  static constexpr int RPW = 32;            // rows (keys or queries) each wave owns
-  static constexpr int BR = WAVES * RPW;    // rows per workgroup
+  static constexpr int WAVES = 4;           // waves the tile loader splits a tile over by default
+  static constexpr int BR = 128;            // keys per dK/dV workgroup
   static constexpr int BT = 64;             // rows per streamed tile
   static constexpr int KS = D / 16;         // k-steps of a contraction over the head dim
-  // dK/dV accumulate up to 128 head-dim columns per pass (32 fp32 registers per column block
-  // and wave); d = 256 takes two passes (NDH), each recomputing S and dP over the full d.
-  static constexpr int DB = (D <= 128 ? D : 128) / 32;
-  static constexpr int NDH = D / (DB * 32);
   static constexpr int ROWB = D * 2;
   static constexpr int TILE = BT * ROWB;
   static constexpr int RO = KS < 8 ? KS : 8;  // distinct row-read offsets (chunks 16+ add 256 B)
@@ -162,307 +159,41 @@ __global__ __launch_bounds__(256) void fa2_bwd_pre_kernel(const float* __restric
   }
 }
 
-// ------------------------------------------------------------------ 2. dK / dV
+// ------------------------------------------------------------------ 2. dK / dV, paired waves
 
-// Q and dO tiles: stage s holds 64 query rows of Q, of dO, and [-D | lse2] of those rows.
-template <int D>
-struct DkdvStage {
-  lds_char* q;
-  lds_char* dO;
-  lds_char* stat;  // -D at +0 (64 floats), lse2 at +1024 bytes
-};
-
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void fa2_bwd_dkdv_kernel(BwdParams p) {
-  using C = BwdCfg<D>;
-  // Two stages, each in separate arrays (DMA into one stage never aliases reads of the other).
-  __shared__ __attribute__((aligned(1024))) char q_st0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char q_st1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char do_st0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char do_st1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char stat_st0[2048];
-  __shared__ __attribute__((aligned(1024))) char stat_st1[2048];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hf = lane >> 5, l32 = lane & 31;
-  agpr_accumulators_hint();
-  const int N = p.N;
-  int bg, kblk, dh;  // causal: low key blocks see the most queries and go first
-  map_slice_block(blockIdx.x, p.B * p.Hkv, p.nblk * C::NDH, bg, kblk);
-  dh = kblk % C::NDH;  // which 128-column half of dK/dV this workgroup accumulates (d = 256)
-  kblk /= C::NDH;
-  const int b = bg / p.Hkv, g = bg % p.Hkv;
-  const int G = p.Hq / p.Hkv;
-  const int k0 = kblk * C::BR;
-  const int kw = k0 + wave * C::RPW;  // this wave's first key
-
-  const uint32_t head_bytes = (uint32_t)N * C::ROWB;
-  const size_t kvoff = ((size_t)b * p.Hkv + g) * (size_t)N * D;
-
-  // Query tiles: every query head of the group, tiles from the one holding key k0 up to the
-  // last one that sees a key of the block (the end, unless a window stops earlier), walked
-  // from the TOP tile down, so all key blocks of a head start on the same tiles and read them
-  // at about the same time (shared through L2 instead of each block from HBM).
-  const int W = p.window;
-  const int nqt_all = (N + C::BT - 1) / C::BT;
-  const int qt0 = p.causal ? k0 / C::BT : 0;
-  const int qt_top = min(nqt_all - 1, (k0 + C::BR - 1 + W) / C::BT);
-  const int nqt = qt_top - qt0 + 1;
-  const int iters = G * nqt;
-  auto tile_row0 = [&](int it) { return (qt_top - it % nqt) * C::BT; };
-
-  auto stage = [&](int s) {
-    return s ? DkdvStage<D>{(lds_char*)q_st1, (lds_char*)do_st1, (lds_char*)stat_st1}
-             : DkdvStage<D>{(lds_char*)q_st0, (lds_char*)do_st0, (lds_char*)stat_st0};
-  };
-  auto fetch = [&](int it) {
-    if (it >= iters) return;
-    const DkdvStage<D> st = stage(it & 1);
-    const int hq = g * G + it / nqt;
-    const int qrow0 = tile_row0(it);
-    const size_t qoff = ((size_t)b * p.Hq + hq) * (size_t)N * D;
-    load_tile_dual<D>(make_rsrc(p.q + qoff, head_bytes), st.q, qrow0, wave, lane);
-    load_tile_dual<D>(make_rsrc(p.dO + qoff, head_bytes), st.dO, qrow0, wave, lane);
-    if (wave == 0) {
-      // -D and lse2 of the tile's 64 rows; lanes past 15 read past the end (zeros).
-      const size_t roff = ((size_t)b * p.Hq + hq) * (size_t)N;
-      const uint32_t off = lane < 16 ? (uint32_t)(qrow0 + 4 * lane) * 4 : (uint32_t)N * 4;
-      buffer_load16_lds(make_rsrc(p.delta + roff, (uint32_t)N * 4), st.stat, off);
-      buffer_load16_lds(make_rsrc(p.lse2 + roff, (uint32_t)N * 4), st.stat + 1024, off);
-    }
-  };
-
-  fetch(0);
-
-  // K and V of this wave's 32 keys as B operands (lane = key, k = head dim).
-  u32x4 kf[C::KS], vf[C::KS];
-  {
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + kvoff, head_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + kvoff, head_bytes);
-    const uint32_t row = (uint32_t)(kw + l32);
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const uint32_t off = row * C::ROWB + (16 * ks + 8 * hf) * 2;
-      kf[ks] = buffer_load16(rk, off) ^ p.kneg;
-      vf[ks] = buffer_load16(rv, off);
-    }
-  }
-  int roff[C::RO], toff[C::DB], toff8[C::DB];
-#pragma unroll
-  for (int ks = 0; ks < C::RO; ++ks) roff[ks] = row_read_off<D>(lane, ks);
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db) {
-    toff[db] = tr_read_off<D>(lane, dh * C::DB + db, 0);
-    toff8[db] = tr_read_off<D>(lane, dh * C::DB + db, 1);
-  }
-  // Row-read offset of k-step ks: the swizzle leaves chunk bit 4 alone, so k-steps 8.. repeat
-  // those of 0.. shifted by 16 chunks.
-  auto rowoff = [&](int ks) { return roff[ks % C::RO] + (ks / C::RO) * 256; };
-
-  f32x16 adk[C::DB], adv[C::DB];  // dK^T, dV^T: rows = head dim, columns = keys (lanes)
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db) {
-    adk[db] = f32x16{};
-    adv[db] = f32x16{};
-  }
-  const float c = p.c;
-  const int key = kw + l32;
-
-  // One query tile for this wave, as one unrolled sequence of NS MFMA steps:
-  //   S (Q K^T, row blocks mb = 0, 1) | dP (dO V^T) | dV^T += dO^T P | dK^T += Q^T dS.
-  // Each step issues the LDS read of the operand PF steps ahead, one MFMA, and a slice of
-  // VALU work whose inputs are complete by then: P = 2^(S c - lse2) of row block 0 while the
-  // S MFMAs of block 1 run, P of block 1 during dP of block 0, and dS = P (dP - D) of blocks
-  // 0 and 1 during dP of block 1 and the first dV steps; each packed operand is complete
-  // before the first MFMA that reads it. (Spreading the same work evenly over the tile
-  // measured slower: finishing the exponentials early lets dS and the dV/dK MFMAs follow
-  // sooner.) Scheduling fences keep the order.
-  // Rows past the end of the sequence need no mask: their Q, dO, D and LSE read as zero, so
-  // P = 1 there but dO = 0 and dS = 1 * (0 - 0) = 0, and they add nothing to dV or dK.
-  // A tile crossing the wave's causal diagonal or the end of its keys' window (fix) has P
-  // zeroed outside key <= query <= key + window, eight rows at a time, in the step that
-  // completes those rows' exponentials.
-  constexpr int KS = C::KS, DB = C::DB;
-  constexpr int NS = 4 * KS + 8 * DB;  // MFMA steps per tile
-  constexpr int PF = 3;                // operand reads in flight ahead of the MFMA using them
-  constexpr int DL = 2;                // steps between an accumulator's last MFMA and its use
-  constexpr int EXP_RATE = 16 / KS;    // P elements per step
-  constexpr int DS_STEPS = KS < 8 ? KS : 8;  // steps per row block's dS
-  constexpr int DS_RATE = 8 / DS_STEPS;      // dS element pairs per step
-  auto exp_start = [](int mb) { return KS + DL + KS * mb; };      // KS steps per row block
-  auto ds_start = [](int mb) { return 3 * KS + DL + KS * mb; };
-  auto tile = [&](const DkdvStage<D>& st, int qrow0, bool fix) __attribute__((always_inline)) {
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s[mb] = f32x16{};
-      dp[mb] = f32x16{};
-    }
-    float pf[2][16];           // P in fp32, kept for dS
-    u32x4 pp[2][2], pd[2][2];  // B operands [mb][h]: 16 queries x 32 keys, packed bf16
-    f32x4 lse4[2][4], d4[2][4];
-    const FA2_LDS float* dstat = (const FA2_LDS float*)st.stat;
-    const FA2_LDS float* lstat = (const FA2_LDS float*)(st.stat + 1024);
-    auto load_stats = [&](const FA2_LDS float* base, f32x4 (&dst)[2][4], int mb) __attribute__((always_inline)) {
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) dst[mb][rq] = *(const FA2_LDS f32x4*)(base + 32 * mb + 8 * rq + 4 * hf);
-    };
-    // Registers hold query rows 32 mb + 8 (r / 4) + 4 hf + r % 4 of row block mb; the row sees
-    // this lane's key iff lo <= 32 mb + 8 (r / 4) + r % 4 <= lo + window, lo = key - qrow0 - 4 hf.
-    auto causal_fixup = [&](int mb, int h) __attribute__((always_inline)) {
-      const int lo = key - qrow0 - 4 * hf;
-      const int hi = lo + W;
-#pragma unroll
-      for (int r = 8 * h; r < 8 * h + 8; r += 2) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int x = 32 * mb + 8 * ((r + u) >> 2) + ((r + u) & 3);
-          pf[mb][r + u] = (x >= lo && x <= hi) ? pf[mb][r + u] : 0.f;
-        }
-        pp[mb][h][(r >> 1) & 3] = pack_bf16(pf[mb][r], pf[mb][r + 1]);
-      }
-    };
-    // P elements [e0, e1) of row block mb; a pair is packed once both halves exist.
-    auto exp_part = [&](int mb, int e0, int e1) __attribute__((always_inline)) {
-#pragma unroll
-      for (int rr = e0; rr < e1; ++rr) {
-        pf[mb][rr] = fast_exp2(__builtin_fmaf(s[mb][rr], c, -lse4[mb][rr >> 2][rr & 3]));
-        if (rr & 1) pp[mb][rr >> 3][(rr >> 1) & 3] = pack_bf16(pf[mb][rr - 1], pf[mb][rr]);
-      }
-    };
-    // dS element pairs [q0, q1) of row block mb.
-    auto ds_part = [&](int mb, int q0, int q1) __attribute__((always_inline)) {
-#pragma unroll
-      for (int q = q0; q < q1; ++q) {
-        const int r = 2 * q;
-        float dv2[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) dv2[u] = pf[mb][r + u] * (dp[mb][r + u] + d4[mb][(r + u) >> 2][(r + u) & 3]);
-        pd[mb][r >> 3][(r >> 1) & 3] = pack_bf16(dv2[0], dv2[1]);
-      }
-    };
-    auto trread = [&](const lds_char* base, int i) __attribute__((always_inline)) {
-      const int db = i % DB, mb = i / (2 * DB), h = (i / DB) & 1;
-      const int rowsel = (32 * mb + 16 * h) * C::ROWB;
-      return tr_pair(base + toff[db] + rowsel, base + toff8[db] + rowsel);
-    };
-    auto read_op = [&](auto J) __attribute__((always_inline)) -> u32x4 {
-      constexpr int j = decltype(J)::value;
-      if constexpr (j < 2 * KS) return lds_read16(st.q + rowoff(j % KS) + (j / KS) * 32 * C::ROWB);
-      else if constexpr (j < 4 * KS) return lds_read16(st.dO + rowoff(j % KS) + ((j - 2 * KS) / KS) * 32 * C::ROWB);
-      else if constexpr (j < 4 * KS + 4 * DB) return trread(st.dO, j - 4 * KS);
-      else return trread(st.q, j - 4 * KS - 4 * DB);
-    };
-    auto mfma_step = [&](auto J, u32x4 a) __attribute__((always_inline)) {
-      constexpr int j = decltype(J)::value;
-      if constexpr (j < 2 * KS) {
-        s[j / KS] = mfma32x32x16(a, kf[j % KS], s[j / KS]);
-      } else if constexpr (j < 4 * KS) {
-        constexpr int jj = j - 2 * KS;
-        dp[jj / KS] = mfma32x32x16(a, vf[jj % KS], dp[jj / KS]);
-      } else if constexpr (j < 4 * KS + 4 * DB) {
-        constexpr int i = j - 4 * KS, db = i % DB, mb = i / (2 * DB), h = (i / DB) & 1;
-        adv[db] = mfma32x32x16(a, pp[mb][h], adv[db]);
-      } else {
-        constexpr int i = j - 4 * KS - 4 * DB, db = i % DB, mb = i / (2 * DB), h = (i / DB) & 1;
-        adk[db] = mfma32x32x16(a, pd[mb][h], adk[db]);
-      }
-    };
-    auto valu_step = [&](auto J) __attribute__((always_inline)) {
-      constexpr int j = decltype(J)::value;
-      if constexpr (j == 0) load_stats(lstat, lse4, 0);
-      if constexpr (j == exp_start(1) - 8) load_stats(lstat, lse4, 1);
-      if constexpr (j == ds_start(0) - 8) load_stats(dstat, d4, 0);
-      if constexpr (j == ds_start(1) - 8) load_stats(dstat, d4, 1);
-      static_for<0, 2>([&](auto MB) __attribute__((always_inline)) {
-        constexpr int mb = decltype(MB)::value;
-        constexpr int t = j - exp_start(mb);
-        if constexpr (t >= 0 && t < KS) {
-          constexpr int e0 = t * EXP_RATE, e1 = e0 + EXP_RATE;
-          exp_part(mb, e0, e1);
-          if constexpr (e1 % 8 == 0) {
-            if (fix) causal_fixup(mb, e1 / 8 - 1);
-          }
-        }
-        constexpr int u = j - ds_start(mb);
-        if constexpr (u >= 0 && u < DS_STEPS) ds_part(mb, u * DS_RATE, (u + 1) * DS_RATE);
-      });
-    };
-    u32x4 ring[PF + 1];
-    static_for<0, PF>([&](auto J) __attribute__((always_inline)) { ring[decltype(J)::value] = read_op(J); });
-    static_for<0, NS>([&](auto J) __attribute__((always_inline)) {
-      constexpr int j = decltype(J)::value;
-      if constexpr (j + PF < NS) ring[(j + PF) % (PF + 1)] = read_op(std::integral_constant<int, j + PF>{});
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_step(J, ring[j % (PF + 1)]);
-      valu_step(J);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-  };
-  auto sync_stage = [&]() {
-    wait_vmem_all();
-    __syncthreads();
-  };
-  auto step = [&](auto par_tag, int it) {
-    constexpr int PAR = decltype(par_tag)::value;  // it % 2
-    fetch(it + 1);
-    const DkdvStage<D> st = stage(PAR);
-    const int qrow0 = tile_row0(it);
-    // Causal: skip tiles wholly above this wave's keys or past their window; fix up tiles
-    // crossing the diagonal or the window's end.
-    const bool skip = (p.causal && qrow0 + C::BT - 1 < kw) || qrow0 > kw + C::RPW - 1 + W;
-    if (!skip) tile(st, qrow0, (p.causal && qrow0 < kw + C::RPW - 1) || qrow0 + C::BT - 1 > kw + W);
-    sync_stage();
-  };
-
-  sync_stage();
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  int it = 0;
-  for (; it + 1 < iters; it += 2) {
-    step(P0{}, it);
-    step(P1{}, it + 1);
-  }
-  if (it < iters) step(P0{}, it);
-
-  // ---- store dK = scale dK^T^T, dV: lane = key, registers = head dim (this pass's columns) ----
-  if (key < N) {
-    float* dkrow = p.dk + kvoff + (size_t)key * D + dh * C::DB * 32;
-    float* dvrow = p.dv + kvoff + (size_t)key * D + dh * C::DB * 32;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int col = 32 * db + 8 * rq + 4 * hf;
-        *(f32x4*)(dkrow + col) = f32x4{adk[db][4 * rq], adk[db][4 * rq + 1], adk[db][4 * rq + 2],
-                                       adk[db][4 * rq + 3]} * p.scale;
-        *(f32x4*)(dvrow + col) = f32x4{adv[db][4 * rq], adv[db][4 * rq + 1], adv[db][4 * rq + 2],
-                                       adv[db][4 * rq + 3]};
-      }
-  }
-}
-
-// ------------------------------------------------------------------ 2b. dK / dV, paired waves
-
-// Head dims up to 128: eight waves, two per SIMD, in four pairs that each own 32 keys. Wave w
+// Eight waves, two per SIMD, in four pairs that each own 32 keys. Wave w
 // (w < 4) keeps the keys' K and computes S = Q K^T, P = 2^(S c - lse2) and dV^T += dO^T P; it
 // leaves P in LDS as packed bf16, in the MFMA operand layout. Its partner w + 4, on the same
 // SIMD, keeps V and works one query tile behind: dP = dO V^T, dS = P (dP - D) from the P it
 // reads back, dK^T += Q^T dS. The two halves are one MFMA sequence on one register set (K or
 // V, dV^T or dK^T, S or dP, P or dS) with the row-read and transposed-read tiles swapped, so
-// a wave holds half the state of the single-wave kernel: everything stays in VGPRs, and a
-// SIMD runs the MFMAs of one wave beside the exponentials or dS arithmetic of the other.
-// P enters dS rounded to bf16, the value the dV product consumed.
+// a wave holds half the state of a wave doing all four products: everything stays in VGPRs,
+// and a SIMD runs the MFMAs of one wave beside the exponentials or dS arithmetic of the other.
+// P enters dS rounded to bf16, the value the dV product consumed. Q/dO tiles (and -D, lse2)
+// stream into LDS by buffer_load ... lds; rows past the end of the sequence need no mask:
+// their Q, dO, -D and LSE read as zero, so P = 1 there but dO = 0 and dS = 1 * (0 + 0) = 0,
+// and they add nothing to dV or dK.
 template <int D>
 struct PairCfg {
   static constexpr int WAVES = 8;
   static constexpr int PAIRS = 4;
   static constexpr int RPW = 32;             // keys per pair
   static constexpr int BR = PAIRS * RPW;     // keys per workgroup
-  static constexpr int PBUF = PAIRS * 4096;  // one tile's P: [pair][row block][half][lane] x 16 B
-  static_assert(BR == BwdCfg<D>::BR, "both dK/dV kernels use the same key blocks");
+  // Query rows per tile: 64 (two 32-row blocks) up to d = 128; 32 at d = 256, where three
+  // stages of Q and dO then still fit in LDS.
+  static constexpr int BT = D <= 128 ? 64 : 32;
+  static constexpr int NMB = BT / 32;
+  static constexpr int TILE = BT * 2 * D;
+  // dK/dV head-dim blocks a wave accumulates per pass: all of them up to d = 128; at d = 256 a
+  // wave's K (or V) and its full dK (or dV) would not fit beside the rest, so two passes
+  // (workgroups) each accumulate 128 columns and recompute S and dP over the full d.
+  static constexpr int DBP = (D <= 128 ? D : 128) / 32;
+  static constexpr int NDH = D / (32 * DBP);
+  static constexpr int PBUF = PAIRS * NMB * 2048;  // one tile's P: [pair][row block][half][lane] x 16 B
+  // The LDS statistics arrays come after the tiles and P buffers: reads reach them through a
+  // base lowered by this much.
+  static constexpr int STAT_BIAS = D == 128 ? 131072 : 65536;
+  static_assert(BR == BwdCfg<D>::BR, "the key blocks of the launcher's grid");
 };
 
 template <int D>
@@ -475,12 +206,12 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
   // as q0 q1 q2 do0 do1 do2 pbuf0 pbuf1, then the statistics: an LDS read reaches the tiles
   // below 64 KB through its immediate offset; the others get lane offsets raised by 64 KB
   // once per tile (tile below), the statistics a base lowered by 128 KB.
-  __shared__ __attribute__((aligned(1024))) char t0_do0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char t1_do1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char t2_do2[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char t3_q0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char t4_q1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char t5_q2[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char t0_do0[PC::TILE];
+  __shared__ __attribute__((aligned(1024))) char t1_do1[PC::TILE];
+  __shared__ __attribute__((aligned(1024))) char t2_do2[PC::TILE];
+  __shared__ __attribute__((aligned(1024))) char t3_q0[PC::TILE];
+  __shared__ __attribute__((aligned(1024))) char t4_q1[PC::TILE];
+  __shared__ __attribute__((aligned(1024))) char t5_q2[PC::TILE];
   __shared__ __attribute__((aligned(1024))) char t6_pbuf0[PC::PBUF];
   __shared__ __attribute__((aligned(1024))) char t7_pbuf1[PC::PBUF];
   __shared__ __attribute__((aligned(1024))) char stat_st0[2048];
@@ -494,7 +225,9 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
   const int hf = lane >> 5, l32 = lane & 31;
   const int N = p.N;
   int bg, kblk;
-  map_slice_block(blockIdx.x, p.B * p.Hkv, p.nblk, bg, kblk);
+  map_slice_block(blockIdx.x, p.B * p.Hkv, p.nblk * PC::NDH, bg, kblk);
+  const int dh = kblk % PC::NDH;  // which head-dim part of dK/dV this workgroup accumulates
+  kblk /= PC::NDH;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int G = p.Hq / p.Hkv;
   const int k0 = kblk * PC::BR;
@@ -503,12 +236,15 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
   const uint32_t head_bytes = (uint32_t)N * C::ROWB;
   const size_t kvoff = ((size_t)b * p.Hkv + g) * (size_t)N * D;
 
-  // Query tiles as in the single-wave kernel: every query head of the group, from the top
-  // tile that sees a key of the block down to the one holding key k0.
+  // Query tiles: every query head of the group, tiles from the one holding key k0 up to the
+  // last one that sees a key of the block (the end, unless a window stops earlier), walked
+  // from the TOP tile down, so all key blocks of a head start on the same tiles and read them
+  // at about the same time (shared through L2 instead of each block from HBM).
   const int W = p.window;
-  const int nqt_all = (N + C::BT - 1) / C::BT;
-  const int qt0 = p.causal ? k0 / C::BT : 0;
-  const int qt_top = min(nqt_all - 1, (k0 + PC::BR - 1 + W) / C::BT);
+  constexpr int BT = PC::BT, NMB = PC::NMB;
+  const int nqt_all = (N + BT - 1) / BT;
+  const int qt0 = p.causal ? k0 / BT : 0;
+  const int qt_top = min(nqt_all - 1, (k0 + PC::BR - 1 + W) / BT);
   const int nqt = qt_top - qt0 + 1;
   const int iters = G * nqt;
 
@@ -524,7 +260,7 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
     constexpr int s = decltype(S)::value;
     return (lds_char*)(s == 0 ? stat_st0 : s == 1 ? stat_st1 : stat_st2);
   };
-  // Tiles are numbered it = h nqt + u (query head g G + h, tile row (qt_top - u) 64); the
+  // Tiles are numbered it = h nqt + u (query head g G + h, tile row (qt_top - u) BT); the
   // loops below step a (head, tile) cursor instead of dividing.
   struct Cursor {
     int h, u;
@@ -536,7 +272,7 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
     }
   };
   // Lane part of the DMA offsets (row within the tile, swizzled chunk), fixed for the kernel.
-  constexpr int LPW = C::TILE / 1024 / PC::WAVES;
+  constexpr int LPW = PC::TILE / 1024 / PC::WAVES;
   uint32_t dma_off[LPW];
 #pragma unroll
   for (int t = 0; t < LPW; ++t) {
@@ -547,7 +283,7 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
   auto fetch = [&](auto S, int it, const Cursor& cur) __attribute__((always_inline)) {
     if (it >= iters) return;
     const int hq = g * G + cur.h;
-    const int qrow0 = (qt_top - cur.u) * C::BT;
+    const int qrow0 = (qt_top - cur.u) * BT;
     const size_t qoff = ((size_t)b * p.Hq + hq) * (size_t)N * D;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + qoff, head_bytes);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dO + qoff, head_bytes);
@@ -558,9 +294,9 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
       buffer_load16_lds(rd, do_st(S) + (wave * LPW + t) * 1024, off);
     }
     if (wave == 0) {
-      // -D and lse2 of the tile's 64 rows; lanes past 15 read past the end (zeros).
+      // -D and lse2 of the tile's BT rows; lanes past BT/4 - 1 read past the end (zeros).
       const size_t roff = ((size_t)b * p.Hq + hq) * (size_t)N;
-      const uint32_t off = lane < 16 ? (uint32_t)(qrow0 + 4 * lane) * 4 : (uint32_t)N * 4;
+      const uint32_t off = lane < BT / 4 ? (uint32_t)(qrow0 + 4 * lane) * 4 : (uint32_t)N * 4;
       buffer_load16_lds(make_rsrc(p.delta + roff, (uint32_t)N * 4), stat_st(S), off);
       buffer_load16_lds(make_rsrc(p.lse2 + roff, (uint32_t)N * 4), stat_st(S) + 1024, off);
     }
@@ -571,33 +307,37 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
   using I2 = std::integral_constant<int, 2>;
   fetch(I0{}, 0, Cursor{0, 0});
 
-  constexpr int KS = C::KS, DB = C::DB;
+  constexpr int KS = C::KS, DB = PC::DBP;
   int roff[C::RO], toff[DB], toff8[DB];
 #pragma unroll
   for (int ks = 0; ks < C::RO; ++ks) roff[ks] = row_read_off<D>(lane, ks);
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
-    toff[db] = tr_read_off<D>(lane, db, 0);
-    toff8[db] = tr_read_off<D>(lane, db, 1);
+    toff[db] = tr_read_off<D>(lane, dh * DB + db, 0);
+    toff8[db] = tr_read_off<D>(lane, dh * DB + db, 1);
   }
 
   const float c = p.c;
   const int key = kw + l32;
 
-  // One query tile: NS MFMA steps, S or dP of row blocks 0 and 1 (KS steps each), then
+  // One query tile: NS MFMA steps, S or dP of the NMB row blocks (KS steps each), then
   // dV^T or dK^T over (row block, half, head-dim block). Operand reads run PF steps ahead.
   // The steps are placed in this order with no scheduling fences: the compiler interleaves
   // them as well (fences around each step measured the same within about 1 %; in the dQ
   // kernel they measured 1-3 % faster and stay).
   // The P or dS values of row block mb become readable DL steps after its last S or dP step
   // (ready) and are consumed from step use(mb, h) on: the first half's eight values are made
-  // in [ready, use(mb, 0)), the second half's in [use(mb, 0), use(mb, 1)).
-  constexpr int NS = 2 * KS + 4 * DB;
+  // in [ready, use(mb, 0)), the second half's in [use(mb, 0), use(mb, 1)). With one row block
+  // (d = 256) the first half's values are formed in the step before their first use, waiting
+  // on the last S or dP MFMA; the partner wave keeps the SIMD busy meanwhile.
+  constexpr int NS = NMB * KS + NMB * 2 * DB;
   constexpr int PF = 3;
   constexpr int DL = 2;
-  auto ready = [](int mb) { return KS * (mb + 1) + DL; };
-  auto use = [](int mb, int h) { return 2 * KS + (2 * mb + h) * DB; };
-  static_assert(ready(0) < use(0, 0) && ready(1) < use(1, 0), "row block consumed before ready");
+  auto use = [](int mb, int h) { return NMB * KS + (2 * mb + h) * DB; };
+  auto first = [](int mb, int h) {  // first step forming values of (mb, h)
+    const int ready = KS * (mb + 1) + DL, use0 = NMB * KS + 2 * mb * DB;
+    return h == 0 ? (ready < use0 ? ready : use0 - 1) : use0;
+  };
   // RH / TH: the row-read / transposed-read tile lies above the reach of a read's immediate
   // offset; its reads then use lane offsets raised by 64 KB once per tile (an opaque add, so
   // the compiler does not fold it back into one add per read).
@@ -616,18 +356,22 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
     }
     const lds_char* rlo = rsrc - RB;
     const lds_char* tlo = tsrc - TB;
-    f32x16 sd[2] = {f32x16{}, f32x16{}};  // S (P waves) or dP
-    u32x4 op[2][2];                        // [mb][h]: P or dS, 16 queries x 32 keys, packed bf16
-    float pf[2][16];                       // P in fp32 until packed (P waves)
-    f32x4 st4[2][4];                       // lse2 (P waves) or -D of the lane's rows
-    const FA2_LDS float* sbase = (const FA2_LDS float*)(stat - 131072 + opaque_add<131072>(16 * hf));
+    f32x16 sd[NMB];        // S (P waves) or dP
+    u32x4 op[NMB][2];      // [mb][h]: P or dS, 16 queries x 32 keys, packed bf16
+    float pf[NMB][16];     // P in fp32 until packed (P waves)
+    f32x4 st4[NMB][4];     // lse2 (P waves) or -D of the lane's rows
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) sd[mb] = f32x16{};
+    constexpr int SB = PC::STAT_BIAS;
+    const FA2_LDS float* sbase = (const FA2_LDS float*)(stat - SB + opaque_add<SB>(16 * hf));
     auto load_stats = [&](int mb) __attribute__((always_inline)) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) st4[mb][rq] = *(const FA2_LDS f32x4*)(sbase + 32 * mb + 8 * rq);
     };
-    lds_char* pfrag = pb + pair * 4096 + lane * 16;  // + (2 mb + h) KB
-    // Zero P outside key <= query <= key + window for the eight rows of half h (see the
-    // single-wave kernel for the register-to-row map).
+    lds_char* pfrag = pb + pair * (NMB * 2048) + lane * 16;  // + (2 mb + h) KB
+    // Zero P outside key <= query <= key + window for the eight rows of half h. Registers hold
+    // query rows 32 mb + 8 (r / 4) + 4 hf + r % 4 of the tile; the row sees this lane's key iff
+    // lo <= 32 mb + 8 (r / 4) + r % 4 <= lo + window, lo = key - qrow0 - 4 hf.
     auto causal_fixup = [&](int mb, int h) __attribute__((always_inline)) {
       const int lo = key - qrow0 - 4 * hf;
       const int hi = lo + W;
@@ -660,18 +404,18 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
     };
     auto read_op = [&](auto J) __attribute__((always_inline)) -> u32x4 {
       constexpr int j = decltype(J)::value;
-      if constexpr (j < 2 * KS) {
+      if constexpr (j < NMB * KS) {
         constexpr int ks = j % KS;
         return lds_read16(rlo + ro[ks % C::RO] + (ks / C::RO) * 256 + (j / KS) * 32 * C::ROWB);
       } else {
-        constexpr int i = j - 2 * KS, db = i % DB, mb = i / (2 * DB), h = (i / DB) & 1;
+        constexpr int i = j - NMB * KS, db = i % DB, mb = i / (2 * DB), h = (i / DB) & 1;
         const int rowsel = (32 * mb + 16 * h) * C::ROWB;
         return tr_pair(tlo + to[db] + rowsel, tlo + to8[db] + rowsel);
       }
     };
     auto mfma_step = [&](auto J, u32x4 a) __attribute__((always_inline)) {
       constexpr int j = decltype(J)::value;
-      if constexpr (j < 2 * KS) {
+      if constexpr (j < NMB * KS) {
         constexpr int mb = j / KS;
         if constexpr (!PWAVE && j % KS == 0) {
           // dP chain of row block mb starts from -D (register r holds row 8 (r/4) + 4 hf + r%4).
@@ -684,7 +428,7 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
           sd[mb] = mfma32x32x16(a, kv[j % KS], sd[mb]);
         }
       } else {
-        constexpr int i = j - 2 * KS, db = i % DB, mb = i / (2 * DB), h = (i / DB) & 1;
+        constexpr int i = j - NMB * KS, db = i % DB, mb = i / (2 * DB), h = (i / DB) & 1;
         acc[db] = mfma32x32x16(a, op[mb][h], acc[db]);
       }
     };
@@ -695,15 +439,15 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
           load_stats(0);
         } else {
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
+          for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
             for (int h = 0; h < 2; ++h) op[mb][h] = lds_read16(pfrag + (2 * mb + h) * 1024);
         }
       }
-      if constexpr (PWAVE && j == KS) load_stats(1);
-      static_for<0, 4>([&](auto MH) __attribute__((always_inline)) {
+      if constexpr (PWAVE && NMB > 1 && j == KS) load_stats(1);
+      static_for<0, 2 * NMB>([&](auto MH) __attribute__((always_inline)) {
         constexpr int mb = decltype(MH)::value / 2, h = decltype(MH)::value % 2;
-        constexpr int lo = h == 0 ? ready(mb) : use(mb, 0), hi = use(mb, h), n = hi - lo;
+        constexpr int lo = first(mb, h), hi = use(mb, h), n = hi - lo;
         if constexpr (j >= lo && j < hi) {
           constexpr int e0 = 2 * ((4 * (j - lo)) / n), e1 = 2 * ((4 * (j - lo + 1)) / n);
           values(mb, h, e0, e1);
@@ -715,8 +459,8 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
       });
     };
     if constexpr (!PWAVE) {
-      load_stats(0);  // -D initialises the dP chains
-      load_stats(1);
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) load_stats(mb);  // -D initialises the dP chains
     }
     u32x4 ring[PF + 1];
     static_for<0, PF>([&](auto J) __attribute__((always_inline)) { ring[decltype(J)::value] = read_op(J); });
@@ -758,19 +502,20 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
       advance(fc);
       const int t = PWAVE ? s : s - 1;
       if (t >= 0 && t < iters) {
-        const int qrow0 = (qt_top - tc.u) * C::BT;
+        const int qrow0 = (qt_top - tc.u) * BT;
         advance(tc);
         // Causal: skip tiles wholly above the pair's keys or past their window.
-        const bool skip = (p.causal && qrow0 + C::BT - 1 < kw) || qrow0 > kw + PC::RPW - 1 + W;
+        const bool skip = (p.causal && qrow0 + BT - 1 < kw) || qrow0 > kw + PC::RPW - 1 + W;
         lds_char* pb = (lds_char*)((t & 1) ? t7_pbuf1 : t6_pbuf0);
         if (!skip) {
-          // dO stages 1 and 2 lie at 64 KB and above.
+          // With 16 KB tiles, dO stages 1 and 2 lie at 64 KB and above.
+          constexpr bool HI = PC::TILE == 16384;
           if constexpr (PWAVE) {
-            const bool fix = (p.causal && qrow0 < kw + PC::RPW - 1) || qrow0 + C::BT - 1 > kw + W;
-            tile(PW, std::false_type{}, std::bool_constant<D == 128 && st != 0>{}, kv, acc, q_st(S),
+            const bool fix = (p.causal && qrow0 < kw + PC::RPW - 1) || qrow0 + BT - 1 > kw + W;
+            tile(PW, std::false_type{}, std::bool_constant<HI && st != 0>{}, kv, acc, q_st(S),
                  do_st(S), stat_st(S) + 1024, pb, qrow0, fix);
           } else {
-            tile(PW, std::bool_constant<D == 128 && SP::value != 0>{}, std::false_type{}, kv, acc,
+            tile(PW, std::bool_constant<HI && SP::value != 0>{}, std::false_type{}, kv, acc,
                  do_st(SP{}), q_st(SP{}), stat_st(SP{}), pb, qrow0, false);
           }
         }
@@ -788,9 +533,9 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
     if (s <= iters) step(I0{}, s);
     if (s + 1 <= iters) step(I1{}, s + 1);
 
-    // Store dV, or dK = scale dK^T^T: lane = key, registers = head dim.
+    // Store dV, or dK = scale dK^T^T: lane = key, registers = head dim (this pass's columns).
     if (key < N) {
-      float* row = (PWAVE ? p.dv : p.dk) + kvoff + (size_t)key * D;
+      float* row = (PWAVE ? p.dv : p.dk) + kvoff + (size_t)key * D + dh * DB * 32;
       const float f = PWAVE ? 1.f : p.scale;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -1168,14 +913,14 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
   p.dk = dk;
   p.dv = dv;
   p.nblk = (s.N + BwdCfg<128>::BR - 1) / BwdCfg<128>::BR;
-  const int ndh = s.d == 256 ? BwdCfg<256>::NDH : 1;
-  const dim3 grid((unsigned)(s.B * s.Hkv * p.nblk * ndh));
+  const int ndh = s.d == 256 ? PairCfg<256>::NDH : 1;
+  const dim3 grid((unsigned)(s.B * s.Hkv * p.nblk * ndh)), block(PairCfg<128>::WAVES * 64);
   if (s.d == 128)
-    hipLaunchKernelGGL(fa2_bwd_dkdv_pair_kernel<128>, grid, dim3(PairCfg<128>::WAVES * 64), 0, stream, p);
+    hipLaunchKernelGGL(fa2_bwd_dkdv_pair_kernel<128>, grid, block, 0, stream, p);
   else if (s.d == 256)
-    hipLaunchKernelGGL(fa2_bwd_dkdv_kernel<256>, grid, dim3(BwdCfg<256>::WAVES * 64), 0, stream, p);
+    hipLaunchKernelGGL(fa2_bwd_dkdv_pair_kernel<256>, grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL(fa2_bwd_dkdv_pair_kernel<64>, grid, dim3(PairCfg<64>::WAVES * 64), 0, stream, p);
+    hipLaunchKernelGGL(fa2_bwd_dkdv_pair_kernel<64>, grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
