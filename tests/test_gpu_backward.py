@@ -268,3 +268,4 @@ def test_head_dim_256_gqa_long_scale():
     check_backward(9100, 2, 8, 2, 400, 256, True)
     check_backward(9101, 1, 4, 4, 2048, 256, True, sample=256)
     check_backward(9102, 1, 4, 2, 300, 256, False, scale=-0.06)
+    check_backward(9103, 1, 8, 1, 333, 256, True)  # all query heads on one KV head
