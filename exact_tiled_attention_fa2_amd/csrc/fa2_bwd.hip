@@ -161,6 +161,12 @@ __global__ __launch_bounds__(256) void fa2_bwd_pre_kernel(const float* __restric
 
 // ------------------------------------------------------------------ 2. dK / dV, paired waves
 
+// Work items (workgroups per slice and head-dim pass) of the dK/dV kernel: key-block pairs
+// up to head dim 128 without grouped-query heads, single key blocks otherwise.
+__host__ __device__ inline int dkdv_work_items(int nblk, int G, int d) {
+  return G == 1 && d <= 128 ? (nblk + 1) / 2 : nblk;
+}
+
 // Eight waves, two per SIMD, in four pairs that each own 32 keys. Wave w
 // (w < 4) keeps the keys' K and computes S = Q K^T, P = 2^(S c - lse2) and dV^T += dO^T P; it
 // leaves P in LDS as packed bf16, in the MFMA operand layout. Its partner w + 4, on the same
@@ -224,12 +230,22 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
   const bool pwave = wave < 4;  // keeps K and produces P (else keeps V and produces dS)
   const int hf = lane >> 5, l32 = lane & 31;
   const int N = p.N;
-  int bg, kblk;
-  map_slice_block(blockIdx.x, p.B * p.Hkv, p.nblk * PC::NDH, bg, kblk);
-  const int dh = kblk % PC::NDH;  // which head-dim part of dK/dV this workgroup accumulates
-  kblk /= PC::NDH;
-  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  // Without grouped-query heads each workgroup takes two key blocks of one slice, one after
+  // the other: block j and block nblk - 1 - j (causal: the heaviest with the lightest, so every
+  // workgroup carries about the same work), which halves the workgroups' start-up and
+  // wind-down costs (3 % at B2 H32 N8192, 8 % at B4 H16 N4096). With a group of query heads
+  // per block the work per block is long already, and one block per workgroup keeps the
+  // blocks of a head walking the same query tiles in step (pairs measured 1-2 % slower); at
+  // d = 256 the two head-dim passes already double the workgroups (pairs 1 % slower).
   const int G = p.Hq / p.Hkv;
+  const int nwork = dkdv_work_items(p.nblk, G, D);
+  int bg, u;
+  map_slice_block(blockIdx.x, p.B * p.Hkv, nwork * PC::NDH, bg, u);
+  const int dh = u % PC::NDH;  // which head-dim part of dK/dV this workgroup accumulates
+  const int j = u / PC::NDH;
+  const int nmy = nwork < p.nblk && p.nblk - 1 - j > j ? 2 : 1;
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  auto block = [&](int kblk) __attribute__((always_inline)) {
   const int k0 = kblk * PC::BR;
   const int kw = k0 + pair * PC::RPW;  // the pair's first key
 
@@ -552,6 +568,8 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
     run(std::true_type{});
   else
     run(std::false_type{});
+  };
+  for (int i = 0; i < nmy; ++i) block(i == 0 ? j : p.nblk - 1 - j);
 }
 
 // ------------------------------------------------------------------ 3. dQ
@@ -914,7 +932,8 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
   p.dv = dv;
   p.nblk = (s.N + BwdCfg<128>::BR - 1) / BwdCfg<128>::BR;
   const int ndh = s.d == 256 ? PairCfg<256>::NDH : 1;
-  const dim3 grid((unsigned)(s.B * s.Hkv * p.nblk * ndh)), block(PairCfg<128>::WAVES * 64);
+  const dim3 grid((unsigned)(s.B * s.Hkv * dkdv_work_items(p.nblk, s.Hq / s.Hkv, s.d) * ndh));
+  const dim3 block(PairCfg<128>::WAVES * 64);
   if (s.d == 128)
     hipLaunchKernelGGL(fa2_bwd_dkdv_pair_kernel<128>, grid, block, 0, stream, p);
   else if (s.d == 256)
