@@ -614,11 +614,15 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   const int hf = lane >> 5, l32 = lane & 31;
   if constexpr (NW == 4) agpr_accumulators_hint();
   const int N = p.N;
-  int bh, r;
-  map_slice_block(blockIdx.x, p.B * p.Hq, p.nblk, bh, r);
-  const int qblk = p.causal ? p.nblk - 1 - r : r;  // longest rows first
+  // Each workgroup takes two query blocks of one head, one after the other: block j and block
+  // nblk - 1 - j (causal: the longest rows with the shortest, so every workgroup carries about
+  // the same work), which halves the workgroups' start-up and wind-down costs.
+  int bh, j;
+  map_slice_block(blockIdx.x, p.B * p.Hq, (p.nblk + 1) / 2, bh, j);
+  const int nmy = p.nblk - 1 - j > j ? 2 : 1;
   const int b = bh / p.Hq, hq = bh % p.Hq;
   const int hkv = hq / (p.Hq / p.Hkv);
+  auto block = [&](int qblk) __attribute__((always_inline)) {
   const int q0 = qblk * Q::BR;
   const int qw = q0 + wave * Q::RPW;  // this wave's first query
 
@@ -882,6 +886,11 @@ void fa2_bwd_dq_kernel(BwdParams p) {
                     adq[qb][db][4 * rq + 3]} * p.scale;
     }
   }
+  };
+  for (int i = 0; i < nmy; ++i) {
+    if (i) __syncthreads();  // every wave is past its last reads of the first block's tiles
+    block(i == 0 ? j : p.nblk - 1 - j);
+  }
 }
 
 // ------------------------------------------------------------------ launchers
@@ -950,7 +959,7 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
   constexpr int NW = 8;  // head dims 64 and 128: two waves per SIMD (measured 5-20 % faster)
   const int BR = s.d == 256 ? DqCfg<256>::BR : DqCfg<128, NW>::BR;
   p.nblk = (s.N + BR - 1) / BR;
-  const dim3 grid((unsigned)(s.B * s.Hq * p.nblk));
+  const dim3 grid((unsigned)(s.B * s.Hq * ((p.nblk + 1) / 2)));
   if (s.d == 128)
     hipLaunchKernelGGL((fa2_bwd_dq_kernel<128, NW>), grid, dim3(NW * 64), 0, stream, p);
   else if (s.d == 256)
