@@ -90,20 +90,29 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, lds_char* t
   }
 }
 
-__device__ __forceinline__ void map_block(int bid, const FwdParams& p, int& bh, int& qblk) {
-  int r;
+// Workgroups per head. With 8-wave workgroups at d = 128 (one workgroup per CU, nothing else
+// to hide its start-up behind) each takes query block j, then block nqb - 1 - j (causal: the
+// longest rows with the shortest, so every workgroup carries about the same work), which
+// halves the workgroups' start-up (Q, first K/V tiles) and wind-down (O stores) costs. The
+// other configurations keep one block per workgroup (the second block's live ranges push
+// them into register spills).
+__host__ __device__ constexpr bool fwd_paired(int d, int nw) { return d == 128 && nw == 8; }
+__host__ __device__ inline int fwd_work_items(int nqb, bool paired) { return paired ? (nqb + 1) / 2 : nqb; }
+
+// Block id -> (head slice, work item j). Workgroups are dealt round-robin to the 8 XCDs
+// (bid & 7 is the XCD); when the slice count divides by 8, each XCD gets a contiguous range of
+// heads and walks their work items in order.
+__device__ __forceinline__ void map_block(int bid, const FwdParams& p, bool paired, int& bh, int& j) {
+  const int nw = fwd_work_items(p.nqb, paired);
   if (p.xcd_remap) {
-    // Workgroups are dealt round-robin to the 8 XCDs: bid & 7 is the XCD. Give each XCD a
-    // contiguous range of heads and walk its query blocks in order there.
     const int x = bid & 7, s = bid >> 3;
     const int heads_per_xcd = (p.B * p.Hq) >> 3;
-    bh = x * heads_per_xcd + s / p.nqb;
-    r = s % p.nqb;
+    bh = x * heads_per_xcd + s / nw;
+    j = s % nw;
   } else {
-    bh = bid / p.nqb;
-    r = bid % p.nqb;
+    bh = bid / nw;
+    j = bid % nw;
   }
-  qblk = p.causal ? p.nqb - 1 - r : r;  // causal: longest rows first
 }
 
 // Online softmax with a reference that is raised only when needed. The exponentials of a
@@ -141,11 +150,14 @@ void fa2_fwd_kernel(FwdParams p) {
   const int l32 = lane & 31;
   if constexpr (D == 256) agpr_accumulators_hint();  // O in AGPRs: one wave per SIMD
 
-  int bh, qblk;
-  map_block(blockIdx.x, p, bh, qblk);
+  constexpr bool PAIRED = fwd_paired(D, NW);
+  int bh, j;
+  map_block(blockIdx.x, p, PAIRED, bh, j);
   const int b = bh / p.Hq, hq = bh % p.Hq;
   const int hkv = hq / (p.Hq / p.Hkv);
   const int N = p.N;
+  const int first = p.causal ? p.nqb - 1 - j : j;  // causal: longest rows first
+  auto block = [&](int qblk) __attribute__((always_inline)) {
   const int q0 = qblk * C::BM;
   const int qlo = q0 + wave * C::QPW;
 
@@ -503,6 +515,14 @@ void fa2_fwd_kernel(FwdParams p) {
       if (hf == 0) p.lse[(size_t)bh * N + row] = (m[qb] + __log2f(lt)) * kLn2;
     }
   }
+  };
+  block(first);
+  if constexpr (PAIRED) {
+    if (p.nqb - 1 - first != first) {
+      __syncthreads();  // every wave is past its last reads of the first block's tiles
+      block(p.nqb - 1 - first);
+    }
+  }
 }
 
 // Waves per workgroup: 4 (128 query rows, several workgroups per CU, so that one's start-up --
@@ -544,7 +564,7 @@ static FwdParams forward_params(const void* q, const void* k, const void* v, flo
 template <int D, int NW, bool FP8>
 static void launch_fwd_kernel(const FwdParams& p, const AttnShape& s, hipStream_t stream) {
   static_assert(32 * NW == FwdCfg<D, NW>::BM, "rows per workgroup");
-  const dim3 grid((unsigned)(s.B * s.Hq * p.nqb));
+  const dim3 grid((unsigned)(s.B * s.Hq * fwd_work_items(p.nqb, fwd_paired(D, NW))));
   hipLaunchKernelGGL((fa2_fwd_kernel<D, NW, FP8>), grid, dim3(NW * 64), 0, stream, p);
 }
 
