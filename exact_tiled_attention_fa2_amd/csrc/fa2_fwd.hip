@@ -91,19 +91,24 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, lds_char* t
 }
 
 // Workgroups per head. With 8-wave workgroups at d = 128 (one workgroup per CU, nothing else
-// to hide its start-up behind) each takes query block j, then block nqb - 1 - j (causal: the
-// longest rows with the shortest, so every workgroup carries about the same work), which
-// halves the workgroups' start-up (Q, first K/V tiles) and wind-down (O stores) costs. The
-// other configurations keep one block per workgroup (the second block's live ranges push
-// them into register spills).
-__host__ __device__ constexpr bool fwd_paired(int d, int nw) { return d == 128 && nw == 8; }
-__host__ __device__ inline int fwd_work_items(int nqb, bool paired) { return paired ? (nqb + 1) / 2 : nqb; }
+// to hide its start-up behind) each takes two pairs of query blocks, block p then block
+// nqb - 1 - p for consecutive pairs p (causal: the longest rows with the shortest, so every
+// workgroup carries about the same work); this divides the workgroups' start-up (Q, first
+// K/V tiles) and wind-down (O stores) costs by four. Measured against one block per
+// workgroup at causal B2 H32 N8192: one pair 6 % faster, two pairs 9 %, four pairs slower
+// again (too few workgroups to balance). The other configurations keep one block per
+// workgroup (a second block's live ranges push them into register spills).
+// Pairs of query blocks per workgroup; 0: one block per workgroup.
+__host__ __device__ constexpr int fwd_pairs_per_wg(int d, int nw) { return d == 128 && nw == 8 ? 2 : 0; }
+__host__ __device__ inline int fwd_work_items(int nqb, int kp) {
+  return kp == 0 ? nqb : ((nqb + 1) / 2 + kp - 1) / kp;
+}
 
 // Block id -> (head slice, work item j). Workgroups are dealt round-robin to the 8 XCDs
 // (bid & 7 is the XCD); when the slice count divides by 8, each XCD gets a contiguous range of
 // heads and walks their work items in order.
-__device__ __forceinline__ void map_block(int bid, const FwdParams& p, bool paired, int& bh, int& j) {
-  const int nw = fwd_work_items(p.nqb, paired);
+__device__ __forceinline__ void map_block(int bid, const FwdParams& p, int kp, int& bh, int& j) {
+  const int nw = fwd_work_items(p.nqb, kp);
   if (p.xcd_remap) {
     const int x = bid & 7, s = bid >> 3;
     const int heads_per_xcd = (p.B * p.Hq) >> 3;
@@ -150,13 +155,12 @@ void fa2_fwd_kernel(FwdParams p) {
   const int l32 = lane & 31;
   if constexpr (D == 256) agpr_accumulators_hint();  // O in AGPRs: one wave per SIMD
 
-  constexpr bool PAIRED = fwd_paired(D, NW);
+  constexpr int KP = fwd_pairs_per_wg(D, NW);
   int bh, j;
-  map_block(blockIdx.x, p, PAIRED, bh, j);
+  map_block(blockIdx.x, p, KP, bh, j);
   const int b = bh / p.Hq, hq = bh % p.Hq;
   const int hkv = hq / (p.Hq / p.Hkv);
   const int N = p.N;
-  const int first = p.causal ? p.nqb - 1 - j : j;  // causal: longest rows first
   auto block = [&](int qblk) __attribute__((always_inline)) {
   const int q0 = qblk * C::BM;
   const int qlo = q0 + wave * C::QPW;
@@ -516,11 +520,17 @@ void fa2_fwd_kernel(FwdParams p) {
     }
   }
   };
-  block(first);
-  if constexpr (PAIRED) {
-    if (p.nqb - 1 - first != first) {
-      __syncthreads();  // every wave is past its last reads of the first block's tiles
-      block(p.nqb - 1 - first);
+  if constexpr (KP == 0) {
+    block(p.causal ? p.nqb - 1 - j : j);  // causal: longest rows first
+  } else {
+    const int npair = (p.nqb + 1) / 2;
+    for (int i = 0; i < 2 * KP; ++i) {
+      const int pi = j * KP + i / 2;
+      const int first = p.causal ? p.nqb - 1 - pi : pi;  // causal: longest rows first
+      const int qblk = i & 1 ? p.nqb - 1 - first : first;
+      if (pi >= npair || (i & 1 && qblk == first)) continue;
+      if (i) __syncthreads();  // every wave is past its last reads of the previous block's tiles
+      block(qblk);
     }
   }
 }
@@ -564,7 +574,7 @@ static FwdParams forward_params(const void* q, const void* k, const void* v, flo
 template <int D, int NW, bool FP8>
 static void launch_fwd_kernel(const FwdParams& p, const AttnShape& s, hipStream_t stream) {
   static_assert(32 * NW == FwdCfg<D, NW>::BM, "rows per workgroup");
-  const dim3 grid((unsigned)(s.B * s.Hq * fwd_work_items(p.nqb, fwd_paired(D, NW))));
+  const dim3 grid((unsigned)(s.B * s.Hq * fwd_work_items(p.nqb, fwd_pairs_per_wg(D, NW))));
   hipLaunchKernelGGL((fa2_fwd_kernel<D, NW, FP8>), grid, dim3(NW * 64), 0, stream, p);
 }
 
