@@ -161,10 +161,19 @@ __global__ __launch_bounds__(256) void fa2_bwd_pre_kernel(const float* __restric
 
 // ------------------------------------------------------------------ 2. dK / dV, paired waves
 
-// Work items (workgroups per slice and head-dim pass) of the dK/dV kernel: key-block pairs
-// up to head dim 128 without grouped-query heads, single key blocks otherwise.
+// Work items (workgroups per slice and head-dim pass) of the dK/dV kernel. Up to head dim 128
+// without grouped-query heads a workgroup takes two pairs of key blocks (j, nblk-1-j), which
+// spreads its fixed start-up and wind-down over four blocks (2-4% faster than one pair on causal
+// d=64 and d=128 shapes); otherwise one key block each.
+constexpr int kDkdvPairs = 2;
 __host__ __device__ inline int dkdv_work_items(int nblk, int G, int d) {
-  return G == 1 && d <= 128 ? (nblk + 1) / 2 : nblk;
+  return G == 1 && d <= 128 ? ((nblk + 1) / 2 + kDkdvPairs - 1) / kDkdvPairs : nblk;
+}
+// Pairs of query blocks per dQ workgroup: two at head dim 256 (3% faster than one), one below,
+// where a second pair measured no faster.
+__host__ __device__ constexpr int dq_pairs(int d) { return d == 256 ? 2 : 1; }
+__host__ __device__ inline int dq_work_items(int nblk, int d) {
+  return ((nblk + 1) / 2 + dq_pairs(d) - 1) / dq_pairs(d);
 }
 
 // Eight waves, two per SIMD, in four pairs that each own 32 keys. Wave w
@@ -230,10 +239,11 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
   const bool pwave = wave < 4;  // keeps K and produces P (else keeps V and produces dS)
   const int hf = lane >> 5, l32 = lane & 31;
   const int N = p.N;
-  // Without grouped-query heads each workgroup takes two key blocks of one slice, one after
-  // the other: block j and block nblk - 1 - j (causal: the heaviest with the lightest, so every
-  // workgroup carries about the same work), which halves the workgroups' start-up and
-  // wind-down costs (3 % at B2 H32 N8192, 8 % at B4 H16 N4096). With a group of query heads
+  // Without grouped-query heads each workgroup takes two pairs of key blocks of one slice, one
+  // block after the other: blocks 2j, nblk-1-2j, 2j+1, nblk-2-2j (causal: the heaviest with the
+  // lightest, so every workgroup carries about the same work), which spreads the workgroups'
+  // start-up and wind-down costs over four blocks (one pair against one block: 3 % at B2 H32
+  // N8192, 8 % at B4 H16 N4096; two pairs another 1-3 %). With a group of query heads
   // per block the work per block is long already, and one block per workgroup keeps the
   // blocks of a head walking the same query tiles in step (pairs measured 1-2 % slower); at
   // d = 256 the two head-dim passes already double the workgroups (pairs 1 % slower).
@@ -243,7 +253,7 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
   map_slice_block(blockIdx.x, p.B * p.Hkv, nwork * PC::NDH, bg, u);
   const int dh = u % PC::NDH;  // which head-dim part of dK/dV this workgroup accumulates
   const int j = u / PC::NDH;
-  const int nmy = nwork < p.nblk && p.nblk - 1 - j > j ? 2 : 1;
+  const bool paired = G == 1 && D <= 128;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   auto block = [&](int kblk) __attribute__((always_inline)) {
   const int k0 = kblk * PC::BR;
@@ -569,7 +579,17 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
   else
     run(std::false_type{});
   };
-  for (int i = 0; i < nmy; ++i) block(i == 0 ? j : p.nblk - 1 - j);
+  if (!paired) {
+    block(j);
+  } else {
+    const int npair = (p.nblk + 1) / 2;
+    for (int i = 0; i < 2 * kDkdvPairs; ++i) {
+      const int pi = j * kDkdvPairs + i / 2;
+      const int kb = i & 1 ? p.nblk - 1 - pi : pi;
+      if (pi >= npair || (i & 1 && kb == pi)) continue;
+      block(kb);
+    }
+  }
 }
 
 // ------------------------------------------------------------------ 3. dQ
@@ -614,12 +634,12 @@ void fa2_bwd_dq_kernel(BwdParams p) {
   const int hf = lane >> 5, l32 = lane & 31;
   if constexpr (NW == 4) agpr_accumulators_hint();
   const int N = p.N;
-  // Each workgroup takes two query blocks of one head, one after the other: block j and block
-  // nblk - 1 - j (causal: the longest rows with the shortest, so every workgroup carries about
-  // the same work), which halves the workgroups' start-up and wind-down costs.
+  // Each workgroup takes dq_pairs(D) pairs of query blocks of one head, one block after the
+  // other: a block and its mirror nblk - 1 - block (causal: the longest rows with the shortest,
+  // so every workgroup carries about the same work), which spreads the workgroups' start-up and
+  // wind-down costs.
   int bh, j;
-  map_slice_block(blockIdx.x, p.B * p.Hq, (p.nblk + 1) / 2, bh, j);
-  const int nmy = p.nblk - 1 - j > j ? 2 : 1;
+  map_slice_block(blockIdx.x, p.B * p.Hq, dq_work_items(p.nblk, D), bh, j);
   const int b = bh / p.Hq, hq = bh % p.Hq;
   const int hkv = hq / (p.Hq / p.Hkv);
   auto block = [&](int qblk) __attribute__((always_inline)) {
@@ -887,9 +907,15 @@ void fa2_bwd_dq_kernel(BwdParams p) {
     }
   }
   };
-  for (int i = 0; i < nmy; ++i) {
-    if (i) __syncthreads();  // every wave is past its last reads of the first block's tiles
-    block(i == 0 ? j : p.nblk - 1 - j);
+  const int npair = (p.nblk + 1) / 2;
+  constexpr int KP = dq_pairs(D);
+  for (int i = 0; i < 2 * KP; ++i) {
+    const int pi = j * KP + i / 2;
+    const int first = p.causal ? p.nblk - 1 - pi : pi;  // causal: longest rows first
+    const int qb = i & 1 ? p.nblk - 1 - first : first;
+    if (pi >= npair || (i & 1 && qb == first)) continue;
+    if (i) __syncthreads();  // every wave is past its last reads of the previous block's tiles
+    block(qb);
   }
 }
 
@@ -959,7 +985,7 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
   constexpr int NW = 8;  // head dims 64 and 128: two waves per SIMD (measured 5-20 % faster)
   const int BR = s.d == 256 ? DqCfg<256>::BR : DqCfg<128, NW>::BR;
   p.nblk = (s.N + BR - 1) / BR;
-  const dim3 grid((unsigned)(s.B * s.Hq * ((p.nblk + 1) / 2)));
+  const dim3 grid((unsigned)(s.B * s.Hq * dq_work_items(p.nblk, s.d)));
   if (s.d == 128)
     hipLaunchKernelGGL((fa2_bwd_dq_kernel<128, NW>), grid, dim3(NW * 64), 0, stream, p);
   else if (s.d == 256)
