@@ -117,6 +117,17 @@ def test_ragged_lengths(N, d, causal):
     check_backward(2000 + N, 1, 2, 1, N, d, causal)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 129, 300, 420, 640, 900, 1100])
+def test_block_pairing_counts(N, d, causal):
+    # One KV head per query head: the dK/dV workgroups take pairs of 128-key blocks and the dQ
+    # workgroups pairs of query blocks, so N runs over 1 to 9 key blocks (odd and even counts,
+    # a middle block that is its own mirror, workgroups with a partial second pair) and
+    # ragged tails.
+    check_backward(2500 + N, 1, 2, 2, N, d, causal)
+
+
 @pytest.mark.parametrize("Hkv", [1, 2, 4, 8])
 def test_gqa_ratios(Hkv):
     check_backward(3000 + Hkv, 2, 8, Hkv, 300, 128, True)
@@ -269,3 +280,9 @@ def test_head_dim_256_gqa_long_scale():
     check_backward(9101, 1, 4, 4, 2048, 256, True, sample=256)
     check_backward(9102, 1, 4, 2, 300, 256, False, scale=-0.06)
     check_backward(9103, 1, 8, 1, 333, 256, True)  # all query heads on one KV head
+
+
+@pytest.mark.parametrize("N", [129, 385, 640, 1000])
+def test_d256_dq_block_pairs(N):
+    # At d = 256 a dQ workgroup takes two pairs of 128-row query blocks: 2 to 8 blocks here.
+    check_backward(9200 + N, 1, 2, 2, N, 256, True)
