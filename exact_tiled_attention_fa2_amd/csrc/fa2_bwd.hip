@@ -9,14 +9,16 @@
 // Three kernels run in stream order, none with atomics (the result is deterministic, as
 // the wiki article "FlashAttention-2" stresses in its performance section):
 //   1. preprocess   D_i = sum_c dO_ic O_ic                   (one value per query row)
-//   2. dK/dV        one workgroup per (batch, KV head, 128-key block), walking every query
-//                   tile of every query head sharing the KV head: four pairs of waves, one
-//                   pair per 32 keys; the first keeps K and makes P and dV, the second keeps
-//                   V and makes dS and dK from the P its partner leaves in LDS (head dim 256:
-//                   32-row tiles and two passes over head-dim halves).
-//   3. dQ           one workgroup per (batch, query head, query block); each wave keeps its
-//                   32 queries' Q, dO and fp32 dQ^T in registers and walks the key tiles
-//                   (eight waves, two per SIMD; four at head dim 256).
+//   2. dK/dV        per (batch, KV head) 128-key blocks, each walking every query tile of
+//                   every query head sharing the KV head: four pairs of waves, one pair per
+//                   32 keys; the first keeps K and makes P and dV, the second keeps V and
+//                   makes dS and dK from the P its partner leaves in LDS (head dim 256:
+//                   32-row tiles and two passes over head-dim halves). A workgroup takes one
+//                   block, or two mirrored pairs of blocks without grouped-query heads.
+//   3. dQ           per (batch, query head) query blocks; each wave keeps its 32 queries' Q,
+//                   dO and fp32 dQ^T in registers and walks the key tiles (eight waves, two
+//                   per SIMD; four at head dim 256). A workgroup takes a mirrored pair of
+//                   blocks (two pairs at head dim 256).
 // Q/dO (dK/dV kernels) and K/V (dQ kernel) tiles stream into LDS by buffer_load ... lds, in
 // two or three stages, in a layout that serves both 16-byte row reads and the transposing
 // ds_read_b64_tr_b16 reads without bank conflicts.

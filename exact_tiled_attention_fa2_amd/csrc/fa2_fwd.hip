@@ -23,6 +23,8 @@
 //  * Causal: K/V tiles above a wave's last row are skipped; only tiles that straddle the
 //    diagonal (or the ragged end of the sequence) are masked. Query blocks are scheduled
 //    heaviest first, and blocks of one head stay on one XCD so their K/V reads share an L2.
+//    8-wave d = 128 workgroups take two mirrored pairs of query blocks (j with nqb - 1 - j)
+//    one after the other, so every workgroup carries the same causal work.
 //  * Sliding window (causal, keys i - W .. i): the workgroup starts at its first visible tile,
 //    and the leading tiles that cross the window's lower edge are masked too.
 //  * Scale folded into the exponent: p = 2^(s*c - m) with c = |scale|*log2(e); a negative
