@@ -159,7 +159,8 @@ def extra_workloads(fa2, seedgen, dev, stream, steps, only=None):
              "fwd_algorithmic_bytes": fwd_bytes, "fwd_GBps": round(fwd_bytes / (per[0] * 1e-3) / 1e9, 1)}
         if with_bwd:
             r["bwd_ms"] = round(per[1], 4)
-            r["fwd_bwd_tflops"] = round(pairs * 10 * d / (total * 1e-3) / 1e12, 1)
+            # forward 4 FLOP per visible pair and head-dim element, backward 2.5 times that
+            r["fwd_bwd_tflops"] = round(pairs * 14 * d / (total * 1e-3) / 1e12, 1)
         out[name] = r
         log("  extra %-38s %s" % (name, r))
         del q, k, v, dO, qd, kd, vd, dod, o, lse, dq, dk, dv, ws
