@@ -347,7 +347,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on exactly one GPU; --gpus %d (WORLD_SIZE=%d) is not supported"
+        print("bench.py: the benchmark runs on exactly one GPU (heads would shard across GPUs with no exchange, not implemented here); --gpus %d (WORLD_SIZE=%d) is not supported"
               % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
 
