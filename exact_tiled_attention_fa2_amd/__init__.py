@@ -102,6 +102,38 @@ def _stream(s):
     return s.cuda_stream  # torch.cuda.Stream
 
 
+def _torch_stream(s, device):
+    """Stream for the torch conveniences: the caller's, else torch's current stream on
+    ``device`` (so the launch is ordered after the work that produced the inputs there)."""
+    if s is not None:
+        return s
+    import torch
+    return torch.cuda.current_stream(device)
+
+
+def _check_tensors(specs):
+    """Host-side checks of the torch conveniences, before anything is launched: every tensor
+    lives on one GPU and has the shape the call implies. The C ABI receives bare pointers and
+    cannot tell a host buffer or a short tensor from a good one.
+
+    ``specs``: (name, tensor, expected shape tuple)."""
+    for name, x, shape in specs:
+        if tuple(x.shape) != tuple(shape):
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(x.shape), tuple(shape)))
+    dev = specs[0][1].device
+    if dev.type != "cuda":
+        raise ValueError("%s must be a GPU tensor, got device %s" % (specs[0][0], dev))
+    for name, x, _ in specs:
+        if x.device != dev:
+            raise ValueError("%s is on %s, expected %s (all tensors on one GPU)" % (name, x.device, dev))
+
+
+def _four_dims(name, x):
+    if x.dim() != 4:
+        raise ValueError("%s must be 4-D [B, H, N, d], got shape %s" % (name, tuple(x.shape)))
+    return tuple(x.shape)
+
+
 # ---------------------------------------------------------------- C entry points, same names
 
 def fa2_forward(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream=None) -> int:
@@ -180,8 +212,8 @@ def fa2_status_string(status: int) -> str:
 # ------------------------------------------------------------ torch conveniences (memory only)
 
 def _dims(q, k):
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
+    B, Hq, N, d = _four_dims("q", q)
+    Hkv = _four_dims("k", k)[1]
     return B, Hq, Hkv, N, d
 
 
@@ -193,6 +225,8 @@ def forward(q, k, v, causal: bool, scale: float, stream=None, window: int | None
     for name, x in (("q", q), ("k", k), ("v", v)):
         _expect(name, x, torch.bfloat16)
     B, Hq, Hkv, N, d = _dims(q, k)
+    _check_tensors([("q", q, (B, Hq, N, d)), ("k", k, (B, Hkv, N, d)), ("v", v, (B, Hkv, N, d))])
+    stream = _torch_stream(stream, q.device)
     o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     if window is None:
@@ -215,6 +249,12 @@ def backward(q, k, v, o, lse, dO, causal: bool, scale: float, stream=None, works
     _expect("o", o, torch.float32)
     _expect("lse", lse, torch.float32)
     B, Hq, Hkv, N, d = _dims(q, k)
+    specs = [("q", q, (B, Hq, N, d)), ("k", k, (B, Hkv, N, d)), ("v", v, (B, Hkv, N, d)),
+             ("o", o, (B, Hq, N, d)), ("lse", lse, (B, Hq, N)), ("dO", dO, (B, Hq, N, d))]
+    if workspace is not None:
+        specs.append(("workspace", workspace, tuple(workspace.shape)))
+    _check_tensors(specs)
+    stream = _torch_stream(stream, q.device)
     dq = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
     dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device)
     dv = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device)
@@ -241,8 +281,13 @@ def decode(q, k, v, causal: bool, scale: float, stream=None, workspace=None):
     import torch
     for name, x in (("q", q), ("k", k), ("v", v)):
         _expect(name, x, torch.bfloat16)
-    B, Hq, Nq, d = q.shape
-    Hkv, Nk = k.shape[1], k.shape[2]
+    B, Hq, Nq, d = _four_dims("q", q)
+    Hkv, Nk = _four_dims("k", k)[1:3]
+    specs = [("q", q, (B, Hq, Nq, d)), ("k", k, (B, Hkv, Nk, d)), ("v", v, (B, Hkv, Nk, d))]
+    if workspace is not None:
+        specs.append(("workspace", workspace, tuple(workspace.shape)))
+    _check_tensors(specs)
+    stream = _torch_stream(stream, q.device)
     o = torch.empty((B, Hq, Nq, d), dtype=torch.float32, device=q.device)
     lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
     need = fa2_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d)
@@ -261,8 +306,13 @@ def forward_fp8(q8, k8, v8, scales, causal: bool, scale: float, stream=None, wor
     import torch
     for name, x in (("q8", q8), ("k8", k8), ("v8", v8)):
         _expect(name, x, torch.uint8)
-    B, Hq, N, d = q8.shape
-    Hkv = k8.shape[1]
+    B, Hq, N, d = _four_dims("q8", q8)
+    Hkv = _four_dims("k8", k8)[1]
+    specs = [("q8", q8, (B, Hq, N, d)), ("k8", k8, (B, Hkv, N, d)), ("v8", v8, (B, Hkv, N, d))]
+    if workspace is not None:
+        specs.append(("workspace", workspace, tuple(workspace.shape)))
+    _check_tensors(specs)
+    stream = _torch_stream(stream, q8.device)
     o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q8.device)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device)
     need = fa2_forward_fp8_workspace_size(B, Hkv, N, d)

@@ -114,6 +114,9 @@ int forward_impl(const void* q, const void* k, const void* v, float* o, float* l
   const Buf out[2] = {{o, rq * d * 4}, {lse, rq * 4}};
   st = check_buffers(in, 3, out, 2);
   if (st != FA2_OK) return st;
+  // A window that hides nothing (window >= N - 1) is plain causal attention: the same launch
+  // configuration and kernels as fa2_forward, so the results are bitwise those of causal.
+  if (window >= N - 1) window = -1;
   fa2::AttnShape s{B, Hq, Hkv, N, d, causal != 0, scale, window};
   return hip_status(fa2::launch_forward(q, k, v, o, lse, s, stream));
 }
@@ -151,6 +154,22 @@ int check_workspace(const void* ws, size_t ws_bytes, int B, int Hq, int N) {
 
 }  // extern "C"
 
+namespace fa2 {
+
+int backward_check_args(const void* q, const void* k, const void* v, const float* o,
+                        const float* lse, const void* dO, float* dq, float* dk, float* dv, int B,
+                        int Hq, int Hkv, int N, int d, float scale, bool* empty) {
+  int st = check_shape(B, Hq, Hkv, N, d, scale, empty, DIMS_64_128_256);
+  if (st != FA2_OK || *empty) return st;
+  const uint64_t rq = (uint64_t)B * Hq * N, rkv = (uint64_t)B * Hkv * N;
+  const Buf in[6] = {{q, rq * d * 2}, {k, rkv * d * 2}, {v, rkv * d * 2},
+                     {o, rq * d * 4}, {lse, rq * 4},     {dO, rq * d * 2}};
+  const Buf out[3] = {{dq, rq * d * 4}, {dk, rkv * d * 4}, {dv, rkv * d * 4}};
+  return check_buffers(in, 6, out, 3);
+}
+
+}  // namespace fa2
+
 namespace {
 
 int backward_impl(const void* q, const void* k, const void* v, const float* o, const float* lse,
@@ -158,20 +177,19 @@ int backward_impl(const void* q, const void* k, const void* v, const float* o, c
                   int d, int causal, int window, float scale, void* workspace,
                   size_t workspace_bytes, hipStream_t stream) {
   bool empty = false;
-  int st = check_shape(B, Hq, Hkv, N, d, scale, &empty, DIMS_64_128_256);
+  int st = fa2::backward_check_args(q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, N, d, scale, &empty);
   if (st != FA2_OK || empty) return st;
   const uint64_t rq = (uint64_t)B * Hq * N, rkv = (uint64_t)B * Hkv * N;
   const Buf in[6] = {{q, rq * d * 2}, {k, rkv * d * 2}, {v, rkv * d * 2},
                      {o, rq * d * 4}, {lse, rq * 4},     {dO, rq * d * 2}};
   const Buf out[3] = {{dq, rq * d * 4}, {dk, rkv * d * 4}, {dv, rkv * d * 4}};
-  st = check_buffers(in, 6, out, 3);
-  if (st != FA2_OK) return st;
   st = check_workspace(workspace, workspace_bytes, B, Hq, N);
   if (st != FA2_OK) return st;
   const Buf all_in[9] = {in[0], in[1], in[2], in[3], in[4], in[5], out[0], out[1], out[2]};
   const Buf ws[1] = {{workspace, fa2_backward_workspace_size(B, Hq, N)}};
   st = check_buffers(all_in, 9, ws, 1);
   if (st != FA2_OK) return st;
+  if (window >= N - 1) window = -1;  // hides nothing: plain causal, as in forward_impl
   fa2::AttnShape s{B, Hq, Hkv, N, d, causal != 0, scale, window};
   float* w = static_cast<float*>(workspace);
   hipError_t e = fa2::launch_bwd_preprocess(o, dO, lse, w, s, stream);

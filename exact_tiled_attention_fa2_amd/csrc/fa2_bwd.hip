@@ -942,7 +942,7 @@ static BwdParams make_params(const void* q, const void* k, const void* v, const 
   p.c = fabsf(s.scale) * kLog2e;
   p.scale = s.scale;
   p.kneg = s.scale < 0.f ? 0x80008000u : 0u;
-  p.window = s.window >= 0 ? s.window : kNoWindow;
+  p.window = kernel_window(s);
   return p;
 }
 

@@ -568,7 +568,7 @@ static FwdParams forward_params(const void* q, const void* k, const void* v, flo
   const int BM = 32 * nw;  // FwdCfg<D, nw>::BM
   p.nqb = (s.N + BM - 1) / BM;
   p.xcd_remap = ((s.B * s.Hq) % 8) == 0;
-  p.window = s.window >= 0 ? s.window : kNoWindow;
+  p.window = kernel_window(s);
   p.vmul = 1.0f;
   return p;
 }

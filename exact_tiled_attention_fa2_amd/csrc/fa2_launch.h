@@ -17,6 +17,14 @@ struct AttnShape {
 // Window value the kernels use when there is none: larger than any supported N.
 constexpr int kNoWindow = 0x3fffffff;
 
+// The window the kernels see: none (kNoWindow) unless 0 <= window < N - 1. A window of N - 1 or
+// more hides no key of any row, so it is plain causal attention; mapping it here keeps the
+// kernels' index arithmetic (key + window, query - window) far from int overflow whatever value
+// the caller passed.
+inline int kernel_window(const AttnShape& s) {
+  return (s.window >= 0 && s.window < s.N - 1) ? s.window : kNoWindow;
+}
+
 hipError_t launch_forward(const void* q, const void* k, const void* v, float* o, float* lse,
                           const AttnShape& s, hipStream_t stream);
 
@@ -37,6 +45,12 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
                          const float* ws, float* dq, const AttnShape& s, hipStream_t stream);
+
+// fa2_backward's checks of its sizes and its non-workspace buffers (status codes of fa2.h);
+// sets *empty for a problem with nothing to compute. Launches nothing.
+int backward_check_args(const void* q, const void* k, const void* v, const float* o,
+                        const float* lse, const void* dO, float* dq, float* dk, float* dv, int B,
+                        int Hq, int Hkv, int N, int d, float scale, bool* empty);
 
 // Decode: s.N is unused; Nq query rows against Nk cache rows. The workspace holds the partial
 // results of the cache chunks (decode_workspace_bytes, 0 when one chunk suffices).

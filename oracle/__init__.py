@@ -43,7 +43,8 @@ def _bind(path: str):
     lib.oracle_forward.restype = cint
     lib.oracle_forward.argtypes = [p, p, p, i64, i64, i64, i64, i64, cint, i64, dbl, p, i64, p, p, cint]
     lib.oracle_row_stats.restype = cint
-    lib.oracle_row_stats.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, cint, i64, dbl, p, p, p, cint]
+    lib.oracle_row_stats.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, cint, i64, dbl, p, i64, p, p, p,
+                                     cint]
     lib.oracle_backward_dq.restype = cint
     lib.oracle_backward_dq.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, cint, i64, dbl, p, p, i64, p,
                                        cint]
@@ -115,14 +116,17 @@ class Oracle:
         return o, lse
 
     def row_stats(self, q, k, v, dO, causal: bool, scale: float, threads: int | None = None,
-                  window: int = -1):
-        """(m, l, D), each [B,Hq,N]: row max, softmax denominator, and sum_j P_ij dP_ij."""
+                  window: int = -1, rows=None):
+        """(m, l, D), each [B,Hq,R]: row max, softmax denominator, and sum_j P_ij dP_ij of the
+        query rows ``rows`` (all N rows if None; same forms as in :func:`forward`)."""
         q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
         B, Hq, Hkv, N, d = _shapes(q, k)
-        m = np.empty((B, Hq, N)); l = np.empty((B, Hq, N)); D = np.empty((B, Hq, N))
+        r = _rows(rows, B * Hq, N)
+        R = r.shape[1]
+        m = np.empty((B, Hq, R)); l = np.empty((B, Hq, R)); D = np.empty((B, Hq, R))
         rc = self.lib.oracle_row_stats(q.ctypes.data, k.ctypes.data, v.ctypes.data, dO.ctypes.data,
                                       B, Hq, Hkv, N, d, int(bool(causal)), int(window), float(scale),
-                                      m.ctypes.data, l.ctypes.data, D.ctypes.data,
+                                      r.ctypes.data, R, m.ctypes.data, l.ctypes.data, D.ctypes.data,
                                       threads or default_threads())
         if rc:
             raise RuntimeError("oracle_row_stats failed (%d)" % rc)
@@ -197,8 +201,9 @@ def forward(q, k, v, causal: bool, scale: float, rows=None, threads: int | None 
     return default().forward(q, k, v, causal, scale, rows=rows, threads=threads, window=window)
 
 
-def row_stats(q, k, v, dO, causal: bool, scale: float, threads: int | None = None, window: int = -1):
-    return default().row_stats(q, k, v, dO, causal, scale, threads=threads, window=window)
+def row_stats(q, k, v, dO, causal: bool, scale: float, threads: int | None = None, window: int = -1,
+              rows=None):
+    return default().row_stats(q, k, v, dO, causal, scale, threads=threads, window=window, rows=rows)
 
 
 def backward(q, k, v, dO, causal: bool, scale: float, qrows=None, krows=None,

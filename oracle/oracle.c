@@ -34,8 +34,9 @@
  *   (dK, dV of a key/value head sum over the query heads that share it)
  *
  * All arithmetic is fp64; every sum runs in index order, so results do not depend on the
- * thread count. Rows can be restricted to a sample: the forward and dQ take query rows,
- * dK/dV take key rows; dK/dV and dQ use the per-row statistics m, l, D of every query row.
+ * thread count. Rows can be restricted to a sample: the forward, the row statistics and dQ
+ * take query rows, dK/dV take key rows; dK/dV and dQ read the statistics m, l, D of the query
+ * rows they visit.
  *
  * Layouts: q, dO [B,Hq,N,d]; k, v [B,Hkv,N,d]; all contiguous row-major fp64.
  */
@@ -133,7 +134,8 @@ static void do_item(job_t* J, int64_t item, double* s, double* acc) {
       for (int64_t c = 0; c < d; ++c) dq[c] = J->scale * acc[c];
     }
   } else if (J->kind == K_STATS) {
-    int64_t slice = item / N, i = item % N;
+    int64_t slice = item / J->nrows, r = item % J->nrows;
+    int64_t i = J->rows[slice * J->nrows + r];
     int64_t b = slice / J->Hq, hq = slice % J->Hq, g = hq / group;
     const double* qi = J->q + (slice * N + i) * d;
     const double* dOi = J->dO + (slice * N + i) * d;
@@ -246,16 +248,19 @@ int oracle_forward(const double* q, const double* k, const double* v, int64_t B,
   return run(&J, nthreads);
 }
 
-/* Per-row statistics of every query row: m, l [B,Hq,N] and D = sum_j P_ij dP_ij [B,Hq,N]. */
+/* Per-row statistics of query rows rows[(b*Hq+hq)*nrows + r]: the row max m, the softmax
+   denominator l = sum_j exp(s_ij - m) and D = sum_j P_ij dP_ij, each [B,Hq,nrows]. */
 int oracle_row_stats(const double* q, const double* k, const double* v, const double* dO,
                      int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int causal,
-                     int64_t window, double scale, double* m, double* l, double* D, int nthreads) {
-  if (check_shape(B, Hq, Hkv, N, d, causal, window)) return -1;
+                     int64_t window, double scale, const int32_t* rows, int64_t nrows, double* m,
+                     double* l, double* D, int nthreads) {
+  if (check_shape(B, Hq, Hkv, N, d, causal, window) || check_rows(rows, B * Hq, nrows, N)) return -1;
   job_t J;
   memset(&J, 0, sizeof J);
   J.q = q; J.k = k; J.v = v; J.dO = dO; J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.N = N; J.d = d;
   J.causal = causal != 0; J.window = window < 0 ? -1 : window; J.scale = scale;
-  J.out0 = m; J.out1 = l; J.out2 = D; J.nitems = B * Hq * N; J.kind = K_STATS;
+  J.rows = rows; J.nrows = nrows;
+  J.out0 = m; J.out1 = l; J.out2 = D; J.nitems = B * Hq * nrows; J.kind = K_STATS;
   return run(&J, nthreads);
 }
 

@@ -204,10 +204,13 @@ def pin_sampled_rows_match_full(orc):
     for causal in (False, True):
         of, lf = orc.forward(q, k, v, causal, 0.5)
         os_, ls = orc.forward(q, k, v, causal, 0.5, rows=rows_q)
-        dqf, dkf, dvf, _ = orc.backward(q, k, v, dO, causal, 0.5)
+        dqf, dkf, dvf, full_stats = orc.backward(q, k, v, dO, causal, 0.5)
         dqs, dks, dvs, _ = orc.backward(q, k, v, dO, causal, 0.5, qrows=rows_q, krows=rows_k)
+        part_stats = orc.row_stats(q, k, v, dO, causal, 0.5, rows=rows_q)
         for s in range(B * Hq):
             b, h = divmod(s, Hq)
+            for part, full in zip(part_stats, full_stats):
+                assert np.array_equal(part[b, h], full[b, h, rows_q[s]])
             assert np.array_equal(os_[b, h], of[b, h, rows_q[s]])
             assert np.array_equal(ls[b, h], lf[b, h, rows_q[s]])
             assert np.array_equal(dqs[b, h], dqf[b, h, rows_q[s]])

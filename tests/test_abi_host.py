@@ -208,3 +208,40 @@ def test_binding_rejects_strided_views_and_wrong_dtypes(lib):
         fa2.forward(q.float(), q, q, True, 0.125)
     with pytest.raises(TypeError, match="uint8"):
         fa2.forward_fp8(q, q, q, (1.0, 1.0, 1.0), True, 0.125)
+
+
+def test_binding_rejects_host_tensors_and_wrong_shapes(lib):
+    # The C ABI sees bare pointers: a host buffer or a tensor shorter than the sizes imply would
+    # reach the kernels. The torch conveniences refuse both before anything is launched (CPU
+    # tensors here, so nothing could be launched anyway).
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros(1, 4, 64, 64, dtype=bf)
+    k = torch.zeros(1, 2, 64, 64, dtype=bf)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa2.forward(q, k, k, True, 0.125)
+    with pytest.raises(ValueError, match="k has shape"):
+        fa2.forward(q, torch.zeros(1, 2, 32, 64, dtype=bf), k, True, 0.125)
+    with pytest.raises(ValueError, match="v has shape"):
+        fa2.forward(q, k, torch.zeros(1, 2, 64, 32, dtype=bf), True, 0.125)
+    with pytest.raises(ValueError, match="4-D"):
+        fa2.forward(q[0], k, k, True, 0.125)
+    o = torch.zeros(1, 4, 64, 64)
+    lse = torch.zeros(1, 4, 64)
+    with pytest.raises(ValueError, match="lse has shape"):
+        fa2.backward(q, k, k, o, torch.zeros(1, 4, 63), q, True, 0.125)
+    with pytest.raises(ValueError, match="dO has shape"):
+        fa2.backward(q, k, k, o, lse, torch.zeros(1, 4, 64, 32, dtype=bf), True, 0.125)
+    with pytest.raises(ValueError, match="o has shape"):
+        fa2.backward(q, k, k, torch.zeros(1, 2, 64, 64), lse, q, True, 0.125)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa2.backward(q, k, k, o, lse, q, True, 0.125)
+    with pytest.raises(ValueError, match="v has shape"):
+        fa2.decode(q, k, torch.zeros(1, 2, 65, 64, dtype=bf), True, 0.125)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa2.decode(q[:, :, :1], k, k, True, 0.125)
+    u8 = torch.uint8
+    with pytest.raises(ValueError, match="k8 has shape"):
+        fa2.forward_fp8(torch.zeros(1, 4, 64, 128, dtype=u8), torch.zeros(1, 2, 64, 64, dtype=u8),
+                        torch.zeros(1, 2, 64, 128, dtype=u8), (1.0, 1.0, 1.0), True, 0.125)
+

@@ -98,7 +98,7 @@ def test_wide_window_is_causal():
     qd, kd, vd, dod = H.to_dev(q), H.to_dev(k), H.to_dev(v), H.to_dev(dO)
     o, lse = fa2.forward(qd, kd, vd, True, 0.1)
     grads = fa2.backward(qd, kd, vd, o, lse, dod, True, 0.1)
-    for W in (N - 1, N, 1 << 20):
+    for W in (N - 1, N, 1 << 20, 2**31 - 1):  # 2^31 - 1: the usual 'unbounded' sentinel
         ow, lw = fa2.forward(qd, kd, vd, True, 0.1, window=W)
         gw = fa2.backward(qd, kd, vd, ow, lw, dod, True, 0.1, window=W)
         torch.cuda.synchronize()

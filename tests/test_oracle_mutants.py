@@ -31,6 +31,9 @@ MUTATIONS = [
     ("dQ missing scale", "dq[c] = J->scale * acc[c];", "dq[c] = acc[c];"),
     ("dS with + D", "double dS = P * (dP - Di);", "double dS = P * (dP + Di);"),
     ("dQ uses V instead of K", "acc[c] += dS * Kh[j * d + c];", "acc[c] += dS * Vh[j * d + c];"),
+    ("row statistics ignore the chosen rows",
+     "int64_t i = J->rows[slice * J->nrows + r];\n    int64_t b = slice / J->Hq, hq = slice % J->Hq, g = hq / group;\n    const double* qi = J->q + (slice * N + i) * d;\n    const double* dOi",
+     "int64_t i = r;\n    int64_t b = slice / J->Hq, hq = slice % J->Hq, g = hq / group;\n    const double* qi = J->q + (slice * N + i) * d;\n    const double* dOi"),
     ("D without 1/l", "D += (s[j] / l) * dot(dOi, Vh + j * d, d);", "D += s[j] * dot(dOi, Vh + j * d, d);"),
     ("dK uses dO instead of Q", "dk[c] += dS * qi[c];", "dk[c] += dS * dOi[c];"),
     ("dV uses Q instead of dO", "dv[c] += P * dOi[c];", "dv[c] += P * qi[c];"),
