@@ -20,12 +20,13 @@ FA2_OK = 0
 STATUS_NAMES = {
     0: "FA2_OK", 1: "FA2_ERR_NULL_POINTER", 2: "FA2_ERR_BAD_SHAPE", 3: "FA2_ERR_UNSUPPORTED_HEAD_DIM",
     4: "FA2_ERR_BAD_GQA", 5: "FA2_ERR_BAD_SCALE", 6: "FA2_ERR_MISALIGNED", 7: "FA2_ERR_ALIASING",
-    8: "FA2_ERR_WORKSPACE", 9: "FA2_ERR_HIP", 10: "FA2_ERR_BAD_WINDOW",
+    8: "FA2_ERR_WORKSPACE", 9: "FA2_ERR_HIP", 10: "FA2_ERR_BAD_WINDOW", 11: "FA2_ERR_SCRATCH_LIMIT",
 }
+NOALLOC_SCRATCH_BYTES = 16 << 20  # FA2_NOALLOC_SCRATCH_BYTES
 EXPORTED = ("fa2_forward", "fa2_backward", "fa2_backward_workspace_size", "fa2_backward_preprocess",
             "fa2_backward_dkdv", "fa2_backward_dq", "fa2_forward_window", "fa2_backward_window",
             "fa2_decode_workspace_size", "fa2_decode", "fa2_forward_fp8_workspace_size", "fa2_forward_fp8",
-            "fa2_status_string")
+            "fa2_backward_noalloc", "fa2_status_string")
 
 _lib = None
 
@@ -70,6 +71,8 @@ def load() -> ctypes.CDLL:
     lib.fa2_forward_fp8_workspace_size.argtypes = [i, i, i, i]
     lib.fa2_forward_fp8.restype = i
     lib.fa2_forward_fp8.argtypes = [p, p, p, f, f, f, p, p, i, i, i, i, i, i, f, p, z, p]
+    lib.fa2_backward_noalloc.restype = i
+    lib.fa2_backward_noalloc.argtypes = [p, p, p, p, p, p, p, p, p, i, i, i, i, i, i, f, p]
     lib.fa2_status_string.restype = ctypes.c_char_p
     lib.fa2_status_string.argtypes = [i]
     _lib = lib
@@ -203,6 +206,13 @@ def fa2_forward_fp8(q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, d
     return load().fa2_forward_fp8(_ptr(q), _ptr(k), _ptr(v), float(q_scale), float(k_scale), float(v_scale),
                                   _ptr(o), _ptr(lse), B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
                                   _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def fa2_backward_noalloc(q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale,
+                         stream=None) -> int:
+    return load().fa2_backward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
+                                       _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
+                                       _stream(stream))
 
 
 def fa2_status_string(status: int) -> str:

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libfa2.so")
-SOURCES = ["fa2_abi.cpp", "fa2_fwd.hip", "fa2_bwd.hip", "fa2_decode.hip"]
+SOURCES = ["fa2_abi.cpp", "fa2_fwd.hip", "fa2_bwd.hip", "fa2_decode.hip", "fa2_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-Wall",

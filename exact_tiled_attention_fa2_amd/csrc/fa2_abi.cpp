@@ -96,6 +96,7 @@ const char* fa2_status_string(int status) {
     case FA2_ERR_WORKSPACE: return "FA2_ERR_WORKSPACE";
     case FA2_ERR_HIP: return "FA2_ERR_HIP";
     case FA2_ERR_BAD_WINDOW: return "FA2_ERR_BAD_WINDOW";
+    case FA2_ERR_SCRATCH_LIMIT: return "FA2_ERR_SCRATCH_LIMIT";
     default: return "FA2_UNKNOWN";
   }
 }

@@ -62,7 +62,8 @@ typedef enum {
   FA2_ERR_ALIASING = 7,             /* an output overlaps an input or another output       */
   FA2_ERR_WORKSPACE = 8,            /* workspace NULL or smaller than required             */
   FA2_ERR_HIP = 9,                  /* a kernel launch failed                              */
-  FA2_ERR_BAD_WINDOW = 10           /* sliding window < 0                                  */
+  FA2_ERR_BAD_WINDOW = 10,          /* sliding window < 0                                  */
+  FA2_ERR_SCRATCH_LIMIT = 11        /* fa2_backward_noalloc: problem exceeds its fixed buffer */
 } fa2_status;
 
 /*
@@ -197,6 +198,29 @@ int fa2_forward_fp8(const void* q, const void* k, const void* v, float q_scale, 
                     float v_scale, float* o, float* lse, int B, int Hq, int Hkv, int N, int d,
                     int causal, float scale, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
+
+/*
+ * fa2_backward for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Arguments, layouts, checks, results
+ * and guarantees are those of fa2_backward (bitwise the same outputs), without the workspace
+ * arguments: the workspace is a fixed array of FA2_NOALLOC_SCRATCH_BYTES bytes of device memory
+ * inside the library, one per GPU, which lives until the process ends. No call allocates or
+ * frees anything; the first call on a device looks up that device's array (with that device
+ * current) and keeps its address.
+ *   Limit: fa2_backward_workspace_size(B, Hq, N) <= FA2_NOALLOC_SCRATCH_BYTES, i.e.
+ *   B*Hq*N <= 2^21 query rows; larger problems return FA2_ERR_SCRATCH_LIMIT (checked before
+ *   anything else) and launch nothing.
+ *   Every call on one GPU uses that GPU's one array: calls whose work overlaps in time on the
+ *   same GPU (other streams, other host threads) race on it and corrupt each other's results;
+ *   the caller must order them (one stream, or events). Nothing in the array needs to be
+ *   zero on entry: each call overwrites the part it reads.
+ */
+#define FA2_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+int fa2_backward_noalloc(const void* q, const void* k, const void* v, const float* o,
+                         const float* lse, const void* dO, float* dq, float* dk, float* dv,
+                         int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                         hipStream_t stream);
 
 /* Static, human-readable name of a status code ("FA2_OK", ...); "FA2_UNKNOWN" otherwise. */
 const char* fa2_status_string(int status);

@@ -245,3 +245,13 @@ def test_binding_rejects_host_tensors_and_wrong_shapes(lib):
         fa2.forward_fp8(torch.zeros(1, 4, 64, 128, dtype=u8), torch.zeros(1, 2, 64, 64, dtype=u8),
                         torch.zeros(1, 2, 64, 128, dtype=u8), (1.0, 1.0, 1.0), True, 0.125)
 
+
+def test_noalloc_limit_checked_first(lib):
+    # fa2_backward_noalloc serves problems whose workspace fits its fixed device buffer; larger
+    # ones are refused before anything else (fake pointers: nothing is launched).
+    f = lambda B, Hq, N, **k: fa2.fa2_backward_noalloc(P(0), P(1), P(2), P(3), P(4), P(5), P(6), P(7), P(8),
+                                                      B, Hq, k.get("Hkv", 1), N, k.get("d", 64), 1, 0.125)
+    assert fa2.NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert fa2.fa2_backward_workspace_size(1, 32, 65536) == fa2.NOALLOC_SCRATCH_BYTES  # 2^21 rows fit
+    assert f(1, 32, 65536 + 8) == 11 and f(2, 32769, 32) == 11
+    assert f(1, 2, 128, d=96) == 3 and f(0, 2, 128) == 0 and f(-1, 2, 128) == 2
