@@ -29,6 +29,21 @@ PEAK_HBM_GBS = 8000.0
 WORKLOAD = dict(B=2, Hq=32, Hkv=32, N=8192, d=128, causal=True)
 SEED = 0x5EED0006
 
+# The pages' own figures, all measured on NVIDIA hardware. Printed beside the MI355X numbers as
+# context only: none is quoted for this workload, precision or chip, so none is a target.
+PAGES_CONTEXT = [
+    {"figure": "FlashAttention-1 utilisation of the theoretical peak FLOP/s", "value": "25-40 %",
+     "hardware": "NVIDIA A100", "source": "FlashAttention-2 (wiki), section \"Разработка и цели\""},
+    {"figure": "FlashAttention-2 utilisation of the theoretical peak FLOP/s", "value": "50-73 %",
+     "hardware": "NVIDIA A100", "source": "FlashAttention-2 (wiki), section \"Производительность и эффективность\""},
+    {"figure": "FlashAttention-2 speed-up over FlashAttention-1", "value": "about 2x", "hardware": "not stated",
+     "source": "FlashAttention-2 (wiki), section \"Производительность и эффективность\""},
+    {"figure": "FlashAttention-2 throughput", "value": "335 TFLOP/s", "hardware": "NVIDIA H100",
+     "source": "FlashAttention-2 (wiki), section \"Производительность и эффективность\""},
+    {"figure": "FlashAttention-3 throughput", "value": "up to 740 TFLOP/s, about 75 % of peak", "hardware": "NVIDIA H100",
+     "source": "Flash Attention spiegata: una guida completa, section \"Flash Attention 3\""},
+]
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -295,6 +310,147 @@ def decode(fa2, seedgen, dev, stream, steps, out):
     log("  extra %-38s %s" % ("decode_B8_Hq32_Hkv8_Nq1_Nk32768_d128", r))
 
 
+def clock_under_load(call, seconds=1.0):
+    """Median graphics clock (MHz) while ``call`` (one kernel launch) runs back to back for about
+    ``seconds``, sampled every few ms from the driver's GPU metrics (amdsmi). None when the
+    metrics cannot be read. Runs outside every timed region."""
+    import threading
+    import numpy as np
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as e:  # noqa: BLE001 - no metrics on this machine: report none
+        log("clock sampling unavailable: %s" % e)
+        return None
+
+    def read():
+        m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+        xs = m.get("current_gfxclks")
+        if isinstance(xs, (list, tuple)):
+            xs = [x for x in xs if isinstance(x, (int, float)) and 0 < x < 10000]
+            if xs:
+                return float(np.mean(xs))
+        x = m.get("current_gfxclk")
+        return float(x) if isinstance(x, (int, float)) and 0 < x < 10000 else None
+
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                v = read()
+            except Exception:  # noqa: BLE001
+                v = None
+            if v is not None:
+                samples.append(v)
+            time.sleep(0.004)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler)
+    t0 = time.perf_counter()
+    th.start()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            call()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:  # noqa: BLE001
+        pass
+    if len(samples) < 5:
+        return None
+    return {"median_mhz": round(float(np.median(samples)), 1), "p10_mhz": round(float(np.percentile(samples, 10)), 1),
+            "p90_mhz": round(float(np.percentile(samples, 90)), 1), "samples": len(samples)}
+
+
+# The five workloads (B, Hq, Hkv, N, d, causal, with backward, seed) and how the oracle covers each.
+CONFIGS = [
+    ("C1", 1, 2, 2, 256, 64, False, False, 0x5EED0001),
+    ("C2", 4, 16, 16, 2048, 64, False, False, 0x5EED0002),
+    ("C3", 2, 32, 32, 8192, 128, True, False, 0x5EED0003),
+    ("C4", 1, 32, 8, 32768, 128, True, False, 0x5EED0004),
+    ("C5", 4, 16, 16, 4096, 128, True, True, 0x5EED0005),
+]
+
+
+def oracle_per_config(gpu_ms):
+    """The fp64 oracle timed on each workload, outside every GPU timing: C1 and C2 in full; C3 and C4
+    on 256 sampled query rows of four heads; C5 (forward + backward) with the full-row statistics
+    of two heads, 256 sampled query rows (dQ) and key rows (dK, dV) of those heads. Work is counted
+    like the GPU's (4d FLOP per visible query/key pair forward; 10d fwd+bwd); sampled configs give
+    an extrapolated full time at the sample's rate. ``gpu_ms``: config name -> GPU time of the same
+    pass (forward, or forward + backward for C5), or absent."""
+    import numpy as np
+
+    import oracle
+    import seedgen
+    cores = oracle.default_threads()
+    f64 = seedgen.bf16_bits_to_f64
+    out = {}
+    for name, B, Hq, Hkv, N, d, causal, bwd, seed in CONFIGS:
+        scale = 1.0 / math.sqrt(d)
+        full_flop = counted_fwd_flops(B, Hq, N, d, causal) * (3.5 if bwd else 1.0)
+        r = {"B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "causal": causal,
+             "pass": "fwd+bwd" if bwd else "fwd", "counted_gflop_full": round(full_flop / 1e9, 2)}
+        if name in ("C1", "C2"):
+            q, k, v = (f64(x) for x in seedgen.attention_inputs(seed, B, Hq, Hkv, N, d))
+            t0 = time.perf_counter()
+            oracle.forward(q, k, v, causal, scale, threads=cores)
+            el = time.perf_counter() - t0
+            r.update({"mode": "full", "oracle_s": round(el, 4), "rows": B * Hq * N,
+                      "rows_per_s": round(B * Hq * N / el, 1), "fp64_gflops": round(full_flop / el / 1e9, 2),
+                      "full_s": round(el, 4), "full_s_kind": "measured"})
+        else:
+            heads = [0, Hq - 1] if name == "C5" else [0, Hq // 4, Hq // 2, Hq - 1]
+            nrows = 256
+            group = Hq // Hkv
+            bits = seedgen.attention_inputs(seed, 1, Hq, Hkv, N, d, with_do=bwd)  # batch 0 only
+            q, k, v = bits[:3]
+            dO = bits[3] if bwd else None
+            rows = seedgen.sample_rows_all(seed, len(heads), N, nrows)
+            el, work, nr = 0.0, 0.0, 0
+            for i, h in enumerate(heads):
+                g = h // group
+                qs, ks, vs = f64(q[:, h:h + 1]), f64(k[:, g:g + 1]), f64(v[:, g:g + 1])
+                rr = rows[i:i + 1]
+                if not bwd:
+                    t0 = time.perf_counter()
+                    oracle.forward(qs, ks, vs, causal, scale, rows=rr, threads=cores)
+                    el += time.perf_counter() - t0
+                    work += sum(4 * d * ((int(x) + 1) if causal else N) for x in rr[0])
+                    nr += rr.shape[1]
+                else:
+                    ds = f64(dO[:, h:h + 1])
+                    t0 = time.perf_counter()
+                    stats = oracle.row_stats(qs, ks, vs, ds, causal, scale, threads=cores)
+                    oracle.backward(qs, ks, vs, ds, causal, scale, qrows=rr, krows=rr, stats=stats, threads=cores)
+                    el += time.perf_counter() - t0
+                    # statistics: 4d per visible pair of the head; dQ rows 6d, dK/dV keys 8d per pair
+                    work += 4 * d * visible_pairs(N, causal)
+                    work += sum(6 * d * ((int(x) + 1) if causal else N) for x in rr[0])
+                    work += sum(8 * d * ((N - int(x)) if causal else N) for x in rr[0])
+                    nr += 2 * rr.shape[1]
+            rate = work / el
+            r.update({"mode": "sampled", "sample": "%d rows in each of %d heads (batch 0)%s" % (
+                nrows, len(heads), "; full-row statistics of those heads, then dQ at the rows and dK/dV at the same key indices" if bwd else ""),
+                "oracle_s": round(el, 4), "rows": nr, "rows_per_s": round(nr / el, 1),
+                "fp64_gflops": round(rate / 1e9, 2), "full_s": round(full_flop / rate, 2),
+                "full_s_kind": "extrapolated"})
+        r["cores"] = cores
+        if gpu_ms.get(name):
+            r["gpu_ms"] = round(gpu_ms[name], 4)
+            r["speedup_gpu_over_oracle"] = round(r["full_s"] / (gpu_ms[name] * 1e-3), 1)
+        out[name] = r
+        log("  oracle %s %s" % (name, r))
+    return out
+
+
 def cpu_baseline(q, k, v, dO, w, budget_s):
     """The fp64 oracle on a bounded sample: whole (b, h) heads of the workload, forward and
     backward in full, one head at a time until ``budget_s`` seconds have been spent."""
@@ -340,6 +496,9 @@ def main():
                     help="run only the non-headline workloads whose names contain one of these "
                          "comma-separated strings (no headline step); prints them as one JSON line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-oracle-configs", action="store_true",
+                    help="skip timing the oracle on each of the five workloads")
+    ap.add_argument("--no-clock", action="store_true", help="skip sampling the GPU clock under load")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (5 times), for scaling "
                          "HBM byte counters; prints nothing")
@@ -464,9 +623,40 @@ def main():
     if not args.no_extras:
         extras = extra_workloads(fa2, seedgen, dev, stream, max(5, args.steps))
 
+    # The graphics clock while each MFMA kernel runs alone back to back (after the timed region):
+    # the MFMA fraction at that clock says how much of the gap to the nominal peak is clock.
+    clocks = None
+    if not args.no_clock:
+        ck = {"fwd": lambda: fa2.fa2_forward(qd, kd, vd, o, lse, B, Hq, Hkv, N, d, causal, scale, stream),
+              "bwd_dkdv": lambda: fa2.fa2_backward_dkdv(qd, kd, vd, dod, ws, ws_bytes, dk, dv, B, Hq, Hkv, N, d,
+                                                        causal, scale, stream),
+              "bwd_dq": lambda: fa2.fa2_backward_dq(qd, kd, vd, dod, ws, ws_bytes, dq, B, Hq, Hkv, N, d, causal,
+                                                    scale, stream)}
+        clocks = {}
+        for n, call in ck.items():
+            c = clock_under_load(call)
+            if c is not None:
+                c["mfma_frac_at_this_clock"] = round(kernels[n]["frac"] * 2400.0 / c["median_mhz"], 4)
+                kernels[n]["clock_under_load"] = c
+            clocks[n] = c
+        log("clock under load (MHz): %s" % {n: (c or {}).get("median_mhz") for n, c in clocks.items()})
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(q, k, v, dO, w, args.cpu_seconds)
+
+    oracle_configs = None
+    if not args.no_oracle_configs:
+        gms = {"C3": avg["fwd"]}
+        if extras:
+            for cname, key, field in (("C1", "fwd_B1_H2_N256_d64", "fwd_ms"), ("C2", "fwd_B4_H16_N2048_d64", "fwd_ms"),
+                                      ("C4", "fwd_B1_Hq32_Hkv8_N32768_d128_causal", "fwd_ms")):
+                if key in extras:
+                    gms[cname] = extras[key][field]
+            e5 = extras.get("fwdbwd_B4_H16_N4096_d128_causal")
+            if e5:
+                gms["C5"] = e5["fwd_ms"] + e5["bwd_ms"]
+        oracle_configs = oracle_per_config(gms)
 
     props = torch.cuda.get_device_properties(0)
     peak_dev = peak_from_device(props)
@@ -503,6 +693,8 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "oracle_per_config": oracle_configs,
+        "pages_context": PAGES_CONTEXT,
         "extras": extras,
         "peak_tflops": PEAK_BF16_TFLOPS,
         "peak_from_device": peak_dev,

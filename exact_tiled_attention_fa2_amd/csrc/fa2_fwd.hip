@@ -467,6 +467,8 @@ void fa2_fwd_kernel(FwdParams p) {
     for (int qb = 0; qb < C::NQB; ++qb) m[qb] = -INFINITY;
     rescale_if_needed(mx);  // sets the first reference; O and l are still zero
   }
+  // Step 0 refills K(0)'s stage with K(2): every wave must be done reading K(0) first.
+  __syncthreads();
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   // Steps run in pairs (stage 0, then stage 1) so each step names its arrays statically and no

@@ -75,6 +75,37 @@ def test_prefill_shape_backward_long_rows():
     check_backward_long_causal(0x5EED0006, 2, 32, 32, 8192, 128)
 
 
+def test_prefill_shape_backward_sampled_keys_full_statistics():
+    """dK/dV of the benchmark's workload (B=2, H=32, N=8192, d=128, causal) at 256 sampled keys of
+    two (batch, head) slices -- keys 0-15 (whose query walks are the longest), key N-1 and 239
+    drawn keys -- against the oracle with the full-row statistics of those slices; dQ at 256
+    sampled rows of the same slices."""
+    B, Hq, N, d = 2, 32, 8192, 128
+    seed = 0x5EED0006
+    scale = 1.0 / math.sqrt(d)
+    q, k, v, dO = H.make_inputs(seed, B, Hq, Hq, N, d, with_do=True)
+    o, lse, dq, dk, dv = run_fwd_bwd(q, k, v, dO, True, scale)
+    rows = H.sample_rows(seed ^ 0x5A5A, 2, N, 256)
+    for i, (b, h) in enumerate(((0, 5), (1, 27))):
+        sl = lambda x: H.f64(x[b:b + 1, h:h + 1])
+        q64, k64, v64, dO64 = sl(q), sl(k), sl(v), sl(dO)
+        rr = rows[i:i + 1]
+        assert set(range(16)) <= set(rr[0].tolist()) and N - 1 in rr[0]
+        stats = oracle.row_stats(q64, k64, v64, dO64, True, scale)
+        rdq, rdk, rdv, _ = oracle.backward(q64, k64, v64, dO64, True, scale, qrows=rr, krows=rr, stats=stats)
+        idx = np.asarray(rr[0], dtype=np.int64)
+        gdq = dq[b, h].cpu().numpy().astype(np.float64)[idx]
+        gdk = dk[b, h].cpu().numpy().astype(np.float64)[idx]
+        gdv = dv[b, h].cpu().numpy().astype(np.float64)[idx]
+        eq, ek, ev = H.rel_l2(gdq, rdq[0, 0]), H.rel_l2(gdk, rdk[0, 0]), H.rel_l2(gdv, rdv[0, 0])
+        print("bwd B2 H32 N8192 slice (%d, %d), full statistics: dQ %.3e dK %.3e dV %.3e" % (b, h, eq, ek, ev))
+        assert eq <= H.TOL_GRAD and ek <= H.TOL_GRAD and ev <= H.TOL_GRAD
+        # the longest walks on their own: keys 0-15
+        ek0 = H.rel_l2(gdk[:16], rdk[0, 0, :16]) if np.all(idx[:16] == np.arange(16)) else None
+        if ek0 is not None:
+            assert ek0 <= H.TOL_GRAD and H.rel_l2(gdv[:16], rdv[0, 0, :16]) <= H.TOL_GRAD
+
+
 def test_gqa_long_backward_long_rows():
     check_backward_long_causal(0x5EED0B00, 1, 32, 8, 32768, 128, nq=16)
 
