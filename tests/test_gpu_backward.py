@@ -75,35 +75,50 @@ def test_prefill_shape_backward_long_rows():
     check_backward_long_causal(0x5EED0006, 2, 32, 32, 8192, 128)
 
 
-def test_prefill_shape_backward_sampled_keys_full_statistics():
-    """dK/dV of the benchmark's workload (B=2, H=32, N=8192, d=128, causal) at 256 sampled keys of
-    two (batch, head) slices -- keys 0-15 (whose query walks are the longest), key N-1 and 239
-    drawn keys -- against the oracle with the full-row statistics of those slices; dQ at 256
-    sampled rows of the same slices."""
-    B, Hq, N, d = 2, 32, 8192, 128
-    seed = 0x5EED0006
+def check_backward_full_statistics(seed, B, Hq, Hkv, N, d, slices):
+    """Causal dK/dV at 256 sampled keys of the given (batch, KV head) slices -- keys 0-15 (whose
+    query walks are the longest), key N-1 and 239 drawn keys -- against the oracle with the
+    full-row statistics of the query heads that share each KV head; dQ at 256 sampled rows of the
+    first query head of each group."""
     scale = 1.0 / math.sqrt(d)
-    q, k, v, dO = H.make_inputs(seed, B, Hq, Hq, N, d, with_do=True)
+    q, k, v, dO = H.make_inputs(seed, B, Hq, Hkv, N, d, with_do=True)
     o, lse, dq, dk, dv = run_fwd_bwd(q, k, v, dO, True, scale)
-    rows = H.sample_rows(seed ^ 0x5A5A, 2, N, 256)
-    for i, (b, h) in enumerate(((0, 5), (1, 27))):
-        sl = lambda x: H.f64(x[b:b + 1, h:h + 1])
-        q64, k64, v64, dO64 = sl(q), sl(k), sl(v), sl(dO)
+    rows = H.sample_rows(seed ^ 0x5A5A, len(slices), N, 256)
+    G = Hq // Hkv
+    for i, (b, g) in enumerate(slices):
+        q64, dO64 = H.f64(q[b:b + 1, g * G:(g + 1) * G]), H.f64(dO[b:b + 1, g * G:(g + 1) * G])
+        k64, v64 = H.f64(k[b:b + 1, g:g + 1]), H.f64(v[b:b + 1, g:g + 1])
         rr = rows[i:i + 1]
         assert set(range(16)) <= set(rr[0].tolist()) and N - 1 in rr[0]
         stats = oracle.row_stats(q64, k64, v64, dO64, True, scale)
-        rdq, rdk, rdv, _ = oracle.backward(q64, k64, v64, dO64, True, scale, qrows=rr, krows=rr, stats=stats)
+        rdq, rdk, rdv, _ = oracle.backward(q64, k64, v64, dO64, True, scale, qrows=np.tile(rr, (G, 1)), krows=rr,
+                                           stats=stats)
         idx = np.asarray(rr[0], dtype=np.int64)
-        gdq = dq[b, h].cpu().numpy().astype(np.float64)[idx]
-        gdk = dk[b, h].cpu().numpy().astype(np.float64)[idx]
-        gdv = dv[b, h].cpu().numpy().astype(np.float64)[idx]
+        gdq = dq[b, g * G].cpu().numpy().astype(np.float64)[idx]
+        gdk = dk[b, g].cpu().numpy().astype(np.float64)[idx]
+        gdv = dv[b, g].cpu().numpy().astype(np.float64)[idx]
         eq, ek, ev = H.rel_l2(gdq, rdq[0, 0]), H.rel_l2(gdk, rdk[0, 0]), H.rel_l2(gdv, rdv[0, 0])
-        print("bwd B2 H32 N8192 slice (%d, %d), full statistics: dQ %.3e dK %.3e dV %.3e" % (b, h, eq, ek, ev))
+        print("bwd B%d Hq%d Hkv%d N%d d%d slice (%d, %d), full statistics: dQ %.3e dK %.3e dV %.3e"
+              % (B, Hq, Hkv, N, d, b, g, eq, ek, ev))
         assert eq <= H.TOL_GRAD and ek <= H.TOL_GRAD and ev <= H.TOL_GRAD
         # the longest walks on their own: keys 0-15
-        ek0 = H.rel_l2(gdk[:16], rdk[0, 0, :16]) if np.all(idx[:16] == np.arange(16)) else None
-        if ek0 is not None:
-            assert ek0 <= H.TOL_GRAD and H.rel_l2(gdv[:16], rdv[0, 0, :16]) <= H.TOL_GRAD
+        assert np.all(idx[:16] == np.arange(16))
+        assert H.rel_l2(gdk[:16], rdk[0, 0, :16]) <= H.TOL_GRAD and H.rel_l2(gdv[:16], rdv[0, 0, :16]) <= H.TOL_GRAD
+
+
+def test_prefill_shape_backward_sampled_keys_full_statistics():
+    # the benchmark's workload: B=2, H=32, N=8192, d=128, causal
+    check_backward_full_statistics(0x5EED0006, 2, 32, 32, 8192, 128, ((0, 5), (1, 27)))
+
+
+def test_gqa_long_backward_sampled_keys_full_statistics():
+    # B=1, Hq=32, Hkv=8, N=32768: one KV head's dK/dV sums over its four query heads
+    check_backward_full_statistics(0x5EED0B00, 1, 32, 8, 32768, 128, ((0, 3),))
+
+
+def test_head_dim_256_backward_sampled_keys_full_statistics():
+    # the d = 256 extra's shape (two dK/dV passes over head-dim halves)
+    check_backward_full_statistics(0x5EED0008, 2, 16, 16, 8192, 256, ((1, 9),))
 
 
 def test_gqa_long_backward_long_rows():
