@@ -320,7 +320,17 @@ def clock_under_load(call, seconds=1.0):
     try:
         import amdsmi
         amdsmi.amdsmi_init()
-        handle = amdsmi.amdsmi_get_processor_handles()[0]
+        handles = amdsmi.amdsmi_get_processor_handles()
+        handle = None
+        props = torch.cuda.get_device_properties(torch.cuda.current_device())
+        try:  # the handle of the device the kernels run on, by PCI address
+            bdf = "%04x:%02x:%02x.0" % (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
+            handle = amdsmi.amdsmi_get_processor_handle_from_bdf(bdf)
+        except Exception:  # noqa: BLE001
+            if len(handles) == 1:
+                handle = handles[0]
+        if handle is None:
+            raise RuntimeError("cannot tell which of %d GPUs runs the kernels" % len(handles))
     except Exception as e:  # noqa: BLE001 - no metrics on this machine: report none
         log("clock sampling unavailable: %s" % e)
         return None
