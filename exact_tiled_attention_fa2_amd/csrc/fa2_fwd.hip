@@ -130,6 +130,11 @@ __device__ __forceinline__ void map_block(int bid, const FwdParams& p, int kp, i
 // 64 accumulator registers of a row block are rescaled only when a max really moves.
 constexpr float kRescaleSlack = 8.0f;
 
+// __builtin_amdgcn_sched_barrier mask that lets VALU, SALU, transcendental, VMEM and LDS-write
+// instructions be scheduled across, but neither LDS reads nor MFMAs (the all-ALU bit 0x1 would
+// let MFMAs pass too, so it stays clear).
+constexpr int kPinDsReadMfma = 0x0002 | 0x0004 | 0x0010 | 0x0020 | 0x0040 | 0x0200 | 0x0400;
+
 // FP8: Q and K are FP8 E4M3FN rows of D bytes and S^T = K Q^T runs on the FP8 MFMA (64-deep
 // k-steps); V arrives as bf16 (widened exactly from FP8 by fa2_fp8_widen_kernel), so P V and
 // everything after S are the bf16 path's. The K tile is stored like a bf16 tile of D/2
@@ -191,13 +196,18 @@ void fa2_fwd_kernel(FwdParams p) {
   const int edge = qlo + C::QPW - 1 - W;  // keys below this fall outside some row's window
   const int nlead = edge > 0 ? max(0, (edge + C::BN - 1) / C::BN - tbase) : 0;
 
-  // Tile t goes to stage t % 2: K two tiles ahead of its use, V one tile ahead.
+  // Tile t goes to stage t % 2: K two tiles ahead of its use, V one tile ahead. At d = 128,
+  // tiles at and past ntiles (beyond the end of the head, where rows read as zero, or past the
+  // causal range) are fetched anyway into stages nobody reads any more: without a branch
+  // around the loads the step body stays one basic block the scheduler can interleave (3 %
+  // faster). At d = 64 and 256 the branch stays: there the freed schedule spills registers.
+  constexpr bool kFetchAlways = D == 128;
   auto fetch_k = [&](int t) {
-    if (t < ntiles)
+    if (kFetchAlways || t < ntiles)
       load_tile<KDE, NW, false>(rk, (t & 1) ? (lds_char*)k_st1 : (lds_char*)k_st0, (tbase + t) * C::BN, wave, lane);
   };
   auto fetch_v = [&](int t) {
-    if (t < ntiles)
+    if (kFetchAlways || t < ntiles)
       load_tile<D, NW, true>(rv, (t & 1) ? (lds_char*)v_st1 : (lds_char*)v_st0, (tbase + t) * C::BN, wave, lane);
   };
 
@@ -356,6 +366,10 @@ void fa2_fwd_kernel(FwdParams p) {
     static_for<0, NOP>([&](auto J) __attribute__((always_inline)) {
       constexpr int j = decltype(J)::value;
       if constexpr (j + LA < NOP) load(std::integral_constant<int, j + LA>{});
+      // Keep this slot's LDS read ahead of the MFMAs that follow: left alone, the scheduler
+      // sinks each read next to its MFMA (one slot ahead instead of LA), and every S MFMA then
+      // waits out the LDS latency. VALU work may still move across.
+      if constexpr (D == 128) __builtin_amdgcn_sched_barrier(kPinDsReadMfma);
       if constexpr (D == 256) __builtin_amdgcn_sched_barrier(0);
       if constexpr (j < NSS) {
         constexpr int ks = j >> 1, kb = j & 1;
