@@ -299,28 +299,37 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
       ++c.h;
     }
   };
-  // Lane part of the DMA offsets (row within the tile, swizzled chunk), fixed for the kernel.
+  // Lane part of the DMA offsets (row within the tile, swizzled chunk), fixed for the kernel:
+  // [0] for this wave's 1 KB blocks of a tile, [1] for those of wave + 4.
   constexpr int LPW = PC::TILE / 1024 / PC::WAVES;
-  uint32_t dma_off[LPW];
+  uint32_t dma_off[2][LPW];
 #pragma unroll
-  for (int t = 0; t < LPW; ++t) {
-    const int pos = (wave * LPW + t) * 1024 + lane * 16;
-    const int r = pos / C::ROWB;
-    dma_off[t] = (uint32_t)(r * C::ROWB + ((((pos % C::ROWB) / 16) ^ swz_dual<D>(r)) << 4));
-  }
-  auto fetch = [&](auto S, int it, const Cursor& cur) __attribute__((always_inline)) {
-    if (it >= iters) return;
-    const int hq = g * G + cur.h;
-    const int qrow0 = (qt_top - cur.u) * BT;
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int t = 0; t < LPW; ++t) {
+      const int pos = ((wave + 4 * h) * LPW + t) * 1024 + lane * 16;
+      const int r = pos / C::ROWB;
+      dma_off[h][t] = (uint32_t)(r * C::ROWB + ((((pos % C::ROWB) / 16) ^ swz_dual<D>(r)) << 4));
+    }
+  // Q/dO tile `it` and its statistics into stage S: this wave's blocks, and with BOTH also those
+  // of wave + 4. Past the last tile (it >= iters) the loads read beyond the head's end (zeros)
+  // into a stage no wave reads again, so no branch splits the step around them.
+  auto fetch = [&](auto S, auto both, int it, const Cursor& cur) __attribute__((always_inline)) {
+    constexpr int NH = decltype(both)::value ? 2 : 1;
+    const bool live = it < iters;
+    const int hq = g * G + (live ? cur.h : 0);
+    const int qrow0 = live ? (qt_top - cur.u) * BT : N;
     const size_t qoff = ((size_t)b * p.Hq + hq) * (size_t)N * D;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + qoff, head_bytes);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dO + qoff, head_bytes);
 #pragma unroll
-    for (int t = 0; t < LPW; ++t) {
-      const uint32_t off = (uint32_t)qrow0 * C::ROWB + dma_off[t];
-      buffer_load16_lds(rq, q_st(S) + (wave * LPW + t) * 1024, off);
-      buffer_load16_lds(rd, do_st(S) + (wave * LPW + t) * 1024, off);
-    }
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int t = 0; t < LPW; ++t) {
+        const uint32_t off = (uint32_t)qrow0 * C::ROWB + dma_off[h][t];
+        buffer_load16_lds(rq, q_st(S) + ((wave + 4 * h) * LPW + t) * 1024, off);
+        buffer_load16_lds(rd, do_st(S) + ((wave + 4 * h) * LPW + t) * 1024, off);
+      }
     if (wave == 0) {
       // -D and lse2 of the tile's BT rows; lanes past BT/4 - 1 read past the end (zeros).
       const size_t roff = ((size_t)b * p.Hq + hq) * (size_t)N;
@@ -333,7 +342,7 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  fetch(I0{}, 0, Cursor{0, 0});
+  fetch(I0{}, std::false_type{}, 0, Cursor{0, 0});
 
   constexpr int KS = C::KS, DB = PC::DBP;
   int roff[C::RO], toff[DB], toff8[DB];
@@ -526,7 +535,11 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
       constexpr int st = decltype(S)::value;
       using SN = std::integral_constant<int, (st + 1) % 3>;
       using SP = std::integral_constant<int, (st + 2) % 3>;
-      fetch(SN{}, s + 1, fc);
+      // Only the P waves load the next tile, their blocks and their partners': a wave cannot
+      // issue while the CU's vector-memory queue is full, and with all eight waves issuing their
+      // loads at the start of a step each lost 300-450 cycles before its first MFMA. The P
+      // waves finish their tile several hundred cycles before their partners and absorb it.
+      if constexpr (PWAVE) fetch(SN{}, std::true_type{}, s + 1, fc);
       advance(fc);
       const int t = PWAVE ? s : s - 1;
       if (t >= 0 && t < iters) {
@@ -862,8 +875,12 @@ void fa2_bwd_dq_kernel(BwdParams p) {
     if (2 * T <= my_last) half(S, I0{}, S, I1{}, 2 * T);
     wait_vmem_all();
     __syncthreads();
-    fetch(SN2{}, T + 2);
+    // Waves 4-7 load their part of tile T+2 after half 2T+1, not beside waves 0-3 right after
+    // the barrier: a wave cannot issue while the CU's vector-memory queue is full, and half as
+    // many loads at once halves that stall. The tile is first read after the next barrier.
+    if (wave < 4) fetch(SN2{}, T + 2);
     if (2 * T + 1 <= my_last) half(S, I1{}, SN{}, I0{}, 2 * T + 1);
+    if (wave >= 4) fetch(SN2{}, T + 2);
   };
   // Two stages: tile T in stage T % 2 and T+1 in the other; half 2T+1 reads both, so the DMA
   // of tile T+2 into T's stage waits for a barrier after it.
