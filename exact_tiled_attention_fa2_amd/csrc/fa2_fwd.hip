@@ -428,6 +428,12 @@ void fa2_fwd_kernel(FwdParams p) {
     constexpr bool MASK_NEXT = decltype(mask_tag)::value;
     const lds_char* k_next = (const lds_char*)(PAR ? k_st0 : k_st1);
     const lds_char* v_cur = (const lds_char*)(PAR ? v_st1 : v_st0);
+    // 4-wave workgroups at d = 128 (two per CU, so two workgroups' waves share each SIMD): waves
+    // 2 and 3 take precedence in the MFMA/VALU arbitration during the S phase of each step. That
+    // keeps the waves of a SIMD from running the exponential-heavy S phase in step with each
+    // other: 1-4.5 % faster at B4 H16 N1024-4096 and under sliding windows (bitwise identical;
+    // at 8 waves per workgroup it measured neutral, so those keep the default).
+    if (D == 128 && NW == 4 && wave >= NW / 2) __builtin_amdgcn_s_setprio(1);
     fetch_k(t + 2);
     fetch_v(t + 1);
     PTile pf;
@@ -440,7 +446,10 @@ void fa2_fwd_kernel(FwdParams p) {
     }
     mfma_stream(std::true_type{}, std::true_type{}, k_next, sbuf[PAR ^ 1], v_cur, pf,
                 [&](int ks) { exp_pairs(sbuf[PAR], pf, sum, ks * EXP_PAIRS, (ks + 1) * EXP_PAIRS); },
-                [&](int i) { max_slice(sbuf[PAR ^ 1], mx, i * MAX_SLICE, MASK_NEXT, (tbase + t + 1) * C::BN); });
+                [&](int i) {
+                  if (D == 128 && NW == 4 && i == 0) __builtin_amdgcn_s_setprio(0);
+                  max_slice(sbuf[PAR ^ 1], mx, i * MAX_SLICE, MASK_NEXT, (tbase + t + 1) * C::BN);
+                });
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) {
       l[qb][0] += sum[qb][0];
