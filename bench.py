@@ -310,10 +310,11 @@ def decode(fa2, seedgen, dev, stream, steps, out):
     log("  extra %-38s %s" % ("decode_B8_Hq32_Hkv8_Nq1_Nk32768_d128", r))
 
 
-def clock_under_load(call, seconds=1.0):
+def clock_under_load(call, seconds=2.0, settle=0.8):
     """Median graphics clock (MHz) while ``call`` (one kernel launch) runs back to back for about
-    ``seconds``, sampled every few ms from the driver's GPU metrics (amdsmi). None when the
-    metrics cannot be read. Runs outside every timed region."""
+    ``seconds``, sampled every few ms from the driver's GPU metrics (amdsmi); samples from the
+    first ``settle`` seconds are dropped (the metrics lag the load and the clock settles under
+    the power limit). None when the metrics cannot be read. Runs outside every timed region."""
     import threading
     import numpy as np
     import torch
@@ -353,7 +354,7 @@ def clock_under_load(call, seconds=1.0):
                 v = read()
             except Exception:  # noqa: BLE001
                 v = None
-            if v is not None:
+            if v is not None and time.perf_counter() - t0 >= settle:
                 samples.append(v)
             time.sleep(0.004)
 
