@@ -429,10 +429,10 @@ void fa2_fwd_kernel(FwdParams p) {
     const lds_char* k_next = (const lds_char*)(PAR ? k_st0 : k_st1);
     const lds_char* v_cur = (const lds_char*)(PAR ? v_st1 : v_st0);
     // 4-wave workgroups at d = 128 (two per CU, so two workgroups' waves share each SIMD): waves
-    // 2 and 3 take precedence in the MFMA/VALU arbitration during the S phase of each step. That
-    // keeps the waves of a SIMD from running the exponential-heavy S phase in step with each
-    // other: 1-4.5 % faster at B4 H16 N1024-4096 and under sliding windows (bitwise identical;
-    // at 8 waves per workgroup it measured neutral, so those keep the default).
+    // 2 and 3 take precedence in the instruction arbitration during the S phase of each step,
+    // the half that carries the exponentials. Measured 1-4.5 % faster at B4 H16 N1024-4096 and
+    // under sliding windows, outputs bitwise identical; with 8-wave workgroups it measured
+    // neutral, so those keep the default order (the older wave first).
     if (D == 128 && NW == 4 && wave >= NW / 2) __builtin_amdgcn_s_setprio(1);
     fetch_k(t + 2);
     fetch_v(t + 1);
