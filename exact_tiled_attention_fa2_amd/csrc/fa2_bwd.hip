@@ -330,12 +330,13 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
         buffer_load16_lds(rq, q_st(S) + ((wave + 4 * h) * LPW + t) * 1024, off);
         buffer_load16_lds(rd, do_st(S) + ((wave + 4 * h) * LPW + t) * 1024, off);
       }
-    if (wave == 0) {
-      // -D and lse2 of the tile's BT rows; lanes past BT/4 - 1 read past the end (zeros).
+    if (wave == 1 || wave == 2) {
+      // -D (wave 1) or lse2 (wave 2) of the tile's BT rows; lanes past BT/4 - 1 read past the
+      // end (zeros).
       const size_t roff = ((size_t)b * p.Hq + hq) * (size_t)N;
       const uint32_t off = lane < BT / 4 ? (uint32_t)(qrow0 + 4 * lane) * 4 : (uint32_t)N * 4;
-      buffer_load16_lds(make_rsrc(p.delta + roff, (uint32_t)N * 4), stat_st(S), off);
-      buffer_load16_lds(make_rsrc(p.lse2 + roff, (uint32_t)N * 4), stat_st(S) + 1024, off);
+      const float* src = wave == 1 ? p.delta : p.lse2;
+      buffer_load16_lds(make_rsrc(src + roff, (uint32_t)N * 4), stat_st(S) + (wave - 1) * 1024, off);
     }
   };
 
