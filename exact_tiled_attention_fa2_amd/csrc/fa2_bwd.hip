@@ -14,7 +14,8 @@
 //                   32 keys; the first keeps K and makes P and dV, the second keeps V and
 //                   makes dS and dK from the P its partner leaves in LDS (head dim 256:
 //                   32-row tiles and two passes over head-dim halves). A workgroup takes one
-//                   block, or two mirrored pairs of blocks without grouped-query heads.
+//                   block, or four blocks (one from each quarter of the blocks sorted by
+//                   length) without grouped-query heads.
 //   3. dQ           per (batch, query head) query blocks; each wave keeps its 32 queries' Q,
 //                   dO and fp32 dQ^T in registers and walks the key tiles (eight waves, two
 //                   per SIMD; four at head dim 256). A workgroup takes a mirrored pair of
@@ -164,9 +165,9 @@ __global__ __launch_bounds__(256) void fa2_bwd_pre_kernel(const float* __restric
 // ------------------------------------------------------------------ 2. dK / dV, paired waves
 
 // Work items (workgroups per slice and head-dim pass) of the dK/dV kernel. Up to head dim 128
-// without grouped-query heads a workgroup takes two pairs of key blocks (j, nblk-1-j), which
-// spreads its fixed start-up and wind-down over four blocks (2-4% faster than one pair on causal
-// d=64 and d=128 shapes); otherwise one key block each.
+// without grouped-query heads a workgroup takes 2 kDkdvPairs key blocks, which spreads its
+// fixed start-up and wind-down over four blocks (2-4% faster than two on causal d=64 and d=128
+// shapes); otherwise one key block each.
 constexpr int kDkdvPairs = 2;
 __host__ __device__ inline int dkdv_work_items(int nblk, int G, int d) {
   return G == 1 && d <= 128 ? ((nblk + 1) / 2 + kDkdvPairs - 1) / kDkdvPairs : nblk;
@@ -241,14 +242,13 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
   const bool pwave = wave < 4;  // keeps K and produces P (else keeps V and produces dS)
   const int hf = lane >> 5, l32 = lane & 31;
   const int N = p.N;
-  // Without grouped-query heads each workgroup takes two pairs of key blocks of one slice, one
-  // block after the other: blocks 2j, nblk-1-2j, 2j+1, nblk-2-2j (causal: the heaviest with the
-  // lightest, so every workgroup carries about the same work), which spreads the workgroups'
-  // start-up and wind-down costs over four blocks (one pair against one block: 3 % at B2 H32
-  // N8192, 8 % at B4 H16 N4096; two pairs another 1-3 %). With a group of query heads
-  // per block the work per block is long already, and one block per workgroup keeps the
-  // blocks of a head walking the same query tiles in step (pairs measured 1-2 % slower); at
-  // d = 256 the two head-dim passes already double the workgroups (pairs 1 % slower).
+  // Without grouped-query heads each workgroup takes four key blocks of one slice, one block
+  // after the other (order below), which spreads the workgroups' start-up and wind-down costs
+  // over four blocks (two blocks against one: 3 % at B2 H32 N8192, 8 % at B4 H16 N4096; four
+  // another 1-3 %). With a group of query heads per block the work per block is long
+  // already, and one block per workgroup keeps the blocks of a head walking the same query
+  // tiles in step (two blocks measured 1-2 % slower); at d = 256 the two head-dim passes
+  // already double the workgroups (two blocks 1 % slower).
   const int G = p.Hq / p.Hkv;
   const int nwork = dkdv_work_items(p.nblk, G, D);
   int bg, u;
@@ -598,12 +598,16 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
   if (!paired) {
     block(j);
   } else {
-    const int npair = (p.nblk + 1) / 2;
+    // Block i of workgroup j is number j of the i-th run of nwork blocks in length order
+    // (causal: the longest key walks, the lowest blocks, first), counted from the back in odd
+    // runs, so every workgroup carries the same total. Every block walks down from the head's
+    // top query tile, and the workgroups of a slice start their even-run blocks together, so
+    // they read the same Q/dO tiles at nearly the same time: against mirrored pairs (blocks j,
+    // nblk - 1 - j), 32 % less HBM fetch at causal B2 H32 N8192 (0.95 against 1.40 GB).
     for (int i = 0; i < 2 * kDkdvPairs; ++i) {
-      const int pi = j * kDkdvPairs + i / 2;
-      const int kb = i & 1 ? p.nblk - 1 - pi : pi;
-      if (pi >= npair || (i & 1 && kb == pi)) continue;
-      block(kb);
+      const int rank = i * nwork + (i & 1 ? nwork - 1 - j : j);
+      if (rank >= p.nblk) continue;
+      block(rank);
     }
   }
 }

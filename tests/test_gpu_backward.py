@@ -167,10 +167,10 @@ def test_ragged_lengths(N, d, causal):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 129, 300, 420, 640, 900, 1100])
 def test_block_pairing_counts(N, d, causal):
-    # One KV head per query head: the dK/dV workgroups take pairs of 128-key blocks and the dQ
-    # workgroups pairs of query blocks, so N runs over 1 to 9 key blocks (odd and even counts,
-    # a middle block that is its own mirror, workgroups with a partial second pair) and
-    # ragged tails.
+    # One KV head per query head: the dK/dV workgroups take four 128-key blocks each (one from
+    # each run of the blocks in length order) and the dQ workgroups pairs of query blocks, so N
+    # runs over 1 to 9 key blocks (odd and even counts, a middle block that is its own mirror,
+    # workgroups whose last runs are partial or empty) and ragged tails.
     check_backward(2500 + N, 1, 2, 2, N, d, causal)
 
 
