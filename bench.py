@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the exact-attention hot path on one MI355X.
 
-One step = the whole path on one batch: fa2_forward (O, LSE) then the three backward kernels
-(preprocess, dK/dV, dQ), on the causal prefill workload B=2, H=32, N=8192, d=128, bf16 inputs
-drawn from the seeded generator and resident in HBM before timing starts.
+One step = the whole path on one batch: fa2_forward (O, LSE) then the two backward kernels that
+fa2_backward runs (dQ with the preprocess folded in, then dK/dV), on the causal prefill workload
+B=2, H=32, N=8192, d=128, bf16 inputs drawn from the seeded generator and resident in HBM before
+timing starts.
 
 Prints ONE JSON line on stdout. FLOPs follow the counting rule 4*B*H*N^2*d for a forward,
 halved when causal, and 2.5x that for the backward; the value is fwd+bwd TFLOP/s. Per-kernel
@@ -564,15 +565,17 @@ def main():
     ws_bytes = fa2.fa2_backward_workspace_size(B, Hq, N)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    names = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
+    # The calls fa2_backward makes, one by one so that each kernel is timed: dQ with the
+    # preprocess folded in (it leaves -D and LSE*log2(e) in the workspace), then dK/dV.
+    names = ["fwd", "bwd_dq", "bwd_dkdv"]
 
     def step(events=None):
         calls = [
             lambda: fa2.fa2_forward(qd, kd, vd, o, lse, B, Hq, Hkv, N, d, causal, scale, stream),
-            lambda: fa2.fa2_backward_preprocess(o, dod, lse, ws, ws_bytes, B, Hq, N, d, stream),
+            lambda: fa2.fa2_backward_dq_preprocess(qd, kd, vd, o, lse, dod, ws, ws_bytes, dq, B, Hq, Hkv, N, d,
+                                                   causal, scale, stream),
             lambda: fa2.fa2_backward_dkdv(qd, kd, vd, dod, ws, ws_bytes, dk, dv, B, Hq, Hkv, N, d, causal, scale,
                                           stream),
-            lambda: fa2.fa2_backward_dq(qd, kd, vd, dod, ws, ws_bytes, dq, B, Hq, Hkv, N, d, causal, scale, stream),
         ]
         for i, call in enumerate(calls):
             if events is not None:
@@ -587,7 +590,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -600,22 +603,22 @@ def main():
     for s in range(args.steps):
         for i, n in enumerate(names):
             per_kernel[n].append(ev[s][i].elapsed_time(ev[s][i + 1]))
-        steps_ms.append(ev[s][0].elapsed_time(ev[s][4]))
+        steps_ms.append(ev[s][0].elapsed_time(ev[s][len(names)]))
     avg = {n: float(np.mean(per_kernel[n])) for n in names}
     ms_step = float(np.mean(steps_ms))
 
     F = counted_fwd_flops(B, Hq, N, d, causal)
     total = 3.5 * F
     fwd_tflops = F / (avg["fwd"] * 1e-3) / 1e12
-    bwd_ms = avg["bwd_preprocess"] + avg["bwd_dkdv"] + avg["bwd_dq"]
+    bwd_ms = avg["bwd_dq"] + avg["bwd_dkdv"]
     value = total / (ms_step * 1e-3) / 1e12
     # Algorithmic work per launch: MFMA FLOPs over the visible (query, key) pairs counted as
-    # B*H*N^2/2 when causal: forward 4d per pair, dK/dV 8d, dQ 6d; preprocess moves bytes.
+    # B*H*N^2/2 when causal: forward 4d per pair, dK/dV 8d, dQ 6d (the preprocess folded into
+    # the dQ kernel, D = rowsum(dO * O), adds 2d per row, not counted).
     pairs = B * Hq * N * N / (2 if causal else 1)
     algo = {"fwd": ("mfma", pairs * 4 * d / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
             "bwd_dkdv": ("mfma", pairs * 8 * d / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
-            "bwd_dq": ("mfma", pairs * 6 * d / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
-            "bwd_preprocess": ("hbm", B * Hq * N * (d * 6 + 12) / 1e9, "GB/s", PEAK_HBM_GBS)}
+            "bwd_dq": ("mfma", pairs * 6 * d / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS)}
     kernels = {}
     for n in names:
         bound, work, unit, peak = algo[n]
@@ -641,8 +644,8 @@ def main():
         ck = {"fwd": lambda: fa2.fa2_forward(qd, kd, vd, o, lse, B, Hq, Hkv, N, d, causal, scale, stream),
               "bwd_dkdv": lambda: fa2.fa2_backward_dkdv(qd, kd, vd, dod, ws, ws_bytes, dk, dv, B, Hq, Hkv, N, d,
                                                         causal, scale, stream),
-              "bwd_dq": lambda: fa2.fa2_backward_dq(qd, kd, vd, dod, ws, ws_bytes, dq, B, Hq, Hkv, N, d, causal,
-                                                    scale, stream)}
+              "bwd_dq": lambda: fa2.fa2_backward_dq_preprocess(qd, kd, vd, o, lse, dod, ws, ws_bytes, dq, B, Hq,
+                                                               Hkv, N, d, causal, scale, stream)}
         clocks = {}
         for n, call in ck.items():
             c = clock_under_load(call)

@@ -24,9 +24,9 @@ STATUS_NAMES = {
 }
 NOALLOC_SCRATCH_BYTES = 16 << 20  # FA2_NOALLOC_SCRATCH_BYTES
 EXPORTED = ("fa2_forward", "fa2_backward", "fa2_backward_workspace_size", "fa2_backward_preprocess",
-            "fa2_backward_dkdv", "fa2_backward_dq", "fa2_forward_window", "fa2_backward_window",
-            "fa2_decode_workspace_size", "fa2_decode", "fa2_forward_fp8_workspace_size", "fa2_forward_fp8",
-            "fa2_backward_noalloc", "fa2_status_string")
+            "fa2_backward_dkdv", "fa2_backward_dq", "fa2_backward_dq_preprocess", "fa2_forward_window",
+            "fa2_backward_window", "fa2_decode_workspace_size", "fa2_decode", "fa2_forward_fp8_workspace_size",
+            "fa2_forward_fp8", "fa2_backward_noalloc", "fa2_status_string")
 
 _lib = None
 
@@ -59,6 +59,8 @@ def load() -> ctypes.CDLL:
     lib.fa2_backward_dkdv.argtypes = [p, p, p, p, p, z, p, p, i, i, i, i, i, i, f, p]
     lib.fa2_backward_dq.restype = i
     lib.fa2_backward_dq.argtypes = [p, p, p, p, p, z, p, i, i, i, i, i, i, f, p]
+    lib.fa2_backward_dq_preprocess.restype = i
+    lib.fa2_backward_dq_preprocess.argtypes = [p, p, p, p, p, p, p, z, p, i, i, i, i, i, i, f, p]
     lib.fa2_forward_window.restype = i
     lib.fa2_forward_window.argtypes = [p, p, p, p, p, i, i, i, i, i, i, f, p]
     lib.fa2_backward_window.restype = i
@@ -172,6 +174,13 @@ def fa2_backward_dq(q, k, v, dO, workspace, workspace_bytes, dq, B, Hq, Hkv, N, 
     return load().fa2_backward_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(workspace), int(workspace_bytes),
                                   _ptr(dq), B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
                                   _stream(stream))
+
+
+def fa2_backward_dq_preprocess(q, k, v, o, lse, dO, workspace, workspace_bytes, dq, B, Hq, Hkv, N, d,
+                               causal, scale, stream=None) -> int:
+    return load().fa2_backward_dq_preprocess(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
+                                             _ptr(workspace), int(workspace_bytes), _ptr(dq), B, Hq, Hkv,
+                                             N, d, int(bool(causal)), float(scale), _stream(stream))
 
 
 def fa2_forward_window(q, k, v, o, lse, B, Hq, Hkv, N, d, window, scale, stream=None) -> int:

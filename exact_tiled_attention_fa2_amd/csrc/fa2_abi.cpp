@@ -193,9 +193,8 @@ int backward_impl(const void* q, const void* k, const void* v, const float* o, c
   if (window >= N - 1) window = -1;  // hides nothing: plain causal, as in forward_impl
   fa2::AttnShape s{B, Hq, Hkv, N, d, causal != 0, scale, window};
   float* w = static_cast<float*>(workspace);
-  hipError_t e = fa2::launch_bwd_preprocess(o, dO, lse, w, s, stream);
+  hipError_t e = fa2::launch_bwd_dq_pre(q, k, v, dO, o, lse, w, dq, s, stream);
   if (e == hipSuccess) e = fa2::launch_bwd_dkdv(q, k, v, dO, w, dk, dv, s, stream);
-  if (e == hipSuccess) e = fa2::launch_bwd_dq(q, k, v, dO, w, dq, s, stream);
   return hip_status(e);
 }
 
@@ -326,6 +325,25 @@ int fa2_backward_dkdv(const void* q, const void* k, const void* v, const void* d
   if (st != FA2_OK) return st;
   fa2::AttnShape s{B, Hq, Hkv, N, d, causal != 0, scale};
   return hip_status(fa2::launch_bwd_dkdv(q, k, v, dO, static_cast<const float*>(workspace), dk, dv, s, stream));
+}
+
+int fa2_backward_dq_preprocess(const void* q, const void* k, const void* v, const float* o,
+                               const float* lse, const void* dO, void* workspace,
+                               size_t workspace_bytes, float* dq, int B, int Hq, int Hkv, int N,
+                               int d, int causal, float scale, hipStream_t stream) {
+  bool empty = false;
+  int st = check_shape(B, Hq, Hkv, N, d, scale, &empty, DIMS_64_128_256);
+  if (st != FA2_OK || empty) return st;
+  st = check_workspace(workspace, workspace_bytes, B, Hq, N);
+  if (st != FA2_OK) return st;
+  const uint64_t rq = (uint64_t)B * Hq * N, rkv = (uint64_t)B * Hkv * N;
+  const Buf in[6] = {{q, rq * d * 2}, {k, rkv * d * 2}, {v, rkv * d * 2},
+                     {o, rq * d * 4}, {lse, rq * 4},     {dO, rq * d * 2}};
+  const Buf out[2] = {{dq, rq * d * 4}, {workspace, fa2_backward_workspace_size(B, Hq, N)}};
+  st = check_buffers(in, 6, out, 2);
+  if (st != FA2_OK) return st;
+  fa2::AttnShape s{B, Hq, Hkv, N, d, causal != 0, scale};
+  return hip_status(fa2::launch_bwd_dq_pre(q, k, v, dO, o, lse, static_cast<float*>(workspace), dq, s, stream));
 }
 
 int fa2_backward_dq(const void* q, const void* k, const void* v, const void* dO,

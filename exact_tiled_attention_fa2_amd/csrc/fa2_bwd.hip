@@ -40,6 +40,8 @@ struct BwdParams {
   float* dv;
   float* delta;  // -D, [B,Hq,N]
   float* lse2;   // LSE * log2(e), [B,Hq,N]
+  const float* o;    // forward output and logsumexp: read by the dQ kernel that also does the
+  const float* lse;  // preprocess (else unused)
   int B, Hq, Hkv, N;
   int causal;
   float c;        // |scale| * log2(e)
@@ -633,7 +635,10 @@ struct DqCfg {
   static constexpr int STAGES = D <= 128 ? 3 : 2;
 };
 
-template <int D, int NW>
+// PRE: the kernel also does the preprocess step for its rows (-D and LSE log2(e) from o, dO and
+// lse) and leaves both in the workspace for a dK/dV kernel that runs after it; else it reads
+// them from the workspace.
+template <int D, int NW, bool PRE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DqCfg<D, NW>::WPE, DqCfg<D, NW>::WPE)))
 void fa2_bwd_dq_kernel(BwdParams p) {
   using C = BwdCfg<D>;
@@ -720,8 +725,35 @@ void fa2_bwd_dq_kernel(BwdParams p) {
         qf[qb][ks] = buffer_load16(rq, off) ^ p.kneg;
         df[qb][ks] = buffer_load16(rd, off);
       }
-      lse2v[qb] = qi < N ? p.lse2[(size_t)bh * N + qi] : 0.f;
-      const float nd = qi < N ? p.delta[(size_t)bh * N + qi] : 0.f;
+      float nd;
+      if constexpr (PRE) {
+        // D = sum_c dO_c O_c of the lane's query: the lane holds dO at head dims
+        // 16 ks + 8 hf .. + 7 (df), multiplies them with O there, and the two half-waves
+        // (hf = 0, 1) add their parts. Rows past the end read O = 0, so D = 0 there.
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o + qoff, (uint32_t)N * D * 4);
+        float part = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint32_t off = (uint32_t)qi * (D * 4) + (16 * ks + 8 * hf) * 4;
+          const u32x4 a = buffer_load16(ro, off), b = buffer_load16(ro, off + 16);
+          const u32x4 g = df[qb][ks];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const u32x4& x = w < 2 ? a : b;
+            part += __uint_as_float(g[w] << 16) * __uint_as_float(x[2 * (w & 1)]) +
+                    __uint_as_float(g[w] & 0xffff0000u) * __uint_as_float(x[2 * (w & 1) + 1]);
+          }
+        }
+        nd = -(part + __shfl_xor(part, 32));
+        lse2v[qb] = qi < N ? p.lse[(size_t)bh * N + qi] * kLog2e : 0.f;
+        if (hf == 0 && qi < N) {
+          p.delta[(size_t)bh * N + qi] = nd;
+          p.lse2[(size_t)bh * N + qi] = lse2v[qb];
+        }
+      } else {
+        lse2v[qb] = qi < N ? p.lse2[(size_t)bh * N + qi] : 0.f;
+        nd = qi < N ? p.delta[(size_t)bh * N + qi] : 0.f;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) negd[qb][r] = nd;
     }
@@ -1002,21 +1034,36 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
-                         const float* ws, float* dq, const AttnShape& s, hipStream_t stream) {
-  BwdParams p = make_params(q, k, v, dO, const_cast<float*>(ws), s);
-  p.dq = dq;
+template <bool PRE>
+static hipError_t launch_dq(BwdParams p, const AttnShape& s, hipStream_t stream) {
   constexpr int NW = 8;  // head dims 64 and 128: two waves per SIMD (measured 5-20 % faster)
   const int BR = s.d == 256 ? DqCfg<256>::BR : DqCfg<128, NW>::BR;
   p.nblk = (s.N + BR - 1) / BR;
   const dim3 grid((unsigned)(s.B * s.Hq * dq_work_items(p.nblk, s.d)));
   if (s.d == 128)
-    hipLaunchKernelGGL((fa2_bwd_dq_kernel<128, NW>), grid, dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((fa2_bwd_dq_kernel<128, NW, PRE>), grid, dim3(NW * 64), 0, stream, p);
   else if (s.d == 256)
-    hipLaunchKernelGGL((fa2_bwd_dq_kernel<256, 4>), grid, dim3(4 * 64), 0, stream, p);
+    hipLaunchKernelGGL((fa2_bwd_dq_kernel<256, 4, PRE>), grid, dim3(4 * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((fa2_bwd_dq_kernel<64, NW>), grid, dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((fa2_bwd_dq_kernel<64, NW, PRE>), grid, dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
+                         const float* ws, float* dq, const AttnShape& s, hipStream_t stream) {
+  BwdParams p = make_params(q, k, v, dO, const_cast<float*>(ws), s);
+  p.dq = dq;
+  return launch_dq<false>(p, s, stream);
+}
+
+hipError_t launch_bwd_dq_pre(const void* q, const void* k, const void* v, const void* dO,
+                             const float* o, const float* lse, float* ws, float* dq,
+                             const AttnShape& s, hipStream_t stream) {
+  BwdParams p = make_params(q, k, v, dO, ws, s);
+  p.dq = dq;
+  p.o = o;
+  p.lse = lse;
+  return launch_dq<true>(p, s, stream);
 }
 
 }  // namespace fa2

@@ -46,6 +46,12 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
                          const float* ws, float* dq, const AttnShape& s, hipStream_t stream);
 
+// dQ with the preprocess folded in: also fills the workspace (as launch_bwd_preprocess) from
+// o and lse, for a launch_bwd_dkdv after it.
+hipError_t launch_bwd_dq_pre(const void* q, const void* k, const void* v, const void* dO,
+                             const float* o, const float* lse, float* ws, float* dq,
+                             const AttnShape& s, hipStream_t stream);
+
 // fa2_backward's checks of its sizes and its non-workspace buffers (status codes of fa2.h);
 // sets *empty for a problem with nothing to compute. Launches nothing.
 int backward_check_args(const void* q, const void* k, const void* v, const float* o,

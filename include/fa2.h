@@ -96,9 +96,10 @@ size_t fa2_backward_workspace_size(int B, int Hq, int N);
  *   workspace    device scratch of at least fa2_backward_workspace_size(B,Hq,N) bytes,
  *                owned by the caller; its contents on entry do not matter and are
  *                overwritten. Must not overlap any other argument.
- * Three launches in stream order: a preprocess (D_i = sum_c dO_ic O_ic), a dK/dV kernel
- * (one workgroup per key block, looping over query blocks and the group's query heads) and
- * a dQ kernel (one workgroup per query block, looping over key blocks). No atomics.
+ * Two launches in stream order: a dQ kernel (one workgroup per query block, looping over key
+ * blocks) that first does the preprocess for its rows (D_i = sum_c dO_ic O_ic, written to the
+ * workspace with LSE*log2(e)), then a dK/dV kernel (one workgroup per key block, looping over
+ * query blocks and the group's query heads) that reads them. No atomics.
  */
 int fa2_backward(const void* q, const void* k, const void* v, const float* o, const float* lse,
                  const void* dO, float* dq, float* dk, float* dv,
@@ -106,10 +107,14 @@ int fa2_backward(const void* q, const void* k, const void* v, const float* o, co
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * The three steps of fa2_backward as separate calls, in the order fa2_backward runs them.
- * Each validates its own arguments like fa2_backward (same codes) and enqueues one kernel.
- * Running the three in order on one stream with one workspace gives bitwise the results of
- * fa2_backward; `workspace` must be at least fa2_backward_workspace_size(B,Hq,N) bytes.
+ * The steps of fa2_backward as separate calls. Each validates its own arguments like
+ * fa2_backward (same codes) and enqueues one kernel; `workspace` must be at least
+ * fa2_backward_workspace_size(B,Hq,N) bytes. fa2_backward_dq_preprocess then
+ * fa2_backward_dkdv, on one stream with one workspace, is what fa2_backward runs and gives
+ * bitwise its results. fa2_backward_preprocess, then fa2_backward_dkdv and fa2_backward_dq in
+ * either order, computes the same (the preprocess step on its own, as the method's backward
+ * states it: "Flash Attention spiegata: una guida completa", section "Ricomputazione"); its D
+ * is summed in another order, so results agree with fa2_backward to rounding, not bitwise.
  *
  * fa2_backward_preprocess: fills the workspace from o f32 [B,Hq,N,d], dO bf16 [B,Hq,N,d] and
  *   lse f32 [B,Hq,N] (all read only): -D_i = -sum_c dO_ic o_ic and LSE_i * log2(e).
@@ -119,7 +124,8 @@ int fa2_backward_preprocess(const float* o, const void* dO, const float* lse, vo
                             hipStream_t stream);
 
 /* fa2_backward_dkdv: dK, dV (f32 [B,Hkv,N,d], written) from q, k, v, dO and a workspace filled
-   by fa2_backward_preprocess (read only); recomputes P from the logsumexp, no atomics. */
+   by fa2_backward_preprocess or fa2_backward_dq_preprocess (read only); recomputes P from the
+   logsumexp, no atomics. */
 int fa2_backward_dkdv(const void* q, const void* k, const void* v, const void* dO,
                       const void* workspace, size_t workspace_bytes, float* dk, float* dv,
                       int B, int Hq, int Hkv, int N, int d, int causal, float scale,
@@ -129,6 +135,15 @@ int fa2_backward_dkdv(const void* q, const void* k, const void* v, const void* d
 int fa2_backward_dq(const void* q, const void* k, const void* v, const void* dO,
                     const void* workspace, size_t workspace_bytes, float* dq, int B, int Hq,
                     int Hkv, int N, int d, int causal, float scale, hipStream_t stream);
+
+/* fa2_backward_dq_preprocess: dQ (written) from q, k, v, o, lse, dO (read only), and the
+   workspace filled as fa2_backward_preprocess fills it (written: -D and LSE*log2(e) of every
+   query row), ready for fa2_backward_dkdv. The workspace counts as an output here: it must not
+   overlap any other argument. */
+int fa2_backward_dq_preprocess(const void* q, const void* k, const void* v, const float* o,
+                               const float* lse, const void* dO, void* workspace,
+                               size_t workspace_bytes, float* dq, int B, int Hq, int Hkv, int N,
+                               int d, int causal, float scale, hipStream_t stream);
 
 /*
  * Sliding-window (local) causal attention: query row i attends to key rows j with

@@ -123,6 +123,27 @@ def test_phase_entry_points_validate(lib):
     assert pre(d=192) == 3
 
 
+def test_fused_dq_preprocess_validates(lib):
+    W = fa2.fa2_backward_workspace_size(1, 2, 64)
+
+    def dqp(**k):
+        a = dict(q=P(0), k=P(1), v=P(2), o=P(3), lse=P(4), dO=P(5), ws=P(9), wsb=W, dq=P(6), B=1, Hq=2, Hkv=1,
+                 N=64, d=64, scale=0.1)
+        a.update(k)
+        return fa2.fa2_backward_dq_preprocess(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dO"], a["ws"], a["wsb"],
+                                              a["dq"], a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], 1, a["scale"])
+    assert dqp(d=96) == 3 and dqp(d=192) == 3
+    assert dqp(Hkv=3) == 4
+    assert dqp(scale=0.0) == 5
+    assert dqp(o=None) == 1 and dqp(lse=None) == 1 and dqp(dq=None) == 1
+    assert dqp(ws=None) == 8 and dqp(wsb=W - 1) == 8
+    assert dqp(ws=P(3) + 64) == 7          # workspace (written here) overlaps o
+    assert dqp(ws=P(6)) == 7               # workspace overlaps dq
+    assert dqp(dq=P(4)) == 7               # dq overlaps lse
+    assert dqp(dq=P(6) + 4) == 6
+    assert dqp(B=0) == 0                   # empty: nothing enqueued
+
+
 def fwdw(**kw):
     a = dict(q=P(0), k=P(1), v=P(2), o=P(3), lse=P(4), B=1, Hq=2, Hkv=1, N=128, d=64, window=16, scale=0.125)
     a.update(kw)

@@ -270,36 +270,55 @@ def test_backward_rejects_small_workspace():
     assert bool((dq == 3).all() and (dk == 3).all() and (dv == 3).all())
 
 
-def test_phases_match_composed_backward():
-    """The three phase entry points, in order on one stream, give fa2_backward's bits."""
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_phases_match_composed_backward(d):
+    """fa2_backward_dq_preprocess then fa2_backward_dkdv, on one stream, give fa2_backward's
+    bits; the three-step form (preprocess, dK/dV, dQ) sums D in another order and agrees to
+    rounding."""
     import torch
-    B, Hq, Hkv, N, d = 1, 4, 2, 333, 128
-    q, k, v, dO = H.make_inputs(4400, B, Hq, Hkv, N, d, with_do=True)
+    B, Hq, Hkv, N = 1, 4, 2, 333
+    q, k, v, dO = H.make_inputs(4400 + d, B, Hq, Hkv, N, d, with_do=True)
     qd, kd, vd, dod = H.to_dev(q), H.to_dev(k), H.to_dev(v), H.to_dev(dO)
     o, lse = fa2.forward(qd, kd, vd, True, 0.09)
     dq, dk, dv = fa2.backward(qd, kd, vd, o, lse, dod, True, 0.09)
     W = fa2.fa2_backward_workspace_size(B, Hq, N)
-    ws = torch.empty(W, dtype=torch.uint8, device=qd.device)
+    ws = torch.full((W,), 0xFF, dtype=torch.uint8, device=qd.device)   # NaN patterns
     dq2, dk2, dv2 = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
-    assert fa2.fa2_backward_preprocess(o, dod, lse, ws, W, B, Hq, N, d) == 0
+    assert fa2.fa2_backward_dq_preprocess(qd, kd, vd, o, lse, dod, ws, W, dq2, B, Hq, Hkv, N, d, True, 0.09) == 0
     assert fa2.fa2_backward_dkdv(qd, kd, vd, dod, ws, W, dk2, dv2, B, Hq, Hkv, N, d, True, 0.09) == 0
-    assert fa2.fa2_backward_dq(qd, kd, vd, dod, ws, W, dq2, B, Hq, Hkv, N, d, True, 0.09) == 0
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    ws3 = torch.empty(W, dtype=torch.uint8, device=qd.device)
+    dq3, dk3, dv3 = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
+    assert fa2.fa2_backward_preprocess(o, dod, lse, ws3, W, B, Hq, N, d) == 0
+    assert fa2.fa2_backward_dkdv(qd, kd, vd, dod, ws3, W, dk3, dv3, B, Hq, Hkv, N, d, True, 0.09) == 0
+    assert fa2.fa2_backward_dq(qd, kd, vd, dod, ws3, W, dq3, B, Hq, Hkv, N, d, True, 0.09) == 0
+    torch.cuda.synchronize()
+    R = B * Hq * N
+    w2, w3 = ws.view(torch.float32)[:2 * R], ws3.view(torch.float32)[:2 * R]
+    assert float((w2 - w3).abs().max()) <= 1e-6 * (1 + float(w3.abs().max()))
+    for a, b in ((dq, dq3), (dk, dk3), (dv, dv3)):
+        assert float((a - b).norm() / b.norm()) <= 1e-3
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("d", [64, 128, 256])
-def test_preprocess_workspace_layout(d):
-    """fa2_backward_preprocess leaves -D (D_i = sum_c dO_ic O_ic) at floats [0, R) and
-    LSE * log2(e) at [R, 2R), R = B*Hq*N, as the header documents."""
+def test_preprocess_workspace_layout(d, fused):
+    """fa2_backward_preprocess (or fa2_backward_dq_preprocess, which does the same step inside
+    the dQ kernel) leaves -D (D_i = sum_c dO_ic O_ic) at floats [0, R) and LSE * log2(e) at
+    [R, 2R), R = B*Hq*N, as the header documents."""
     import torch
-    B, Hq, Hkv, N = 2, 3, 3, 100
+    B, Hq, Hkv, N = 2, 3, 3, 100 + 31 * fused   # fused: rows past the last 256-row block too
     q, k, v, dO = H.make_inputs(4500 + d, B, Hq, Hkv, N, d, with_do=True)
     qd, kd, vd, dod = H.to_dev(q), H.to_dev(k), H.to_dev(v), H.to_dev(dO)
     o, lse = fa2.forward(qd, kd, vd, True, 0.1)
     W = fa2.fa2_backward_workspace_size(B, Hq, N)
     ws = torch.full((W // 4,), float("nan"), dtype=torch.float32, device=qd.device)
-    assert fa2.fa2_backward_preprocess(o, dod, lse, ws, W, B, Hq, N, d) == 0
+    if fused:
+        dq = torch.empty((B, Hq, N, d), dtype=torch.float32, device=qd.device)
+        assert fa2.fa2_backward_dq_preprocess(qd, kd, vd, o, lse, dod, ws, W, dq, B, Hq, Hkv, N, d, True, 0.1) == 0
+    else:
+        assert fa2.fa2_backward_preprocess(o, dod, lse, ws, W, B, Hq, N, d) == 0
     torch.cuda.synchronize()
     R = B * Hq * N
     got = ws.cpu().numpy().astype(np.float64)
