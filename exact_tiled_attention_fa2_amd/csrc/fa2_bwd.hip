@@ -6,8 +6,9 @@
 // a stored N x N matrix. The gradients are the chain rule of the standard definition:
 //   dV_j = sum_i P_ij dO_i,  dP_ij = <dO_i, v_j>,  dS_ij = P_ij (dP_ij - D_i),
 //   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  D_i = <dO_i, O_i>.
-// Three kernels run in stream order, none with atomics (the result is deterministic, as
-// the wiki article "FlashAttention-2" stresses in its performance section):
+// Three kernels, none with atomics (the result is deterministic, as the wiki article
+// "FlashAttention-2" stresses in its performance section); the full backward runs dQ in the
+// form that does step 1 for its own rows, then dK/dV:
 //   1. preprocess   D_i = sum_c dO_ic O_ic                   (one value per query row)
 //   2. dK/dV        per (batch, KV head) 128-key blocks, each walking every query tile of
 //                   every query head sharing the KV head: four pairs of waves, one pair per
