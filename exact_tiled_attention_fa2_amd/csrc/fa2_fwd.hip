@@ -569,15 +569,18 @@ void fa2_fwd_kernel(FwdParams p) {
 
 // Waves per workgroup: 4 (128 query rows, several workgroups per CU, so that one's start-up --
 // Q and the first K/V tiles -- and O stores overlap the others' tiles), or, at d = 128 only, 8
-// (256 rows, fewer K/V tile copies per row) for long sequences (N > 4096, and no window of 4096
-// keys or fewer, which makes each row's work as short as a short sequence's) on grids of at
-// least six 8-wave workgroups per CU: the only case where 8 measured faster. d = 64 runs three
-// 4-wave workgroups per CU and d = 256 one.
+// (256 rows, fewer K/V tile copies per row, four blocks per workgroup) where that measured
+// faster: causal with N >= 2048 on grids of at least four 256-row blocks per CU (one full round
+// of 8-wave workgroups; 6-9 % faster at B4 H16 N4096, B4 H32 N2048 and B1 Hq64 Hkv8 N4096,
+// slower below either bound), non-causal with N > 4096 on grids of at least six per CU, and
+// never under a window of 4096 keys or fewer, which makes each row's work as short as a short
+// sequence's. d = 64 runs three 4-wave workgroups per CU and d = 256 one.
 constexpr int kComputeUnits = 256;
 static int forward_waves(const AttnShape& s) {
-  if (s.d != 128 || s.N <= 4096 || (s.window >= 0 && s.window <= 4096)) return 4;
+  if (s.d != 128 || (s.window >= 0 && s.window <= 4096)) return 4;
   const long wg8 = (long)s.B * s.Hq * ((s.N + 255) / 256);
-  return wg8 < 6L * kComputeUnits ? 4 : 8;
+  if (s.causal) return s.N >= 2048 && wg8 >= 4L * kComputeUnits ? 8 : 4;
+  return s.N > 4096 && wg8 >= 6L * kComputeUnits ? 8 : 4;
 }
 
 static FwdParams forward_params(const void* q, const void* k, const void* v, float* o, float* lse,
