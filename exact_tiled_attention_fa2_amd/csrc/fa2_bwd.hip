@@ -578,16 +578,41 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
     if (s <= iters) step(I0{}, s);
     if (s + 1 <= iters) step(I1{}, s + 1);
 
-    // Store dV, or dK = scale dK^T^T: lane = key, registers = head dim (this pass's columns).
-    if (key < N) {
-      float* row = (PWAVE ? p.dv : p.dk) + kvoff + (size_t)key * D + dh * DB * 32;
+    // Store dV, or dK = scale dK^T^T: lane = key, registers = head dim (this pass's columns),
+    // 16-byte pieces 32 bytes apart. After the last barrier every LDS array is idle: each wave
+    // passes its 32 keys through its own array in column chunks and stores whole 128-byte lines
+    // (no barrier needed; the next block's loads wait for one). The lane index is made opaque so
+    // that the chunk addresses are formed here, not hoisted across the tile loop.
+    {
+      int el = lane;
+      asm volatile("" : "+v"(el));
+      const int e32 = el & 31, ehf = el >> 5;
+      constexpr int REG = PC::TILE < PC::PBUF ? PC::TILE : PC::PBUF;  // bytes per wave
+      constexpr int CW = REG / 128 < DB * 32 ? REG / 128 : DB * 32;      // columns per chunk
+      constexpr int UPR = CW / 4;                                        // 16-byte units per row
+      static_assert(CW % 32 == 0 && (DB * 32) % CW == 0 && (UPR & (UPR - 1)) == 0, "chunk shape");
+      lds_char* reg = (lds_char*)(wave == 0 ? t0_do0 : wave == 1 ? t1_do1 : wave == 2 ? t2_do2
+                                  : wave == 3 ? t3_q0 : wave == 4 ? t4_q1 : wave == 5 ? t5_q2
+                                  : wave == 6 ? t6_pbuf0 : t7_pbuf1);
+      float* base = (PWAVE ? p.dv : p.dk) + kvoff + (size_t)kw * D + dh * DB * 32;
       const float f = PWAVE ? 1.f : p.scale;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int c = 0; c < DB * 32 / CW; ++c) {
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq)
-          *(f32x4*)(row + 32 * db + 8 * rq + 4 * hf) =
-              f32x4{acc[db][4 * rq], acc[db][4 * rq + 1], acc[db][4 * rq + 2], acc[db][4 * rq + 3]} * f;
+        for (int dbc = 0; dbc < CW / 32; ++dbc)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const int db = c * (CW / 32) + dbc, cu = 8 * dbc + 2 * rq + ehf;
+            *(FA2_LDS f32x4*)(reg + e32 * (UPR * 16) + ((cu ^ (e32 & (UPR - 1))) << 4)) =
+                f32x4{acc[db][4 * rq], acc[db][4 * rq + 1], acc[db][4 * rq + 2], acc[db][4 * rq + 3]} * f;
+          }
+#pragma unroll
+        for (int k = 0; k < UPR / 2; ++k) {
+          const int u = 64 * k + el, r = u / UPR, cu = u % UPR;
+          const f32x4 val = *(const FA2_LDS f32x4*)(reg + r * (UPR * 16) + ((cu ^ (r & (UPR - 1))) << 4));
+          if (kw + r < N) *(f32x4*)(base + (size_t)r * D + c * CW + 4 * cu) = val;
+        }
+      }
     }
   };
 
@@ -607,9 +632,12 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
     // top query tile, and the workgroups of a slice start their even-run blocks together, so
     // they read the same Q/dO tiles at nearly the same time: against mirrored pairs (blocks j,
     // nblk - 1 - j), 32 % less HBM fetch at causal B2 H32 N8192 (0.95 against 1.40 GB).
+    bool first = true;
     for (int i = 0; i < 2 * kDkdvPairs; ++i) {
       const int rank = i * nwork + (i & 1 ? nwork - 1 - j : j);
       if (rank >= p.nblk) continue;
+      if (!first) __syncthreads();  // every wave is done with its stores' LDS staging
+      first = false;
       block(rank);
     }
   }
@@ -949,18 +977,45 @@ void fa2_bwd_dq_kernel(BwdParams p) {
     if (T < ntiles) tile_iter2(I0{}, T);
   }
 
+  // Store dQ = scale dQ^T^T: lane = query, registers = head dim, 16-byte pieces 32 bytes apart.
+  // Once every wave is past its last reads (and the last look-ahead load has landed), each wave
+  // passes its 32 rows through half of one K/V stage array in column chunks and stores whole
+  // 128-byte lines. The lane index is made opaque so that the chunk addresses are formed here,
+  // not hoisted across the tile loop.
+  static_assert(NQB == 1, "one 32-row block per wave");
+  wait_vmem_all();
+  __syncthreads();
+  {
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    const int e32 = el & 31, ehf = el >> 5;
+    constexpr int REG = Q::TILE / 2;                             // bytes per wave
+    constexpr int CW = REG / 128 < DB * 32 ? REG / 128 : DB * 32;  // columns per chunk
+    constexpr int UPR = CW / 4;                                  // 16-byte units per row
+    static_assert(CW % 32 == 0 && (DB * 32) % CW == 0 && (UPR & (UPR - 1)) == 0, "chunk shape");
+    // Waves 2a and 2a+1 share array a of k_st0, k_st1, k_st2, v_st0 (four waves at d = 256 use
+    // only the first two, full-size arrays).
+    static_assert(NW == 8 ? Q::STAGES == 3 : NW == 4, "the arrays the waves use");
+    const int arr = wave >> 1;
+    lds_char* reg = (lds_char*)(arr == 0 ? k_st0 : arr == 1 ? k_st1 : arr == 2 ? k_st2 : v_st0) + (wave & 1) * REG;
+    float* base = p.dq + qoff + (size_t)qw * D;
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int qi = qw + 32 * qb + l32;
-    if (qi < N) {
-      float* dqrow = p.dq + qoff + (size_t)qi * D;
+    for (int c = 0; c < DB * 32 / CW; ++c) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int dbc = 0; dbc < CW / 32; ++dbc)
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq)
-          *(f32x4*)(dqrow + 32 * db + 8 * rq + 4 * hf) =
-              f32x4{adq[qb][db][4 * rq], adq[qb][db][4 * rq + 1], adq[qb][db][4 * rq + 2],
-                    adq[qb][db][4 * rq + 3]} * p.scale;
+        for (int rq = 0; rq < 4; ++rq) {
+          const int db = c * (CW / 32) + dbc, cu = 8 * dbc + 2 * rq + ehf;
+          *(FA2_LDS f32x4*)(reg + e32 * (UPR * 16) + ((cu ^ (e32 & (UPR - 1))) << 4)) =
+              f32x4{adq[0][db][4 * rq], adq[0][db][4 * rq + 1], adq[0][db][4 * rq + 2],
+                    adq[0][db][4 * rq + 3]} * p.scale;
+        }
+#pragma unroll
+      for (int k = 0; k < UPR / 2; ++k) {
+        const int u = 64 * k + el, r = u / UPR, cu = u % UPR;
+        const f32x4 val = *(const FA2_LDS f32x4*)(reg + r * (UPR * 16) + ((cu ^ (r & (UPR - 1))) << 4));
+        if (qw + r < N) *(f32x4*)(base + (size_t)r * D + c * CW + 4 * cu) = val;
+      }
     }
   }
   };
