@@ -13,10 +13,11 @@
 //   2. dK/dV        per (batch, KV head) 128-key blocks, each walking every query tile of
 //                   every query head sharing the KV head: four pairs of waves, one pair per
 //                   32 keys; the first keeps K and makes P and dV, the second keeps V and
-//                   makes dS and dK from the P its partner leaves in LDS (head dim 256:
-//                   32-row tiles and two passes over head-dim halves). A workgroup takes one
-//                   block, or four blocks (one from each quarter of the blocks sorted by
-//                   length) without grouped-query heads.
+//                   makes dS and dK from the P its partner leaves in LDS. A workgroup takes
+//                   one block, or four blocks (one from each quarter of the blocks sorted by
+//                   length) without grouped-query heads. Head dim 256: 64-key blocks, a quad
+//                   of waves per 32 keys (S and dP computed once, dV and dK split by head-dim
+//                   half, P and dS handed over through LDS).
 //   3. dQ           per (batch, query head) query blocks; each wave keeps its 32 queries' Q,
 //                   dO and fp32 dQ^T in registers and walks the key tiles (eight waves, two
 //                   per SIMD; four at head dim 256). A workgroup takes a mirrored pair of
@@ -167,13 +168,13 @@ __global__ __launch_bounds__(256) void fa2_bwd_pre_kernel(const float* __restric
 
 // ------------------------------------------------------------------ 2. dK / dV, paired waves
 
-// Work items (workgroups per slice and head-dim pass) of the dK/dV kernel. Up to head dim 128
-// without grouped-query heads a workgroup takes 2 kDkdvPairs key blocks, which spreads its
-// fixed start-up and wind-down over four blocks (2-4% faster than two on causal d=64 and d=128
+// Work items (workgroups per slice) of the paired dK/dV kernel (head dims 64 and 128). Without
+// grouped-query heads a workgroup takes 2 kDkdvPairs key blocks, which spreads its fixed
+// start-up and wind-down over four blocks (2-4% faster than two on causal d=64 and d=128
 // shapes); otherwise one key block each.
 constexpr int kDkdvPairs = 2;
-__host__ __device__ inline int dkdv_work_items(int nblk, int G, int d) {
-  return G == 1 && d <= 128 ? ((nblk + 1) / 2 + kDkdvPairs - 1) / kDkdvPairs : nblk;
+__host__ __device__ inline int dkdv_work_items(int nblk, int G) {
+  return G == 1 ? ((nblk + 1) / 2 + kDkdvPairs - 1) / kDkdvPairs : nblk;
 }
 // Pairs of query blocks per dQ workgroup: two at head dim 256 (3% faster than one), one below,
 // where a second pair measured no faster.
@@ -196,20 +197,15 @@ __host__ __device__ inline int dq_work_items(int nblk, int d) {
 // and they add nothing to dV or dK.
 template <int D>
 struct PairCfg {
+  static_assert(D <= 128, "head dim 256 runs the quad kernel below");
   static constexpr int WAVES = 8;
   static constexpr int PAIRS = 4;
   static constexpr int RPW = 32;             // keys per pair
   static constexpr int BR = PAIRS * RPW;     // keys per workgroup
-  // Query rows per tile: 64 (two 32-row blocks) up to d = 128; 32 at d = 256, where three
-  // stages of Q and dO then still fit in LDS.
-  static constexpr int BT = D <= 128 ? 64 : 32;
+  static constexpr int BT = 64;              // query rows per tile (two 32-row blocks)
   static constexpr int NMB = BT / 32;
   static constexpr int TILE = BT * 2 * D;
-  // dK/dV head-dim blocks a wave accumulates per pass: all of them up to d = 128; at d = 256 a
-  // wave's K (or V) and its full dK (or dV) would not fit beside the rest, so two passes
-  // (workgroups) each accumulate 128 columns and recompute S and dP over the full d.
-  static constexpr int DBP = (D <= 128 ? D : 128) / 32;
-  static constexpr int NDH = D / (32 * DBP);
+  static constexpr int DBP = D / 32;         // dK/dV head-dim blocks of a wave: all of them
   static constexpr int PBUF = PAIRS * NMB * 2048;  // one tile's P: [pair][row block][half][lane] x 16 B
   // The LDS statistics arrays come after the tiles and P buffers: reads reach them through a
   // base lowered by this much.
@@ -250,15 +246,12 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
   // over four blocks (two blocks against one: 3 % at B2 H32 N8192, 8 % at B4 H16 N4096; four
   // another 1-3 %). With a group of query heads per block the work per block is long
   // already, and one block per workgroup keeps the blocks of a head walking the same query
-  // tiles in step (two blocks measured 1-2 % slower); at d = 256 the two head-dim passes
-  // already double the workgroups (two blocks 1 % slower).
+  // tiles in step (two blocks measured 1-2 % slower).
   const int G = p.Hq / p.Hkv;
-  const int nwork = dkdv_work_items(p.nblk, G, D);
-  int bg, u;
-  map_slice_block(blockIdx.x, p.B * p.Hkv, nwork * PC::NDH, bg, u);
-  const int dh = u % PC::NDH;  // which head-dim part of dK/dV this workgroup accumulates
-  const int j = u / PC::NDH;
-  const bool paired = G == 1 && D <= 128;
+  const int nwork = dkdv_work_items(p.nblk, G);
+  int bg, j;
+  map_slice_block(blockIdx.x, p.B * p.Hkv, nwork, bg, j);
+  const bool paired = G == 1;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   auto block = [&](int kblk) __attribute__((always_inline)) {
   const int k0 = kblk * PC::BR;
@@ -354,8 +347,8 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
   for (int ks = 0; ks < C::RO; ++ks) roff[ks] = row_read_off<D>(lane, ks);
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
-    toff[db] = tr_read_off<D>(lane, dh * DB + db, 0);
-    toff8[db] = tr_read_off<D>(lane, dh * DB + db, 1);
+    toff[db] = tr_read_off<D>(lane, db, 0);
+    toff8[db] = tr_read_off<D>(lane, db, 1);
   }
 
   const float c = p.c;
@@ -368,9 +361,7 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
   // kernel they measured 1-3 % faster and stay).
   // The P or dS values of row block mb become readable DL steps after its last S or dP step
   // (ready) and are consumed from step use(mb, h) on: the first half's eight values are made
-  // in [ready, use(mb, 0)), the second half's in [use(mb, 0), use(mb, 1)). With one row block
-  // (d = 256) the first half's values are formed in the step before their first use, waiting
-  // on the last S or dP MFMA; the partner wave keeps the SIMD busy meanwhile.
+  // in [ready, use(mb, 0)), the second half's in [use(mb, 0), use(mb, 1)).
   constexpr int NS = NMB * KS + NMB * 2 * DB;
   constexpr int PF = 3;
   constexpr int DL = 2;
@@ -594,7 +585,7 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
       lds_char* reg = (lds_char*)(wave == 0 ? t0_do0 : wave == 1 ? t1_do1 : wave == 2 ? t2_do2
                                   : wave == 3 ? t3_q0 : wave == 4 ? t4_q1 : wave == 5 ? t5_q2
                                   : wave == 6 ? t6_pbuf0 : t7_pbuf1);
-      float* base = (PWAVE ? p.dv : p.dk) + kvoff + (size_t)kw * D + dh * DB * 32;
+      float* base = (PWAVE ? p.dv : p.dk) + kvoff + (size_t)kw * D;
       const float f = PWAVE ? 1.f : p.scale;
 #pragma unroll
       for (int c = 0; c < DB * 32 / CW; ++c) {
@@ -640,6 +631,380 @@ void fa2_bwd_dkdv_pair_kernel(BwdParams p) {
       first = false;
       block(rank);
     }
+  }
+}
+
+// ------------------------------------------------------------------ 2b. dK/dV at head dim 256
+
+// At head dim 256 a wave cannot hold both its keys' K (or V) and their whole dV (or dK) beside
+// the rest, so the work of each 32 keys is split over a quad of waves by role and by half of the
+// head dim, and S and dP are computed once:
+//   A_P  (waves 0, 2): K; S = Q K^T, P = 2^(S c - lse2) -> LDS; dV^T[0:128) += dO^T P
+//   A_DP (waves 1, 3): V; dP = dO V^T (from -D), dS = P (dP - D) with P from LDS -> LDS;
+//                      dK^T[0:128) += Q^T dS
+//   B_DV (waves 5, 7): dV^T[128:256) += dO^T P, P from LDS
+//   B_DK (waves 4, 6): dK^T[128:256) += Q^T dS, dS from LDS
+// Waves w and w + 4 share a SIMD, so each SIMD pairs an A role (24 MFMAs per 32-row query
+// tile) with a B role (8), and a quad's four waves sit on two SIMDs. A_P takes tile s at step
+// s, A_DP and B_DV tile s - 1, B_DK tile s - 2; Q/dO tiles stream through four stages
+// (tile s + 1 lands while s, s - 1, s - 2 are read), P and dS through two buffers each; the
+// B waves, with the least MFMA work, issue every load. One barrier per step.
+struct QuadCfg {
+  static constexpr int D = 256;
+  static constexpr int WAVES = 8;
+  static constexpr int RPW = 32;           // keys per quad
+  static constexpr int BR = 2 * RPW;       // keys per workgroup
+  static constexpr int BT = 32;            // query rows per tile
+  static constexpr int ROWB = 2 * D;
+  static constexpr int TILE = BT * ROWB;   // 16 KB of Q or dO
+  static constexpr int KS = D / 16;        // k-steps of S or dP
+  static constexpr int DB = 4;             // 32-wide head-dim blocks of a wave's dV or dK
+  static constexpr int QBUF = 2 * 2048;    // one tile's P (or dS) of both quads
+  static constexpr int LPW = TILE / 1024 / WAVES;  // 1 KB loads per slot of eight
+};
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa2_bwd_dkdv_quad_kernel(BwdParams p) {
+  using Q = QuadCfg;
+  constexpr int D = Q::D, KS = Q::KS, DB = Q::DB, BT = Q::BT;
+  using C = BwdCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char q_st0[Q::TILE];
+  __shared__ __attribute__((aligned(1024))) char q_st1[Q::TILE];
+  __shared__ __attribute__((aligned(1024))) char q_st2[Q::TILE];
+  __shared__ __attribute__((aligned(1024))) char q_st3[Q::TILE];
+  __shared__ __attribute__((aligned(1024))) char do_st0[Q::TILE];
+  __shared__ __attribute__((aligned(1024))) char do_st1[Q::TILE];
+  __shared__ __attribute__((aligned(1024))) char do_st2[Q::TILE];
+  __shared__ __attribute__((aligned(1024))) char do_st3[Q::TILE];
+  __shared__ __attribute__((aligned(1024))) char p_buf0[Q::QBUF];
+  __shared__ __attribute__((aligned(1024))) char p_buf1[Q::QBUF];
+  __shared__ __attribute__((aligned(1024))) char ds_buf0[Q::QBUF];
+  __shared__ __attribute__((aligned(1024))) char ds_buf1[Q::QBUF];
+  __shared__ __attribute__((aligned(1024))) char st_st0[2048];
+  __shared__ __attribute__((aligned(1024))) char st_st1[2048];
+  __shared__ __attribute__((aligned(1024))) char st_st2[2048];
+  __shared__ __attribute__((aligned(1024))) char st_st3[2048];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int simd = wave & 3, quad = simd >> 1;
+  const bool awave = wave < 4, odd = simd & 1;
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int N = p.N;
+  const int G = p.Hq / p.Hkv;
+  int bg, kblk;
+  map_slice_block(blockIdx.x, p.B * p.Hkv, p.nblk, bg, kblk);
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const int k0 = kblk * Q::BR;
+  const int kw = k0 + quad * Q::RPW;  // the quad's first key
+  const uint32_t head_bytes = (uint32_t)N * Q::ROWB;
+  const size_t kvoff = ((size_t)b * p.Hkv + g) * (size_t)N * D;
+
+  // Query tiles as in the paired kernel: every query head of the group, from the top tile that
+  // sees a key of the block down to the one holding key k0.
+  const int W = p.window;
+  const int nqt_all = (N + BT - 1) / BT;
+  const int qt0 = p.causal ? k0 / BT : 0;
+  const int qt_top = min(nqt_all - 1, (k0 + Q::BR - 1 + W) / BT);
+  const int nqt = qt_top - qt0 + 1;
+  const int iters = G * nqt;
+
+  auto q_st = [&](auto S) __attribute__((always_inline)) {
+    constexpr int s = decltype(S)::value & 3;
+    return (lds_char*)(s == 0 ? q_st0 : s == 1 ? q_st1 : s == 2 ? q_st2 : q_st3);
+  };
+  auto do_st = [&](auto S) __attribute__((always_inline)) {
+    constexpr int s = decltype(S)::value & 3;
+    return (lds_char*)(s == 0 ? do_st0 : s == 1 ? do_st1 : s == 2 ? do_st2 : do_st3);
+  };
+  auto st_st = [&](auto S) __attribute__((always_inline)) {
+    constexpr int s = decltype(S)::value & 3;
+    return (lds_char*)(s == 0 ? st_st0 : s == 1 ? st_st1 : s == 2 ? st_st2 : st_st3);
+  };
+  auto p_buf = [&](auto S) __attribute__((always_inline)) {
+    return (lds_char*)((decltype(S)::value & 1) ? p_buf1 : p_buf0);
+  };
+  auto ds_buf = [&](auto S) __attribute__((always_inline)) {
+    return (lds_char*)((decltype(S)::value & 1) ? ds_buf1 : ds_buf0);
+  };
+  struct Cursor {
+    int h, u;
+  };
+  auto advance = [&](Cursor& c) __attribute__((always_inline)) {
+    if (++c.u == nqt) {
+      c.u = 0;
+      ++c.h;
+    }
+  };
+  // DMA offsets of load slots `wave & 3` and `(wave & 3) + 4` (the slots this wave fills when it
+  // loads a whole tile with another wave), and slot `wave` (the first tile, loaded by all).
+  uint32_t dma_off[3][Q::LPW];
+#pragma unroll
+  for (int h = 0; h < 3; ++h)
+#pragma unroll
+    for (int t = 0; t < Q::LPW; ++t) {
+      const int slot = h == 2 ? wave : (wave & 3) + 4 * h;
+      const int pos = (slot * Q::LPW + t) * 1024 + lane * 16;
+      const int r = pos / Q::ROWB;
+      dma_off[h][t] = (uint32_t)(r * Q::ROWB + ((((pos % Q::ROWB) / 16) ^ swz_dual<D>(r)) << 4));
+    }
+  // Tile `it` into stage S: slots h in [H0, H1) of dma_off; -D by wave 5, lse2 by wave 6.
+  auto fetch = [&](auto S, auto H0, auto H1, int it, const Cursor& cur) __attribute__((always_inline)) {
+    const bool live = it < iters;
+    const int hq = g * G + (live ? cur.h : 0);
+    const int qrow0 = live ? (qt_top - cur.u) * BT : N;
+    const size_t qoff = ((size_t)b * p.Hq + hq) * (size_t)N * D;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + qoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dO + qoff, head_bytes);
+    static_for<decltype(H0)::value, decltype(H1)::value>([&](auto HH) __attribute__((always_inline)) {
+      constexpr int h = decltype(HH)::value;
+      const int slot = h == 2 ? wave : (wave & 3) + 4 * h;
+#pragma unroll
+      for (int t = 0; t < Q::LPW; ++t) {
+        const uint32_t off = (uint32_t)qrow0 * Q::ROWB + dma_off[h][t];
+        buffer_load16_lds(rq, q_st(S) + (slot * Q::LPW + t) * 1024, off);
+        buffer_load16_lds(rd, do_st(S) + (slot * Q::LPW + t) * 1024, off);
+      }
+    });
+    if (wave == 5 || wave == 6) {
+      const size_t roff = ((size_t)b * p.Hq + hq) * (size_t)N;
+      const uint32_t off = lane < BT / 4 ? (uint32_t)(qrow0 + 4 * lane) * 4 : (uint32_t)N * 4;
+      const float* src = wave == 5 ? p.delta : p.lse2;
+      buffer_load16_lds(make_rsrc(src + roff, (uint32_t)N * 4), st_st(S) + (wave - 5) * 1024, off);
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  fetch(I0{}, I2{}, I3{}, 0, Cursor{0, 0});
+
+  // A roles accumulate head-dim blocks 0-3, B roles 4-7.
+  const int dh = awave ? 0 : 1;
+  int roff[C::RO], toff[DB], toff8[DB];
+#pragma unroll
+  for (int ks = 0; ks < C::RO; ++ks) roff[ks] = row_read_off<D>(lane, ks);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    toff[db] = tr_read_off<D>(lane, dh * DB + db, 0);
+    toff8[db] = tr_read_off<D>(lane, dh * DB + db, 1);
+  }
+  const float c = p.c;
+  const int key = kw + l32;
+  const int qslot = quad * 2048 + lane * 16;  // this lane's 16 bytes of a quad's P or dS (+ h KB)
+
+  // A roles, one query tile: KS steps of S (or dP), then 2 DB steps of dV^T (or dK^T); P (or dS)
+  // of half h is formed just before its first use, waiting on the last S or dP MFMA while the
+  // B wave on the same SIMD keeps it busy.
+  constexpr int NS = KS + 2 * DB;
+  constexpr int PF = 3;
+  auto tile_a = [&](auto PW, const u32x4 (&kv)[KS], f32x16 (&acc)[DB], const lds_char* rsrc,
+                    const lds_char* tsrc, const lds_char* stat, lds_char* pin, lds_char* pout,
+                    int qrow0, bool fix) __attribute__((always_inline)) {
+    constexpr bool PWAVE = decltype(PW)::value;
+    f32x16 sd = f32x16{};
+    u32x4 op[2];
+    float pf[16];
+    f32x4 st4[4];
+    const FA2_LDS float* sbase = (const FA2_LDS float*)(stat + 16 * hf);
+    auto load_stats = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) st4[rq] = *(const FA2_LDS f32x4*)(sbase + 8 * rq);
+    };
+    auto causal_fixup = [&](int h) __attribute__((always_inline)) {
+      const int lo = key - qrow0 - 4 * hf;
+      const int hi = lo + W;
+#pragma unroll
+      for (int r = 8 * h; r < 8 * h + 8; r += 2) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int x = 8 * ((r + u) >> 2) + ((r + u) & 3);
+          pf[r + u] = (x >= lo && x <= hi) ? pf[r + u] : 0.f;
+        }
+        op[h][(r >> 1) & 3] = pack_bf16(pf[r], pf[r + 1]);
+      }
+    };
+    auto values = [&](int h) __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int r = 8 * h + e;
+        if constexpr (PWAVE) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            pf[r + u] = fast_exp2(__builtin_fmaf(sd[r + u], c, -st4[(r + u) >> 2][(r + u) & 3]));
+          op[h][(r >> 1) & 3] = pack_bf16(pf[r], pf[r + 1]);
+        } else {
+          const unsigned w = op[h][(r >> 1) & 3];
+          const float p0 = __uint_as_float(w << 16), p1 = __uint_as_float(w & 0xffff0000u);
+          op[h][(r >> 1) & 3] = pack_bf16(p0 * sd[r], p1 * sd[r + 1]);
+        }
+      }
+    };
+    auto read_op = [&](auto J) __attribute__((always_inline)) -> u32x4 {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j < KS) {
+        return lds_read16(rsrc + roff[j % C::RO] + (j / C::RO) * 256);
+      } else {
+        constexpr int i = j - KS, db = i % DB, h = i / DB;
+        return tr_pair(tsrc + toff[db] + 16 * h * Q::ROWB, tsrc + toff8[db] + 16 * h * Q::ROWB);
+      }
+    };
+    load_stats();
+    if constexpr (!PWAVE) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) op[h] = lds_read16(pin + qslot + h * 1024);
+    }
+    u32x4 ring[PF + 1];
+    static_for<0, PF>([&](auto J) __attribute__((always_inline)) { ring[decltype(J)::value] = read_op(J); });
+    static_for<0, NS>([&](auto J) __attribute__((always_inline)) {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j + PF < NS) ring[(j + PF) % (PF + 1)] = read_op(std::integral_constant<int, j + PF>{});
+      if constexpr (j < KS) {
+        if constexpr (!PWAVE && j == 0) {
+          // The dP chain starts from -D (register r holds row 8 (r/4) + 4 hf + r%4).
+          const f32x16 init = {st4[0][0], st4[0][1], st4[0][2], st4[0][3], st4[1][0], st4[1][1],
+                               st4[1][2], st4[1][3], st4[2][0], st4[2][1], st4[2][2], st4[2][3],
+                               st4[3][0], st4[3][1], st4[3][2], st4[3][3]};
+          sd = mfma32x32x16(ring[j % (PF + 1)], kv[0], init);
+        } else {
+          sd = mfma32x32x16(ring[j % (PF + 1)], kv[j], sd);
+        }
+        if constexpr (j == KS - 1) {
+          values(0);
+          if constexpr (PWAVE) {
+            if (fix) causal_fixup(0);
+          }
+          *(FA2_LDS u32x4*)(pout + qslot) = op[0];
+        }
+      } else {
+        constexpr int i = j - KS, db = i % DB, h = i / DB;
+        acc[db] = mfma32x32x16(ring[j % (PF + 1)], op[h], acc[db]);
+        if constexpr (i < DB) {  // the second half's values beside the first half's MFMAs
+          if constexpr (i == 0) values(1);
+          if constexpr (i == DB - 1) {
+            if constexpr (PWAVE) {
+              if (fix) causal_fixup(1);
+            }
+            *(FA2_LDS u32x4*)(pout + qslot + 1024) = op[1];
+          }
+        }
+      }
+    });
+  };
+  // B roles, one query tile: 2 DB steps of dV^T (or dK^T) with P (or dS) from LDS.
+  auto tile_b = [&](f32x16 (&acc)[DB], const lds_char* tsrc, const lds_char* pin) __attribute__((always_inline)) {
+    u32x4 op[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) op[h] = lds_read16(pin + qslot + h * 1024);
+    u32x4 ring[2 * DB];
+    static_for<0, 2 * DB>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value, db = i % DB, h = i / DB;
+      ring[i] = tr_pair(tsrc + toff[db] + 16 * h * Q::ROWB, tsrc + toff8[db] + 16 * h * Q::ROWB);
+    });
+    static_for<0, 2 * DB>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value, db = i % DB, h = i / DB;
+      acc[db] = mfma32x32x16(ring[i], op[h], acc[db]);
+    });
+  };
+
+  // ROLE: 0 A_P, 1 A_DP, 2 B_DV, 3 B_DK; each runs its own copy of the step loop, with the same
+  // number of steps and barriers.
+  auto run = [&](auto RL) __attribute__((always_inline)) {
+    constexpr int ROLE = decltype(RL)::value;
+    constexpr bool AROLE = ROLE < 2;
+    constexpr int LAG = ROLE == 0 ? 0 : ROLE == 3 ? 2 : 1;
+    u32x4 kv[AROLE ? KS : 1];
+    if constexpr (AROLE) {
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc((ROLE == 0 ? p.k : p.v) + kvoff, head_bytes);
+      const unsigned flip = ROLE == 0 ? p.kneg : 0u;
+      const uint32_t row = (uint32_t)(kw + l32);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kv[ks] = buffer_load16(rs, row * Q::ROWB + (16 * ks + 8 * hf) * 2) ^ flip;
+    }
+    f32x16 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+    Cursor fc{0, 0}, tc{0, 0};
+    advance(fc);
+    auto step = [&](auto S, int s) __attribute__((always_inline)) {
+      constexpr int st = decltype(S)::value;
+      using SN = std::integral_constant<int, (st + 1) & 3>;
+      using ST = std::integral_constant<int, (st + 4 - LAG) & 3>;  // stage of this wave's tile
+      if constexpr (!AROLE) fetch(SN{}, I0{}, I2{}, s + 1, fc);
+      advance(fc);
+      const int t = s - LAG;
+      if (t >= 0 && t < iters) {
+        const int qrow0 = (qt_top - tc.u) * BT;
+        advance(tc);
+        const bool skip = (p.causal && qrow0 + BT - 1 < kw) || qrow0 > kw + Q::RPW - 1 + W;
+        if (!skip) {
+          if constexpr (ROLE == 0) {
+            const bool fix = (p.causal && qrow0 < kw + Q::RPW - 1) || qrow0 + BT - 1 > kw + W;
+            tile_a(std::true_type{}, kv, acc, q_st(ST{}), do_st(ST{}), st_st(ST{}) + 1024, nullptr,
+                   p_buf(ST{}), qrow0, fix);
+          } else if constexpr (ROLE == 1) {
+            tile_a(std::false_type{}, kv, acc, do_st(ST{}), q_st(ST{}), st_st(ST{}), p_buf(ST{}),
+                   ds_buf(ST{}), qrow0, false);
+          } else if constexpr (ROLE == 2) {
+            tile_b(acc, do_st(ST{}), p_buf(ST{}));
+          } else {
+            tile_b(acc, q_st(ST{}), ds_buf(ST{}));
+          }
+        }
+      }
+      wait_vmem_all();
+      __syncthreads();
+    };
+    const int nsteps = iters + 2;
+    int s = 0;
+    for (; s + 4 <= nsteps; s += 4) {
+      step(I0{}, s);
+      step(I1{}, s + 1);
+      step(I2{}, s + 2);
+      step(I3{}, s + 3);
+    }
+    if (s < nsteps) step(I0{}, s);
+    if (s + 1 < nsteps) step(I1{}, s + 1);
+    if (s + 2 < nsteps) step(I2{}, s + 2);
+
+    // dV or dK = scale (dK^T)^T of this wave's 32 keys and 128 head-dim columns, staged through
+    // its own 16 KB of the (now idle) Q/dO stages and stored in whole 128-byte lines.
+    {
+      int el = lane;
+      asm volatile("" : "+v"(el));
+      const int e32 = el & 31, ehf = el >> 5;
+      constexpr int CW = DB * 32, UPR = CW / 4;
+      lds_char* reg = (lds_char*)(wave == 0 ? q_st0 : wave == 1 ? q_st1 : wave == 2 ? q_st2
+                                  : wave == 3 ? q_st3 : wave == 4 ? do_st0 : wave == 5 ? do_st1
+                                  : wave == 6 ? do_st2 : do_st3);
+      constexpr bool DV = ROLE == 0 || ROLE == 2;
+      float* base = (DV ? p.dv : p.dk) + kvoff + (size_t)kw * D + dh * CW;
+      const float f = DV ? 1.f : p.scale;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int cu = 8 * db + 2 * rq + ehf;
+          *(FA2_LDS f32x4*)(reg + e32 * (UPR * 16) + ((cu ^ (e32 & (UPR - 1))) << 4)) =
+              f32x4{acc[db][4 * rq], acc[db][4 * rq + 1], acc[db][4 * rq + 2], acc[db][4 * rq + 3]} * f;
+        }
+#pragma unroll
+      for (int k = 0; k < UPR / 2; ++k) {
+        const int u = 64 * k + el, r = u / UPR, cu = u % UPR;
+        const f32x4 val = *(const FA2_LDS f32x4*)(reg + r * (UPR * 16) + ((cu ^ (r & (UPR - 1))) << 4));
+        if (kw + r < N) *(f32x4*)(base + (size_t)r * D + 4 * cu) = val;
+      }
+    }
+  };
+
+  wait_vmem_all();
+  __syncthreads();
+  if (awave) {
+    if (!odd) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 1>{});
+  } else {
+    if (odd) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 3>{});
   }
 }
 
@@ -1077,14 +1442,17 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
   BwdParams p = make_params(q, k, v, dO, const_cast<float*>(ws), s);
   p.dk = dk;
   p.dv = dv;
+  if (s.d == 256) {
+    p.nblk = (s.N + QuadCfg::BR - 1) / QuadCfg::BR;
+    hipLaunchKernelGGL(fa2_bwd_dkdv_quad_kernel, dim3((unsigned)(s.B * s.Hkv * p.nblk)),
+                       dim3(QuadCfg::WAVES * 64), 0, stream, p);
+    return hipGetLastError();
+  }
   p.nblk = (s.N + BwdCfg<128>::BR - 1) / BwdCfg<128>::BR;
-  const int ndh = s.d == 256 ? PairCfg<256>::NDH : 1;
-  const dim3 grid((unsigned)(s.B * s.Hkv * dkdv_work_items(p.nblk, s.Hq / s.Hkv, s.d) * ndh));
+  const dim3 grid((unsigned)(s.B * s.Hkv * dkdv_work_items(p.nblk, s.Hq / s.Hkv)));
   const dim3 block(PairCfg<128>::WAVES * 64);
   if (s.d == 128)
     hipLaunchKernelGGL(fa2_bwd_dkdv_pair_kernel<128>, grid, block, 0, stream, p);
-  else if (s.d == 256)
-    hipLaunchKernelGGL(fa2_bwd_dkdv_pair_kernel<256>, grid, block, 0, stream, p);
   else
     hipLaunchKernelGGL(fa2_bwd_dkdv_pair_kernel<64>, grid, block, 0, stream, p);
   return hipGetLastError();

@@ -117,7 +117,7 @@ def test_gqa_long_backward_sampled_keys_full_statistics():
 
 
 def test_head_dim_256_backward_sampled_keys_full_statistics():
-    # the d = 256 extra's shape (two dK/dV passes over head-dim halves)
+    # the d = 256 extra's shape (dK/dV by quads of waves split over head-dim halves)
     check_backward_full_statistics(0x5EED0008, 2, 16, 16, 8192, 256, ((1, 9),))
 
 
@@ -126,7 +126,7 @@ def test_gqa_long_backward_long_rows():
 
 
 def test_head_dim_256_backward_long_rows():
-    # the d = 256 benchmark extra's shape, B=2, H=16, N=8192 (two dK/dV passes, two-stage dQ ring)
+    # the d = 256 benchmark extra's shape, B=2, H=16, N=8192 (quad dK/dV, two-stage dQ ring)
     check_backward_long_causal(0x5EED0008, 2, 16, 16, 8192, 256)
 
 
@@ -332,8 +332,9 @@ def test_preprocess_workspace_layout(d, fused):
     assert np.abs(-got[:R] - D.reshape(-1)).max() <= 2e-2 * (1 + np.abs(D).max())
 
 
-# Head dim 256: dK/dV in two passes over head-dim halves, dQ with one 32-row block per wave and
-# a two-stage K/V ring.
+# Head dim 256: dK/dV by quads of waves (S and dP once, dV and dK split over head-dim halves,
+# P and dS handed over through LDS; 64-key workgroups, so N = 63, 64, 65, 129 cross their edges),
+# dQ with one 32-row block per wave and a two-stage K/V ring.
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 63, 64, 65, 129, 257, 500])
 def test_head_dim_256_ragged(N, causal):

@@ -68,6 +68,9 @@ def test_window_ragged_lengths(N):
 def test_window_head_dim_256():
     check_window(6800, 1, 4, 2, 700, 256, 100)
     check_window(6801, 1, 2, 1, 333, 256, 0)
+    # windows ending inside and on the edge of the 32-key quads and 64-key dK/dV workgroups
+    check_window(6802, 1, 4, 1, 500, 256, 31)
+    check_window(6803, 1, 2, 2, 300, 256, 64)
 
 
 @pytest.mark.parametrize("Hkv", [1, 2, 8])
