@@ -596,6 +596,366 @@ void fa2_fwd_kernel(FwdParams p) {
   }
 }
 
+// Forward at head dim 256 without a sliding window: split roles on each SIMD. A 32-row block's O
+// (128 fp32 registers) does not fit beside Q and two score tiles in one of two waves per SIMD, so
+// the general kernel runs one wave per SIMD at d = 256. Here the two waves of a SIMD share 32 rows
+// instead: A waves (0-3) keep Q and do S^T = K Q^T, the online softmax, P, and O^T over head-dim
+// columns [0, D/2); B waves (4-7; B wave 4 + k shares A wave k's SIMD) take P from LDS one tile
+// later, accumulate O^T over [D/2, D), apply the rescale factors A leaves beside P whenever its
+// reference moves, and issue every K/V tile load. 32-key tiles: K in two stages, V in three (the
+// B wave reads V(t - 1) while A reads V(t) and V(t + 1) lands), P and the factors in two
+// buffers, one barrier per tile. (Built for any head dim; at d = 128, where the general kernel
+// already runs two symmetric waves per SIMD, it measured slower, so only d = 256 uses it.)
+template <int D_>
+struct SplitCfg {
+  static constexpr int D = D_, BN = D == 256 ? 32 : 64, KB = BN / 32, BM = 128, ROWB = 2 * D;
+  static constexpr int TILE = BN * ROWB;
+  static constexpr int KS = D / 16, DB = D / 32;
+  static constexpr int DBA = DB / 2, DBB = DB - DBA;  // head-dim blocks of A and of B
+  static constexpr int PBW = KB * 2048;  // one A wave's P of a tile
+};
+
+// Keys [j0, j0 + BN) of one head into a swizzled LDS tile, split over the four B waves (w = 0-3).
+template <int D, bool IS_V>
+__device__ __forceinline__ void split_load_tile(__amdgpu_buffer_rsrc_t rs, lds_char* tile, int j0, int w,
+                                                int lane) {
+  using S_ = SplitCfg<D>;
+  constexpr int LPW = S_::TILE / 1024 / 4;
+#pragma unroll
+  for (int t = 0; t < LPW; ++t) {
+    const int blk = w * LPW + t;
+    const int pos = blk * 1024 + lane * 16;
+    const int r = pos / S_::ROWB;
+    const int cp = (pos % S_::ROWB) / 16;
+    const int c = cp ^ (IS_V ? swz_v<D>(r) : swz_k<D>(r));
+    buffer_load16_lds(rs, tile + blk * 1024, (uint32_t)(j0 + r) * S_::ROWB + c * 16);
+  }
+}
+
+template <int D_>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa2_fwd_split_kernel(FwdParams p) {
+  using S_ = SplitCfg<D_>;
+  constexpr int D = D_, KS = S_::KS, DBA = S_::DBA, DBB = S_::DBB, KB = S_::KB;
+  __shared__ __attribute__((aligned(1024))) char k_st0[S_::TILE];
+  __shared__ __attribute__((aligned(1024))) char k_st1[S_::TILE];
+  __shared__ __attribute__((aligned(1024))) char v_st0[S_::TILE];
+  __shared__ __attribute__((aligned(1024))) char v_st1[S_::TILE];
+  __shared__ __attribute__((aligned(1024))) char v_st2[S_::TILE];
+  __shared__ __attribute__((aligned(1024))) char p_buf0[4 * S_::PBW];
+  __shared__ __attribute__((aligned(1024))) char p_buf1[4 * S_::PBW];
+  __shared__ __attribute__((aligned(1024))) char ctl0[4 * 256];  // per A wave: alpha[32] (+128: flag)
+  __shared__ __attribute__((aligned(1024))) char ctl1[4 * 256];
+  __shared__ __attribute__((aligned(1024))) char inv_buf[4 * 128];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool awave = wave < 4;
+  const int aw = wave & 3;  // the A wave whose rows this wave serves
+  const int hf = lane >> 5, l32 = lane & 31;
+  int bh, j;
+  map_block(blockIdx.x, p, 0, bh, j);
+  const int b = bh / p.Hq, hq = bh % p.Hq;
+  const int hkv = hq / (p.Hq / p.Hkv);
+  const int N = p.N;
+  const int qblk = p.causal ? p.nqb - 1 - j : j;
+  const int q0 = qblk * S_::BM;
+  const int qlo = q0 + aw * 32;
+  const uint32_t head_bytes = (uint32_t)N * S_::ROWB;
+  const size_t qoff = (size_t)bh * N * D;
+  const size_t kvoff = ((size_t)b * p.Hkv + hkv) * (size_t)N * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + qoff, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + kvoff, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + kvoff, head_bytes);
+
+  // Tiles: the workgroup's, and those this wave pair computes (causal: up to its last row).
+  const int qend = min(q0 + S_::BM, N);
+  const int ntiles = p.causal ? (qend + S_::BN - 1) / S_::BN : (N + S_::BN - 1) / S_::BN;
+  const int nmine = p.causal ? min(ntiles, (qlo + 31) / S_::BN + 1) : ntiles;
+  const int nfree = min(nmine, p.causal ? (qlo + 1) / S_::BN : N / S_::BN);
+
+  auto kst = [&](int t) { return (lds_char*)((t & 1) ? k_st1 : k_st0); };
+  auto vst_rt = [&](int t) { const int s = t % 3; return (lds_char*)(s == 0 ? v_st0 : s == 1 ? v_st1 : v_st2); };
+  auto fetch_k = [&](int t) { split_load_tile<D, false>(rk, kst(t), t * S_::BN, wave - 4, lane); };
+  auto fetch_v = [&](int t) { split_load_tile<D, true>(rv, vst_rt(t), t * S_::BN, wave - 4, lane); };
+
+  int voff[S_::DB];
+  {
+    const int r = 4 * hf + ((lane & 15) >> 2);
+#pragma unroll
+    for (int db = 0; db < S_::DB; ++db) {
+      const int d = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      voff[db] = r * S_::ROWB + (((d >> 3) ^ swz_v<D>(r)) << 4) + (d & 7) * 2;
+    }
+  }
+  // P V over this wave's head-dim half (A: blocks 0, 1; B: 2, 3) for one tile: 8 MFMA steps,
+  // i = (kb, h, dbh) with dbh fastest.
+  auto vread = [&](const lds_char* vt, int i, int dbase, int nb) {
+    const int db = dbase + i % nb, kb = i / (2 * nb), h = (i / nb) & 1;
+    const lds_char* base = vt + voff[db] + (32 * kb + 16 * h) * S_::ROWB;
+    const u32x2 lo = lds_read8_tr(base);
+    const u32x2 hi = lds_read8_tr(base + 8 * S_::ROWB);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  typedef u32x4 PTile[KB][2];  // [kb][h]
+
+  // Epilogue: this wave's 32 rows x (32 nb) columns of O (from head-dim block db0), staged in its
+  // own 8 KB of the K/V stages (every load has landed and every wave is past its last read).
+  auto store_o = [&](auto& acc, int db0) __attribute__((always_inline)) {
+    constexpr int NB = sizeof(acc) / sizeof(acc[0]);
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    const int e32 = el & 31, ehf = el >> 5;
+    const float inv = *(const FA2_LDS float*)((lds_char*)inv_buf + aw * 128 + e32 * 4);
+    constexpr int CW = 64, UPR = CW / 4;
+    lds_char* reg = (lds_char*)(wave < 2 ? k_st0 : wave < 4 ? k_st1 : wave < 6 ? v_st0 : v_st1) + (wave & 1) * 8192;
+    static_assert(S_::TILE >= 16384, "two 8 KB regions per stage");
+    const int dbase = 32 * db0;
+    float* obase = p.o + qoff + (size_t)qlo * D + dbase;
+#pragma unroll
+    for (int c = 0; c < NB / 2; ++c) {
+#pragma unroll
+      for (int dbc = 0; dbc < 2; ++dbc)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int db = 2 * c + dbc;
+          const f32x4 val = {acc[db][4 * rq] * inv, acc[db][4 * rq + 1] * inv, acc[db][4 * rq + 2] * inv,
+                             acc[db][4 * rq + 3] * inv};
+          const int cu = 8 * dbc + 2 * rq + ehf;
+          *(FA2_LDS f32x4*)(reg + e32 * (UPR * 16) + ((cu ^ (e32 & (UPR - 1))) << 4)) = val;
+        }
+#pragma unroll
+      for (int k = 0; k < UPR / 2; ++k) {
+        const int u = 64 * k + el, r = u / UPR, cu = u % UPR;
+        const f32x4 val = *(const FA2_LDS f32x4*)(reg + r * (UPR * 16) + ((cu ^ (r & (UPR - 1))) << 4));
+        if (qlo + r < N) *(f32x4*)(obase + (size_t)r * D + c * CW + 4 * cu) = val;
+      }
+    }
+  };
+
+  if (!awave) {
+    // ---------------- B wave ----------------
+    f32x16 acc[DBB];
+#pragma unroll
+    for (int i = 0; i < DBB; ++i) acc[i] = f32x16{};
+    fetch_k(0);
+    fetch_v(0);
+    fetch_k(1);
+    wait_vmem_all();
+    __syncthreads();  // prologue: Q, K(0), V(0), K(1) landed
+    __syncthreads();  // A waves' first S done; K(0)'s stage may be refilled
+    for (int t = 0; t <= ntiles; ++t) {
+      fetch_k(t + 2);
+      fetch_v(t + 1);
+      const int u = t - 1;  // tile whose P this step consumes
+      if (u >= 0 && u < nmine) {
+        const lds_char* pb = (const lds_char*)((u & 1) ? p_buf1 : p_buf0);
+        PTile pf;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) pf[kb][h] = lds_read16(pb + aw * S_::PBW + (2 * kb + h) * 1024 + lane * 16);
+        const lds_char* vt = vst_rt(u);
+        constexpr int NPV = 2 * KB * DBB;
+        u32x4 vr[NPV];
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) vr[i] = vread(vt, i, DBA, DBB);
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+          const int kb = i / (2 * DBB), h = (i / DBB) & 1;
+          acc[i % DBB] = mfma32x32x16(vr[i], pf[kb][h], acc[i % DBB]);
+        }
+        const lds_char* cb = (const lds_char*)((u & 1) ? ctl1 : ctl0);
+        const unsigned flag = *(const FA2_LDS unsigned*)(cb + aw * 256 + 128);
+        if (__builtin_amdgcn_readfirstlane(flag)) {
+          const float alpha = *(const FA2_LDS float*)(cb + aw * 256 + l32 * 4);
+#pragma unroll
+          for (int i = 0; i < DBB; ++i) acc[i] = mfma32x32x16(u32x4{}, u32x4{}, acc[i] * alpha);
+        }
+      }
+      wait_vmem_all();
+      __syncthreads();
+    }
+    store_o(acc, DBA);
+  } else {
+    // ---------------- A wave ----------------
+    f32x16 acc[DBA];
+#pragma unroll
+    for (int i = 0; i < DBA; ++i) acc[i] = f32x16{};
+    u32x4 qf[KS];
+    {
+      const uint32_t row = (uint32_t)(qlo + l32);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = buffer_load16(rq, row * S_::ROWB + (16 * ks + 8 * hf) * 2) ^ p.qneg;
+    }
+    constexpr int NKO = KS < 8 ? KS : 8;  // chunks 16 and up: the same offsets + 256 bytes
+    int koff[NKO];
+#pragma unroll
+    for (int i = 0; i < NKO; ++i) koff[i] = l32 * S_::ROWB + (((2 * i + hf) ^ swz_k<D>(l32)) << 4);
+    float m = -INFINITY, l0 = 0.f, l1 = 0.f;
+    const float c = p.c;
+    typedef f32x16 STile[KB];
+    auto exp_pairs = [&](STile& sc, PTile& pf, float& s0, float& s1, int j0, int j1) {
+#pragma unroll
+      for (int jj = j0; jj < j1; ++jj) {
+        const int kb = jj >> 3, r = (2 * jj) & 15;
+        const float mref = m == -INFINITY ? 0.f : m;
+        const float p0 = fast_exp2(__builtin_fmaf(sc[kb][r], c, -mref));
+        const float p1 = fast_exp2(__builtin_fmaf(sc[kb][r + 1], c, -mref));
+        const unsigned pk = pack_bf16(p0, p1);
+        s0 += p0 + p1;
+        s1 = add_bf16_pair(pk, s1);
+        pf[kb][r >> 3][(r >> 1) & 3] = pk;
+      }
+    };
+    auto max_slice = [&](STile& sn, float& mx, int e0, int ne, bool mask, int j0) {
+      const int qi = qlo + l32;
+      const int lim = p.causal ? min(qi, N - 1) : N - 1;
+#pragma unroll
+      for (int e = e0; e < e0 + ne; ++e) {
+        const int kb = e >> 4, r = e & 15;
+        if (mask) {
+          const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          sn[kb][r] = key > lim ? -INFINITY : sn[kb][r];
+        }
+        mx = fmaxf(mx, sn[kb][r]);
+      }
+    };
+    // One tile's stream: S^T = K Q^T slots (16) if HAS_S, then P V slots (8) if HAS_PV.
+    auto stream = [&](auto has_s, auto has_pv, const lds_char* kt, STile& sn, const lds_char* vt,
+                      PTile& pf, auto&& also_s, auto&& also_pv) __attribute__((always_inline)) {
+      constexpr bool HS = decltype(has_s)::value, HP = decltype(has_pv)::value;
+      constexpr int LA = 3, NSS = HS ? KB * KS : 0, NOP = NSS + (HP ? 2 * KB * DBA : 0);
+      u32x4 ring[LA + 1];
+      auto load = [&](auto J) __attribute__((always_inline)) {
+        constexpr int jj = decltype(J)::value;
+        if constexpr (jj < NSS) {
+          constexpr int ks = jj / KB, kb = jj % KB;
+          ring[jj % (LA + 1)] = lds_read16(kt + koff[ks % NKO] + (ks / NKO) * 256 + kb * 32 * S_::ROWB);
+        }
+        else ring[jj % (LA + 1)] = vread(vt, jj - NSS, 0, DBA);
+      };
+      if constexpr (HS) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) sn[kb] = f32x16{};
+      }
+      static_for<0, (LA < NOP ? LA : NOP)>(load);
+      static_for<0, NOP>([&](auto J) __attribute__((always_inline)) {
+        constexpr int jj = decltype(J)::value;
+        if constexpr (jj + LA < NOP) load(std::integral_constant<int, jj + LA>{});
+        __builtin_amdgcn_sched_barrier(kPinDsReadMfma);
+        if constexpr (jj < NSS) {
+          constexpr int ks = jj / KB, kb = jj % KB;
+          sn[kb] = mfma32x32x16(ring[jj % (LA + 1)], qf[ks], sn[kb]);
+          if constexpr (kb == KB - 1) also_s(ks);
+        } else {
+          constexpr int i = jj - NSS, kb = i / (2 * DBA), h = (i / DBA) & 1;
+          acc[i % DBA] = mfma32x32x16(ring[jj % (LA + 1)], pf[kb][h], acc[i % DBA]);
+          also_pv(i);
+        }
+      });
+    };
+    auto rescale = [&](float mx, lds_char* cb) {
+      const float mt = max_halves(mx) * c;
+      const bool grow = mt > m + kRescaleSlack;
+      const bool any = __builtin_amdgcn_ballot_w64(grow) != 0;
+      if (any) {
+        const float mnew = fmaxf(m, mt);
+        const float alpha = m == mnew ? 1.f : fast_exp2(m - mnew);
+        m = mnew;
+        l0 *= alpha;
+        l1 *= alpha;
+#pragma unroll
+        for (int i = 0; i < DBA; ++i) acc[i] = mfma32x32x16(u32x4{}, u32x4{}, acc[i] * alpha);
+        if (hf == 0) *(FA2_LDS float*)(cb + aw * 256 + l32 * 4) = alpha;
+      }
+      if (lane == 0) *(FA2_LDS unsigned*)(cb + aw * 256 + 128) = any ? 1u : 0u;
+    };
+    auto store_p = [&](const PTile& pf, lds_char* pb) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) *(FA2_LDS u32x4*)(pb + aw * S_::PBW + (2 * kb + h) * 1024 + lane * 16) = pf[kb][h];
+    };
+    STile sbuf[2];
+    auto step = [&](auto par, auto mask_tag, int t) {
+      constexpr int PAR = decltype(par)::value;
+      constexpr bool MASK_NEXT = decltype(mask_tag)::value;
+      PTile pf;
+      float s0 = 0.f, s1 = 0.f, mx = -INFINITY;
+      stream(std::true_type{}, std::true_type{}, (const lds_char*)kst(t + 1), sbuf[PAR ^ 1], (const lds_char*)vst_rt(t), pf,
+             [&](int ks) {
+               // 8 KB exponential pairs over the KS k-steps: EPN pairs every EPD steps
+               constexpr int EPN = 8 * KB >= KS ? 8 * KB / KS : 1, EPD = 8 * KB >= KS ? 1 : KS / (8 * KB);
+               if (ks % EPD == 0) exp_pairs(sbuf[PAR], pf, s0, s1, (ks / EPD) * EPN, (ks / EPD) * EPN + EPN);
+               if (ks == KS - 1) store_p(pf, (lds_char*)(PAR ? p_buf1 : p_buf0));
+             },
+             [&](int i) {
+               constexpr int MS = 16 * KB / (2 * KB * DBA);  // score elements max-reduced per P V step
+               max_slice(sbuf[PAR ^ 1], mx, MS * i, MS, MASK_NEXT, (t + 1) * S_::BN);
+             });
+      l0 += s0;
+      l1 += s1;
+      rescale(mx, (lds_char*)(PAR ? ctl1 : ctl0));
+      wait_vmem_all();
+      __syncthreads();
+    };
+    auto last_step = [&](auto par, int t) {
+      constexpr int PAR = decltype(par)::value;
+      PTile pf;
+      float s0 = 0.f, s1 = 0.f;
+      exp_pairs(sbuf[PAR], pf, s0, s1, 0, 8 * KB);
+      store_p(pf, (lds_char*)(PAR ? p_buf1 : p_buf0));
+      if (lane == 0) *(FA2_LDS unsigned*)((lds_char*)(PAR ? ctl1 : ctl0) + aw * 256 + 128) = 0u;
+      stream(std::false_type{}, std::true_type{}, nullptr, sbuf[PAR], (const lds_char*)vst_rt(t), pf, [](int) {}, [](int) {});
+      l0 += s0;
+      l1 += s1;
+      wait_vmem_all();
+      __syncthreads();
+    };
+    wait_vmem_all();
+    __syncthreads();  // prologue loads landed
+    {
+      float mx = -INFINITY;
+      PTile unused;
+      stream(std::true_type{}, std::false_type{}, (const lds_char*)k_st0, sbuf[0], nullptr, unused, [](int) {}, [](int) {});
+      max_slice(sbuf[0], mx, 0, 16 * KB, nfree == 0, 0);
+      const float mt = max_halves(mx) * c;
+      m = mt;  // first reference (O, l still zero)
+    }
+    __syncthreads();
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    int t = 0;
+    const int nfree_steps = nfree > 0 ? ((nfree - 1) & ~1) : 0;
+    for (; t < nfree_steps; t += 2) {
+      step(P0{}, std::false_type{}, t);
+      step(P1{}, std::false_type{}, t + 1);
+    }
+    for (; t + 2 < nmine; t += 2) {
+      step(P0{}, std::true_type{}, t);
+      step(P1{}, std::true_type{}, t + 1);
+    }
+    if (t + 1 < nmine) {
+      step(P0{}, std::true_type{}, t);
+      last_step(P1{}, t + 1);
+    } else {
+      last_step(P0{}, t);
+    }
+    // 1 / (sum of the bf16 P) for the B wave, and this wave's LSE.
+    const float lt = sum_halves(l0);
+    const float inv = p.vmul / sum_halves(l1);
+    if (hf == 0) *(FA2_LDS float*)((lds_char*)inv_buf + aw * 128 + l32 * 4) = inv;
+    const int row = qlo + l32;
+    if (row < N && hf == 0) p.lse[(size_t)bh * N + row] = (m + __log2f(lt)) * kLn2;
+    for (t = nmine; t <= ntiles; ++t) {  // keep the barrier cadence of the B waves
+      wait_vmem_all();
+      __syncthreads();
+    }
+    store_o(acc, 0);
+  }
+}
+
 // Waves per workgroup: 4 (128 query rows, several workgroups per CU, so that one's start-up --
 // Q and the first K/V tiles -- and O stores overlap the others' tiles), or, at d = 128 only, 8
 // (256 rows, fewer K/V tile copies per row, four blocks per workgroup) where that measured
@@ -644,6 +1004,14 @@ static void launch_fwd_kernel(const FwdParams& p, const AttnShape& s, hipStream_
 
 hipError_t launch_forward(const void* q, const void* k, const void* v, float* o, float* lse,
                           const AttnShape& s, hipStream_t stream) {
+  if (s.d == 256 && kernel_window(s) == kNoWindow) {
+    // 6-10 % faster than the one-wave-per-SIMD d = 256 configuration (same box, causal
+    // B2 H16 N8192, B1 Hq32 Hkv8 N16384, B4 H16 N4096); that one stays for sliding windows.
+    const FwdParams p = forward_params(q, k, v, o, lse, s, 4);  // 128-row blocks
+    hipLaunchKernelGGL(fa2_fwd_split_kernel<256>, dim3((unsigned)(s.B * s.Hq * p.nqb)), dim3(512), 0,
+                       stream, p);
+    return hipGetLastError();
+  }
   const int nw = forward_waves(s);
   const FwdParams p = forward_params(q, k, v, o, lse, s, nw);
   if (s.d == 256)

@@ -82,7 +82,7 @@ def test_gqa_ratios(Hkv, d):
 # Online-softmax stress: the reference is raised only when a row's tile max passes it by more than
 # 8 (log2 units). Keys scaled up along the sequence make almost every tile raise it by a large
 # jump; scaled down, later tiles contribute nothing; a huge scale makes each row nearly one-hot.
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("profile", ["growing", "shrinking", "steps"])
 def test_score_range_stress(profile, causal, d):
@@ -95,9 +95,10 @@ def test_score_range_stress(profile, causal, d):
     check_forward_on(q, H.scale_rows(k, factors), v, causal, seed=0x57E5)
 
 
+@pytest.mark.parametrize("d", [128, 256])
 @pytest.mark.parametrize("causal", [False, True])
-def test_near_one_hot_rows(causal):
-    q, k, v = H.make_inputs(0x57E6, 1, 4, 4, 700, 128)
+def test_near_one_hot_rows(causal, d):
+    q, k, v = H.make_inputs(0x57E6, 1, 4, 4, 700, d)
     check_forward_on(q, k, v, causal, scale=8.0, seed=0x57E6)
 
 
@@ -180,7 +181,8 @@ def test_rejected_call_writes_nothing():
     assert bool((o == 7.0).all()) and bool((lse == 7.0).all())
 
 
-# Head dim 256: its own configuration (4 waves x 32 rows, O in AGPRs, 32 KB K/V tiles).
+# Head dim 256 without a window: split roles (A waves: S, softmax, O columns 0-127; B waves: O
+# columns 128-255 from P in LDS, with A's rescale factors), 128-row blocks, 32-key tiles.
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 63, 64, 65, 128, 129, 300, 1000])
 def test_head_dim_256_ragged(N, causal):
@@ -191,3 +193,4 @@ def test_head_dim_256_gqa_and_long():
     check_forward(8100, 2, 8, 2, 777, 256, True)
     check_forward(8101, 1, 4, 4, 4096, 256, True, sample=256)
     check_forward(8102, 1, 4, 2, 2048, 256, False, scale=-0.05)
+    check_forward(8103, 1, 2, 1, 65536, 256, True, sample=24)
