@@ -688,8 +688,8 @@ void fa2_fwd_split_kernel(FwdParams p) {
       voff[db] = r * S_::ROWB + (((d >> 3) ^ swz_v<D>(r)) << 4) + (d & 7) * 2;
     }
   }
-  // P V over this wave's head-dim half (A: blocks 0, 1; B: 2, 3) for one tile: 8 MFMA steps,
-  // i = (kb, h, dbh) with dbh fastest.
+  // P V operand i of a tile over nb head-dim blocks from dbase (A: blocks [0, DBA), B: [DBA, DB)):
+  // 2 KB nb MFMA steps, i = (kb, h, block) with the block fastest.
   auto vread = [&](const lds_char* vt, int i, int dbase, int nb) {
     const int db = dbase + i % nb, kb = i / (2 * nb), h = (i / nb) & 1;
     const lds_char* base = vt + voff[db] + (32 * kb + 16 * h) * S_::ROWB;
