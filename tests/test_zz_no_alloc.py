@@ -41,6 +41,12 @@ def test_noalloc_matches_backward_twice_shrinking():
     run_pair(0x5EED0A02, 1, 4, 4, 300, 64, False)   # second, smaller: 1200 rows
 
 
+def test_noalloc_head_dim_256_twice_shrinking():
+    # head dim 256: the quad dK/dV kernel and the d = 256 dQ kernel on the fixed workspace
+    run_pair(0x5EED0A04, 1, 4, 2, 500, 256, True)
+    run_pair(0x5EED0A05, 1, 2, 2, 130, 256, False)
+
+
 def test_noalloc_rejects_over_limit_without_launch():
     import torch
     q, k, v = (H.to_dev(x) for x in H.make_inputs(0x5EED0A03, 1, 2, 2, 64, 64))
