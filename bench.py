@@ -109,6 +109,27 @@ def time_sequence(calls, steps, warmup, stream, spread=None):
     return per, total
 
 
+def time_back_to_back(call, reps, rounds, stream):
+    """Median over ``rounds`` of the mean duration, in ms, of ``reps`` calls issued back to back
+    between two HIP events on ``stream`` (no event between the calls). For launches of a few
+    tens of microseconds the events recorded around every call in time_sequence add several
+    microseconds each; this is the steady rate of repeated calls."""
+    import numpy as np
+    import torch
+    for _ in range(3):
+        call()
+    ts = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / reps)
+    return float(np.median(ts))
+
+
 def extra_workloads(fa2, seedgen, dev, stream, steps, only=None):
     """Non-headline measurements: the sliding-window path at the headline shape, and the other
     workload shapes (forward-only prefill shapes, a training shape). Values are TFLOP/s of the
@@ -173,6 +194,10 @@ def extra_workloads(fa2, seedgen, dev, stream, steps, only=None):
              "fwd_ms_max": round(spread["max"][0], 4), "timed_runs": runs,
              "fwd_tflops": round(pairs * 4 * d / (per[0] * 1e-3) / 1e12, 1),
              "fwd_algorithmic_bytes": fwd_bytes, "fwd_GBps": round(fwd_bytes / (per[0] * 1e-3) / 1e9, 1)}
+        if per[0] < 0.5:
+            b2b = time_back_to_back(fcall, 50, 7, stream)
+            r["fwd_ms_back_to_back"] = round(b2b, 4)
+            r["fwd_tflops_back_to_back"] = round(pairs * 4 * d / (b2b * 1e-3) / 1e12, 1)
         if with_bwd:
             r["bwd_ms"] = round(per[1], 4)
             # forward 4 FLOP per visible pair and head-dim element, backward 2.5 times that
@@ -215,13 +240,15 @@ def hbm_sweep(fa2, seedgen, dev, stream, steps, out):
                     raise fa2.Fa2Error(st, "fa2_forward")
 
             per, total = time_sequence([call], max(20, steps), 3, stream)
+            b2b = time_back_to_back(call, 50, 7, stream)
             nbytes = 3 * B * H * N * d * 2 + B * H * N * (d + 1) * 4
             flops = 4.0 * B * H * N * N * d
             res["BH%d_N%d" % (B * H, N)] = {
                 "B": B, "H": H, "N": N, "d": d, "ms": round(total, 4), "algorithmic_bytes": nbytes,
                 "GBps": round(nbytes / (total * 1e-3) / 1e9, 1),
                 "hbm_frac": round(nbytes / (total * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                "flop_per_byte": round(flops / nbytes, 1), "tflops": round(flops / (total * 1e-3) / 1e12, 1)}
+                "flop_per_byte": round(flops / nbytes, 1), "tflops": round(flops / (total * 1e-3) / 1e12, 1),
+                "ms_back_to_back": round(b2b, 4), "GBps_back_to_back": round(nbytes / (b2b * 1e-3) / 1e9, 1)}
             del q, k, v, qd, kd, vd, o, lse
     out["hbm_sweep_d64_noncausal"] = res
     log("  extra %-38s %s" % ("hbm_sweep_d64_noncausal", {k: v["GBps"] for k, v in res.items()}))
@@ -304,9 +331,11 @@ def decode(fa2, seedgen, dev, stream, steps, out):
                          "fa2_decode")
     per, total = time_sequence([call], max(20, steps), 3, stream)
     nbytes = 2 * B * Hkv * Nk * d * 2 + B * Hq * Nq * d * (2 + 4) + B * Hq * Nq * 4
+    b2b = time_back_to_back(call, 50, 7, stream)
     r = {"B": B, "Hq": Hq, "Hkv": Hkv, "Nq": Nq, "Nk": Nk, "d": d, "causal": True, "ms": round(total, 4),
          "algorithmic_bytes": nbytes, "GBps": round(nbytes / (total * 1e-3) / 1e9, 1),
-         "hbm_frac": round(nbytes / (total * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+         "hbm_frac": round(nbytes / (total * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+         "ms_back_to_back": round(b2b, 4), "GBps_back_to_back": round(nbytes / (b2b * 1e-3) / 1e9, 1)}
     out["decode_B8_Hq32_Hkv8_Nq1_Nk32768_d128"] = r
     log("  extra %-38s %s" % ("decode_B8_Hq32_Hkv8_Nq1_Nk32768_d128", r))
 
