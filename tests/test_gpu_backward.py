@@ -75,6 +75,12 @@ def test_prefill_shape_backward_long_rows():
     check_backward_long_causal(0x5EED0006, 2, 32, 32, 8192, 128)
 
 
+def test_backward_largest_sequence_accepted():
+    # N = 2^22 - 1 at d = 128, the longest sequence fa2_backward accepts: the fp32 dQ/dK/dV and O
+    # rows of the head end just under 2^31 bytes, the top of every kernel's 32-bit in-head offsets
+    check_backward_long_causal(0x5EED0A03, 1, 1, 1, (1 << 22) - 1, 128, nq=16, nk=64)
+
+
 def check_backward_full_statistics(seed, B, Hq, Hkv, N, d, slices):
     """Causal dK/dV at 256 sampled keys of the given (batch, KV head) slices -- keys 0-15 (whose
     query walks are the longest), key N-1 and 239 drawn keys -- against the oracle with the

@@ -108,6 +108,16 @@ def test_largest_sequence_accepted():
     check_forward(0x5EED0A00, 1, 1, 1, (1 << 22) - 1, 128, True, sample=24)
 
 
+def test_largest_sequence_accepted_head_dim_256():
+    # N = 2^21 - 1 at d = 256 (the split-role kernel): fp32 rows of one head just under 2^31 bytes
+    check_forward(0x5EED0A01, 1, 1, 1, (1 << 21) - 1, 256, True, sample=16)
+
+
+def test_largest_sequence_accepted_head_dim_64():
+    # N = 2^23 - 1 at d = 64: the same limit, the longest key walk any forward runs
+    check_forward(0x5EED0A02, 1, 1, 1, (1 << 23) - 1, 64, True, sample=16)
+
+
 # At d = 128, workgroups hold 8 waves (256 query rows) when the grid of such blocks reaches four
 # per CU for causal N >= 2048 (B*Hq*ceil(N/256) >= 1024), six per CU for non-causal N > 4096, else 4
 # waves (128 rows); the shapes above mostly run 4-wave blocks, these 8-wave ones, with ragged ends,
