@@ -62,13 +62,14 @@ def sample_rows(seed, nslices, N, count=256):
     return seedgen.sample_rows_all(seed, nslices, N, count)
 
 
-def causal_row_stats(q64, k64, v64, dO64, scale, stat_rows):
+def causal_row_stats(q64, k64, v64, dO64, scale, stat_rows, window=-1):
     """The oracle's backward row statistics (m, l, D), [B,Hq,N] each, filled only at the per-slice
-    rows ``stat_rows`` [B*Hq, R] of a causal problem (the oracle's row statistics of just those
-    rows). Other entries are left at m = 0, l = 1, D = 0 and must not be read (causal dK/dV of
-    the keys whose queries are all in ``stat_rows``, and dQ of a row, read only their own rows)."""
+    rows ``stat_rows`` [B*Hq, R] of a causal problem (with a sliding window if ``window`` >= 0;
+    the oracle's row statistics of just those rows). Other entries are left at m = 0, l = 1,
+    D = 0 and must not be read (causal dK/dV of the keys whose queries are all in ``stat_rows``,
+    and dQ of a row, read only their own rows)."""
     B, Hq, N = q64.shape[:3]
-    sm, sl, sD = oracle.row_stats(q64, k64, v64, dO64, True, scale, rows=stat_rows)
+    sm, sl, sD = oracle.row_stats(q64, k64, v64, dO64, True, scale, rows=stat_rows, window=window)
     m = np.zeros((B, Hq, N))
     l = np.ones((B, Hq, N))
     D = np.zeros((B, Hq, N))

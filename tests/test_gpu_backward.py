@@ -81,6 +81,11 @@ def test_backward_largest_sequence_accepted():
     check_backward_long_causal(0x5EED0A03, 1, 1, 1, (1 << 22) - 1, 128, nq=16, nk=64)
 
 
+def test_backward_largest_sequence_accepted_head_dim_256():
+    # N = 2^21 - 1 at d = 256 (quad dK/dV, dQ with one 32-row block per wave)
+    check_backward_long_causal(0x5EED0A04, 1, 1, 1, (1 << 21) - 1, 256, nq=16, nk=64)
+
+
 def check_backward_full_statistics(seed, B, Hq, Hkv, N, d, slices):
     """Causal dK/dV at 256 sampled keys of the given (batch, KV head) slices -- keys 0-15 (whose
     query walks are the longest), key N-1 and 239 drawn keys -- against the oracle with the

@@ -87,6 +87,37 @@ def test_window_long_sampled():
     check_window(6500, 1, 8, 2, 8192, 128, 1024, sample=256)
 
 
+def test_window_largest_sequence_accepted():
+    # N = 2^22 - 1 at d = 128 with a 1000-key window: workgroups whose first visible tile lies
+    # millions of keys into the head, and 32-bit in-head offsets at the top of their range. dK/dV
+    # at keys 0, N - 1 and a few between; the oracle's statistics only for the rows that see them.
+    B, Hq, Hkv, N, d, W = 1, 1, 1, (1 << 22) - 1, 128, 1000
+    scale = 1.0 / math.sqrt(d)
+    seed = 0x5EED0A06
+    q, k, v, dO = H.make_inputs(seed, B, Hq, Hkv, N, d, with_do=True)
+    o, lse, (dq, dk, dv) = run(q, k, v, dO, W, scale)
+    keys = np.array([0, 1, 4095, N // 2, N - W - 1, N - W, N - 2, N - 1], dtype=np.int32)
+    qrows = np.unique(np.concatenate([H.sample_rows(seed, 1, N, 14)[0], [0, N - 1]])).astype(np.int32)
+    seen = np.concatenate([np.arange(j, min(j + W, N - 1) + 1) for j in keys])
+    stat_rows = np.unique(np.concatenate([qrows, seen])).astype(np.int32)[None]
+    fq, fk, fv, fdo = H.f64(q), H.f64(k), H.f64(v), H.f64(dO)
+    ro, rl = oracle.forward(fq, fk, fv, True, scale, rows=qrows[None], window=W)
+    go, gl = H.gather_rows(o, qrows[None]), H.gather_rows(lse, qrows[None])
+    eo, el = H.max_abs(go, ro), H.max_abs(gl, rl)
+    stats = H.causal_row_stats(fq, fk, fv, fdo, scale, stat_rows, window=W)
+    rdq, rdk, rdv, _ = oracle.backward(fq, fk, fv, fdo, True, scale, qrows=qrows[None], krows=keys[None],
+                                       stats=stats, window=W)
+    gdq = H.gather_rows(dq, qrows[None])
+    gdk, gdv = H.gather_rows(dk, keys[None]), H.gather_rows(dv, keys[None])
+    eq, ek, ev = H.rel_l2(gdq, rdq), H.rel_l2(gdk, rdk), H.rel_l2(gdv, rdv)
+    msg = "window W=%d N=%d: O %.3e LSE %.3e dQ %.3e dK %.3e dV %.3e" % (W, N, eo, el, eq, ek, ev)
+    print(msg)
+    for g in (go, gl, gdq, gdk, gdv):
+        assert np.all(np.isfinite(g))
+    assert eo <= H.TOL_O and el <= H.TOL_LSE, msg
+    assert eq <= H.TOL_GRAD and ek <= H.TOL_GRAD and ev <= H.TOL_GRAD, msg
+
+
 def test_window_eight_wave_blocks_sampled():
     # windows of more than 4096 keys on long sequences and large grids run 8-wave workgroups
     # (shorter windows run 4-wave ones, like the shapes above)
