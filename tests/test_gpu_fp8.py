@@ -60,6 +60,12 @@ def test_fp8_gqa_scales_and_sign():
     check_fp8(9602, 1, 32, 8, 4096, 128, True, sample=128)
 
 
+def test_fp8_largest_sequence_accepted():
+    # N = 2^22 - 1: FP8 Q/K rows of 128 bytes and the widened bf16 V (1 GiB workspace) at the
+    # longest sequence fa2_forward_fp8 accepts
+    check_fp8(0x5EED0A07, 1, 1, 1, (1 << 22) - 1, 128, True, sample=16)
+
+
 def test_fp8_eight_wave_blocks_sampled():
     # N > 4096 and B*Hq*ceil(N/256) >= 1536: 8-wave workgroups, ragged end, grouped heads
     check_fp8(9700, 1, 192, 48, 4200, 128, True, sample=48)
