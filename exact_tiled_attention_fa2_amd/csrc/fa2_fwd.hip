@@ -9,9 +9,11 @@
 //
 // gfx950 mapping (one workgroup per (batch, query head, query block of 256 or 128 rows)):
 //  * 8 waves for long sequences on large grids, else 4 (several workgroups per CU); two waves
-//    per SIMD (three at d = 64 with 4-wave workgroups, one at d = 256). Each wave owns 32 query
-//    rows for the whole pass, so the online-softmax state and all row reductions stay in that
-//    wave's registers.
+//    per SIMD (three at d = 64 with 4-wave workgroups, one at d = 256 with a sliding window).
+//    Each wave owns 32 query rows for the whole pass, so the online-softmax state and all row
+//    reductions stay in that wave's registers. Head dim 256 without a window runs the
+//    split-role kernel at the end of this file instead: the two waves of a SIMD share 32 rows,
+//    one holding O's first 128 columns and the softmax, the other O's last 128 columns.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: each lane then
 //    holds one query row and 16 keys, the row max/sum are in-register reductions plus one
 //    v_permlane32_swap, and S^T's accumulator is directly the B operand of O^T += V^T P^T.
